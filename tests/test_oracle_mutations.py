@@ -1,0 +1,67 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake (a dropped term, a wrong sign, a transposed
+index, a wrong rounding rule ...) in a copy of oracle.c on the CPU, builds
+that copy in a temporary directory and runs the pin tests against it; the
+pins must fail.  Slow (one pytest run per mistake): FP_SLOW_TESTS=1.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+MUTATIONS = {
+    "padding_not_zero": ("out[k] = 0;", "out[k] = 1;"),
+    "padded_size_rounded_down": ("((t + world - 1) / world)", "((t) / world)"),
+    "view_offset_in_flat_not_shard": ("buf_offset[i] = lo - (int64_t)rank * s;", "buf_offset[i] = lo - o;"),
+    "view_tensor_offset_wrong": ("tensor_offset[i] = lo - o;", "tensor_offset[i] = lo - (int64_t)rank * s;"),
+    "reduce_drops_rank_1": ("for (int32_t q = 1; q < world; ++q)\n            sum",
+                            "for (int32_t q = 2; q < world; ++q)\n            sum"),
+    "reduce_starts_from_plus_zero": ("float sum = or_bf16_to_f32(grads[0][i]);\n        for (int32_t q = 1;",
+                                     "float sum = 0.0f;\n        for (int32_t q = 0;"),
+    "reduce_wrong_rank_index": ("sum = sum + or_bf16_to_f32(grads[q][i]);",
+                                "sum = sum + or_bf16_to_f32(grads[world - q][i]);"),
+    "reduce_ignores_accumulate": ("acc[i] = acc[i] + y;", "acc[i] = y;"),
+    "reduce_sums_instead_of_mean": ("float y = sum * scale;", "float y = sum;"),
+    "adamw_no_bias_correction_1": ("double m_hat = m / bias1;", "double m_hat = m;"),
+    "adamw_no_bias_correction_2": ("double v_hat = v / bias2;", "double v_hat = v;"),
+    "adamw_decay_sign": ("theta * (1.0 - lr * weight_decay)", "theta * (1.0 + lr * weight_decay)"),
+    "adamw_eps_inside_sqrt": ("(sqrt(v_hat) + eps)", "sqrt(v_hat + eps)"),
+    "adamw_beta_swapped": ("(1.0 - beta2) * g * g", "(1.0 - beta1) * g * g"),
+    "adamw_update_sign": ("theta = theta - lr * m_hat", "theta = theta + lr * m_hat"),
+    "adamw_no_decay": ("theta = theta * (1.0 - lr * weight_decay);\n", ""),
+    "adamw_skip_ignored": ("if (skip)\n        return;", ""),
+    "bf16_ties_away_from_zero": ("(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
+    "bf16_truncates": ("upper += 1u;", "upper += 0u;"),
+    "unshard_transposed": ("full[(int64_t)q * shard + j] = shards[q][j];", "full[j * world + q] = shards[q][j];"),
+    "memory_stage2_drops_grads": ("case 2: return 2.0 * psi + (2.0 * psi + k * psi) / n;",
+                                  "case 2: return 2.0 * psi + (k * psi) / n;"),
+    "memory_stage1_shards_grads": ("case 1: return 2.0 * psi + 2.0 * psi + k * psi / n;",
+                                   "case 1: return 2.0 * psi + 2.0 * psi / n + k * psi / n;"),
+    "overflow_check_misses_nan": ("if (!isfinite(acc[i]))", "if (isinf(acc[i]))"),
+    "norm_squares_in_fp32": ("s = s + (double)acc[i] * (double)acc[i];", "s = s + (double)(acc[i] * acc[i]);"),
+    "locate_offset_by_one": ("offset[j] = pos[j] - start;\n        } else", "offset[j] = pos[j] - start + 1;\n        } else"),
+}
+
+PIN_FILES = ["tests/test_oracle_pack.py", "tests/test_oracle_reduce.py",
+             "tests/test_oracle_adamw.py", "tests/test_oracle_bf16_memory.py"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, "mutation site not found"
+    for sub in ("oracle", "workloads", "tests"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    (tmp_path / "oracle" / "oracle.c").write_text(src.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", *PIN_FILES],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch {name}:\n{r.stdout[-2000:]}"
