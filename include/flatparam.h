@@ -1,0 +1,279 @@
+/*
+ * flatparam.h -- C ABI of libflatparam.so: one rank's FSDP / ZeRO shard step
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * The library implements, as hand-written HIP kernels, the per-rank data
+ * path of sharded data parallelism:
+ *   pack    -- build a FlatParameter from a unit's tensors,
+ *   reduce  -- the arithmetic of the gradient reduce-scatter (average of the
+ *              N ranks' bf16 gradients into this rank's fp32 shard, with
+ *              micro-batch accumulation and an overflow check),
+ *   adamw   -- the mixed-precision AdamW update of the shard,
+ *   unshard -- the bf16 cast and the all-gather's copy of every rank's
+ *              shard back into the full flat buffer,
+ *   views   -- the original tensors as full, fragment or empty views.
+ * On one GPU the N "ranks" are buffers on that GPU.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [DP]    "Infra: Data Parallel" (pufanyi.com)
+ *   [FSDP]  "PyTorch FSDP: 大模型分布式训练的工业级分片并行方案" (2048ai.net,
+ *           a summary of Zhao et al., PyTorch FSDP, VLDB 2023)
+ *   [GUIDE] "4.1 数据并行详解" (AIInfraGuide)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: every device buffer belongs to the caller and is passed as a
+ *   raw device pointer; the library never frees or keeps them.  Host arrays
+ *   (pointer tables, shapes) are read during the call only.  An fp_plan is
+ *   owned by the library until fp_plan_destroy.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Device work is enqueued on it asynchronously; no entry point
+ *   waits for the device, except fp_pack as noted there.
+ * Layout: bf16 values are passed as uint16_t bit patterns.  fp32 buffers
+ *   (grad / acc, master, exp_avg, exp_avg_sq) must be 16-byte aligned;
+ *   bf16 buffers need only their natural 2-byte alignment.
+ * Errors: every call returns an fp_status.  On any error nothing has been
+ *   enqueued, except FP_ERR_DEVICE after a failed launch.  Faults inside a
+ *   kernel surface at the caller's next synchronisation.  fp_last_error()
+ *   returns a message for the calling thread's most recent failure.
+ * The library keeps no global mutable state apart from that message.
+ */
+#ifndef FLATPARAM_H
+#define FLATPARAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fp_status;
+
+#define FP_OK 0
+#define FP_ERR_INVALID (-1) /* null pointer, negative size, bad enum value  */
+#define FP_ERR_RANGE (-2)   /* size, world, rank or count out of range      */
+#define FP_ERR_ALIGN (-3)   /* pointer not aligned as required              */
+#define FP_ERR_DEVICE (-4)  /* the HIP runtime reported an error            */
+
+/* Largest N_d the device entry points accept (pointer tables travel as
+ * kernel arguments).  Plans and views accept any world up to 1 << 20. */
+#define FP_MAX_WORLD 128
+#define FP_MAX_NDIM 8
+
+/* ------------------------------------------------------------------ plan */
+
+/* Immutable description of one FlatParameter: the unit's tensor shapes in
+ * order and the world size N_d.  [DP] section "FSDP1: pack first, then
+ * split" and its figure: the tensors are flattened (row-major) and
+ * concatenated into one 1-D buffer that is split evenly over N_d ranks, a
+ * shard boundary may cut a tensor.  [FSDP] section 2 (FlatParameter).
+ * Geometry: T = sum of numels; P = T rounded up to a multiple of N_d (the
+ * tail P - T elements are zero padding); S = P / N_d; rank q's shard is
+ * flat[q*S, (q+1)*S).  [DP] ZeRO figure: GPU i holds slice i. */
+typedef struct fp_plan fp_plan;
+
+/* n_tensors >= 1 tensors; ndims[i] in [0, FP_MAX_NDIM] (0 = scalar);
+ * shapes holds the dims of all tensors back to back (sum of ndims entries,
+ * each >= 0); world in [1, 1 << 20].  Host only: touches no device.
+ * On success *out receives a new plan.  FP_ERR_RANGE if T exceeds 2^62. */
+fp_status fp_plan_create(int32_t n_tensors, const int32_t* ndims, const int64_t* shapes,
+                         int32_t world, fp_plan** out);
+
+/* Releases the plan and any device tables fp_pack attached to it.  The
+ * caller must make sure no fp_pack on this plan is still running. */
+void fp_plan_destroy(fp_plan* plan);
+
+/* T, P and S of the plan (any output pointer may be NULL).  Host only. */
+fp_status fp_plan_info(const fp_plan* plan, int64_t* numel, int64_t* padded, int64_t* shard);
+
+/* ------------------------------------------------------------------ pack */
+
+/* FlatParameter construction.  flat[o_i + k] = tensor_i[k] bit for bit,
+ * o_i = sum of the numels before tensor i; flat[T, P) = 0.
+ * elem_size: 2 (bf16 / fp16) or 4 (fp32); the copy is dtype-agnostic and
+ * keeps every bit pattern (NaN payloads, -0).
+ * src: host array of n_tensors device pointers, each to a contiguous
+ *   row-major tensor aligned to elem_size; NULL only for empty tensors.
+ * flat: device buffer of P elements, 16-byte aligned, not overlapping any
+ *   source.
+ * On its first call on a device the plan allocates and uploads its tensor
+ * tables to that device (hipMalloc / pinned host staging; released by
+ * fp_plan_destroy); each call uploads the source pointer table on
+ * `stream`.  Calls that share a plan must be ordered on one stream; a call
+ * waits on the host only if the previous call's pointer upload from the
+ * same plan has not finished yet.  A one-time set-up operation per unit,
+ * not part of the per-step path. */
+fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const* src, void* flat,
+                  void* stream);
+
+/* ------------------------------------------------------------------ views */
+
+/* Views of the original tensors on the flat buffer.  [DP] FSDP1 section,
+ * use_orig_params paragraph: each original parameter points into the flat
+ * buffer; on a rank it may be a piece of the tensor or empty.
+ * rank == -1: the full view, buf_offset = o_i into the FlatParameter,
+ *   numel = n_i, tensor_offset = 0, shape = the tensor's shape.
+ * rank in [0, N_d): with lo = max(o_i, rank*S), hi = min(o_i + n_i,
+ *   (rank+1)*S), a 1-D fragment when hi > lo: buf_offset = lo - rank*S
+ *   into the shard, numel = hi - lo, tensor_offset = lo - o_i, ndim = 1,
+ *   shape[0] = numel; otherwise an empty view (numel = 0, ndim = 1,
+ *   shape[0] = 0, offsets 0).
+ * One descriptor per tensor, in tensor order, written to out[0..n) where
+ * n = number of tensors; FP_ERR_RANGE if cap < n (then *n_out = n and
+ * nothing is written).  Host only. */
+typedef struct fp_view {
+    int32_t tensor;
+    int32_t ndim;
+    int64_t buf_offset;
+    int64_t numel;
+    int64_t tensor_offset;
+    int64_t shape[FP_MAX_NDIM];
+} fp_view;
+
+fp_status fp_unpack_views(const fp_plan* plan, int32_t rank, fp_view* out, int32_t cap,
+                          int32_t* n_out);
+
+/* ------------------------------------------------------------------ reduce */
+
+/* Size in bytes of the device workspace fp_reduce_shard and fp_shard_step
+ * need for the optional gradient norm (a fixed size, independent of S). */
+int64_t fp_workspace_bytes(void);
+
+/* One micro-batch of the reduce-scatter arithmetic for this rank's shard.
+ * [GUIDE] section 2 (equation for the averaged gradient): the synchronised
+ * gradient is the mean of the N local gradients.  [DP] ZeRO-1 / ZeRO-2
+ * paragraphs: reduce-scatter with averaging, each rank keeps its own
+ * reduced slice.  [DP] Naive DP section: with n equal micro-batches each
+ * loss is divided by n.  [FSDP] section 3.5: low-precision (bf16)
+ * communication, high precision for the optimizer; sharded grad scaler.
+ * For every i < S:
+ *   s = bf16(grads[0][i]); s = s + bf16(grads[q][i]) for q = 1..N-1 in
+ *   ascending order (fp32, round-to-nearest-even, no fused multiply-add);
+ *   y = s * scale (fp32);  acc[i] = accumulate ? acc[i] + y : y.
+ * Then *found_inf is set to 1 if any new acc[i] is +-inf or NaN (it is
+ * never cleared: the caller zeroes it at the start of a step, so the flag
+ * ORs over micro-batches), and, if sq_norm != NULL, *sq_norm = sum of
+ * acc[i]^2 over the shard in fp64 (a fixed-order tree over a fixed grid:
+ * bitwise reproducible run to run).
+ * S >= 0; world in [1, FP_MAX_WORLD]; grads: host array of world device
+ *   pointers to bf16[S] (rank q's gradient restricted to this shard's
+ *   range); acc: device fp32[S], 16-byte aligned; found_inf: device int32,
+ *   may be NULL; sq_norm: device double, may be NULL; workspace: device
+ *   buffer of fp_workspace_bytes() bytes, needed only when sq_norm != NULL.
+ *   scale is normally 1 / (N * n_micro). */
+fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_t* const* grads,
+                          float scale, int32_t accumulate, float* acc, int32_t* found_inf,
+                          double* sq_norm, void* workspace, void* stream);
+
+/* ------------------------------------------------------------------ adamw */
+
+/* Hyperparameters in fp64; the library derives every coefficient in fp64. */
+typedef struct fp_adamw_hparams {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+    int64_t step; /* t >= 1, the caller's count of steps taken (not skipped) */
+} fp_adamw_hparams;
+
+/* AdamW on the shard.  [DP] ZeRO-1 paragraph: AdamW is elementwise, so a
+ * rank updates its slice from its averaged gradient and its own moments;
+ * [DP] ZeRO figure legend and [GUIDE] section 7: fp32 master weights and
+ * two fp32 moments (12 bytes per parameter).  For every i < S, evaluated in
+ * fp64 from the fp32 values:
+ *   theta = master[i] * (1 - lr * weight_decay)
+ *   m = beta1 * exp_avg[i] + (1 - beta1) * g[i]
+ *   v = beta2 * exp_avg_sq[i] + (1 - beta2) * g[i]^2
+ *   theta = theta - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * and master, exp_avg, exp_avg_sq are each rounded once to fp32.
+ * If found_inf != NULL and *found_inf != 0 (read on the device) the update
+ * is skipped: master / exp_avg / exp_avg_sq are left untouched.
+ * If param_bf16 != NULL, param_bf16[i] = bf16 round-to-nearest-even of the
+ * (new, or on a skip the unchanged) master[i] -- the low-precision copy
+ * that the all-gather moves ([FSDP] section 3.5); usually full + rank * S.
+ * grad, master, exp_avg, exp_avg_sq: device fp32[S], 16-byte aligned,
+ * master / exp_avg / exp_avg_sq distinct; param_bf16: device bf16[S]. */
+fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, const float* grad,
+                         float* master, float* exp_avg, float* exp_avg_sq,
+                         const int32_t* found_inf, uint16_t* param_bf16, void* stream);
+
+/* ------------------------------------------------------------------ unshard */
+
+/* The all-gather's data movement on one GPU: full[q*S + j] = shards[q][j]
+ * for every q with shards[q] != NULL and every j < S (bit copy).  A NULL
+ * entry leaves full[q*S, (q+1)*S) untouched (e.g. the rank's own shard,
+ * already written by fp_adamw_shard).  [DP] ZeRO-1 paragraph (gather the
+ * updated parameters) and ZeRO-3 paragraph (gather a unit before use);
+ * [GUIDE] section 5.1 (all-gather shares the reduced chunks).
+ * world in [1, FP_MAX_WORLD]; shards: host array of world device pointers
+ * to bf16[S]; full: device bf16[world * S], not overlapping the sources. */
+fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* const* shards,
+                     uint16_t* full, void* stream);
+
+/* ------------------------------------------------------------------ step */
+
+#define FP_STEP_EXACT_SKIP 0 /* default: on overflow nothing is updated    */
+#define FP_STEP_NO_SKIP 1    /* one fused pass; state updated regardless   */
+#define FP_STEP_KEEP_GRAD 2  /* also leave the reduced gradient in acc     */
+
+/* One rank's whole shard step for the last micro-batch: reduce (as
+ * fp_reduce_shard), AdamW with the bf16 cast into full + rank*S (as
+ * fp_adamw_shard), and the copy of every other rank's shard into full (as
+ * fp_unshard).  [DP] ZeRO-1 / ZeRO-2 step: reduce-scatter, update the
+ * slice, all-gather the updated parameters; [FSDP] section 3.1.
+ * flags:
+ *   FP_STEP_EXACT_SKIP -- the overflow check over the whole shard (with the
+ *     flag from earlier micro-batches) decides before any state is written;
+ *     on overflow master / exp_avg / exp_avg_sq are untouched and full
+ *     receives bf16 of the unchanged master.
+ *   FP_STEP_NO_SKIP -- reduce and update in one pass without a gate; the
+ *     flag is still reported (for callers without a loss scaler).
+ *   FP_STEP_KEEP_GRAD (may be or-ed in) -- acc holds the reduced gradient
+ *     afterwards; without it acc's contents afterwards are unspecified.
+ * On return *found_inf is the OR of its input and this call's check. */
+typedef struct fp_step_args {
+    int64_t shard;                 /* S */
+    int32_t world;                 /* N_d, in [1, FP_MAX_WORLD] */
+    int32_t rank;                  /* r, in [0, world) */
+    const uint16_t* const* grads;  /* host array: world device ptrs, bf16[S] */
+    float scale;                   /* normally 1 / (N_d * n_micro) */
+    int32_t accumulate;            /* 1 if acc holds earlier micro-batches */
+    float* acc;                    /* device fp32[S], 16-byte aligned */
+    float* master;                 /* device fp32[S] */
+    float* exp_avg;                /* device fp32[S] */
+    float* exp_avg_sq;             /* device fp32[S] */
+    fp_adamw_hparams hp;
+    const uint16_t* const* shards; /* host array: world device ptrs, bf16[S]; entry rank unused */
+    uint16_t* full;                /* device bf16[world * S] */
+    int32_t* found_inf;            /* device int32, required */
+    double* sq_norm;               /* device double, may be NULL */
+    void* workspace;               /* device, fp_workspace_bytes(); may be NULL if sq_norm is */
+    int32_t flags;
+} fp_step_args;
+
+fp_status fp_shard_step(const fp_step_args* args, void* stream);
+
+/* ------------------------------------------------------------------ helpers */
+
+/* Model-state bytes per GPU.  [DP] ZeRO figure (one formula per row) and
+ * [GUIDE] sections 6.1 and 7: parameters and gradients 2 bytes each,
+ * optimizer state k bytes per parameter, N = world:
+ *   stage 0 (replicated, DDP): 2psi + 2psi + k psi
+ *   stage 1 (optimizer state sharded): 2psi + 2psi + k psi / N
+ *   stage 2 (+ gradients): 2psi + (2psi + k psi) / N
+ *   stage 3 (+ parameters, FSDP full shard): (2psi + 2psi + k psi) / N
+ * FP_ERR_INVALID for another stage, psi < 0, k < 0 or world < 1. */
+fp_status fp_state_bytes(double psi, int32_t world, double k, int32_t stage, double* out);
+
+/* Static text for a status code. */
+const char* fp_status_string(fp_status status);
+
+/* Message of the calling thread's most recent failed call ("" if none). */
+const char* fp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLATPARAM_H */

@@ -1,0 +1,259 @@
+"""One rank's FSDP / ZeRO shard step on AMD Instinct MI355X (gfx950).
+
+A thin binding of libflatparam.so (include/flatparam.h): it checks and
+marshals torch tensors (device memory) and torch's current stream into
+the C ABI; every step of the path runs in the library's HIP kernels.
+
+    plan = Plan(shapes, world)            # FlatParameter geometry (host)
+    flat = plan.pack(tensors)             # flatten + concatenate + pad (GPU)
+    views = plan.views(flat)              # original tensors as views
+    reduce_shard(grads, acc, scale=...)   # bf16 -> fp32 reduce, overflow flag
+    adamw_shard(acc, master, m, v, ...)   # fp32 AdamW + bf16 cast
+    unshard(shards, full)                 # gather the bf16 shards
+    shard_step(...)                       # the whole step for the last micro-batch
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Optional, Sequence
+
+from . import _lib
+from ._lib import (FP_MAX_WORLD, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD,  # noqa: F401
+                   FP_STEP_NO_SKIP, FlatParamError, check, lib)
+
+__all__ = ["Plan", "reduce_shard", "adamw_shard", "unshard", "shard_step", "state_bytes",
+           "workspace_bytes", "new_workspace", "FlatParamError", "FP_STEP_EXACT_SKIP",
+           "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+_BF16_DTYPES = None
+
+
+def _bf16_dtypes():
+    global _BF16_DTYPES
+    if _BF16_DTYPES is None:
+        torch = _torch()
+        _BF16_DTYPES = tuple(d for d in (torch.bfloat16, torch.int16, getattr(torch, "uint16", None)) if d)
+    return _BF16_DTYPES
+
+
+def _stream(t):
+    return C.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev_ptr(t, dtypes, n, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {n}")
+    return t.data_ptr()
+
+
+def _f32(t, n, name):
+    return _dev_ptr(t, (_torch().float32,), n, name)
+
+
+def _bf16(t, n, name):
+    return _dev_ptr(t, _bf16_dtypes(), n, name)
+
+
+def _rank_ptrs(x, n, name, allow_none=False):
+    """Device pointers of N bf16 rows: a list of 1-D tensors or one [N, >=n] tensor."""
+    if hasattr(x, "dim") and x.dim() == 2:
+        if not x.is_cuda or x.dtype not in _bf16_dtypes() or x.stride(1) != 1 or x.shape[1] < n:
+            raise ValueError(f"{name}: need a device bf16 [N, >= {n}] tensor with unit column stride")
+        base, step = x.data_ptr(), x.stride(0) * x.element_size()
+        return [base + q * step for q in range(x.shape[0])]
+    ptrs = []
+    for q, t in enumerate(x):
+        if t is None:
+            if not allow_none:
+                raise ValueError(f"{name}[{q}] is None")
+            ptrs.append(None)
+        else:
+            ptrs.append(_bf16(t, n, f"{name}[{q}]"))
+    return ptrs
+
+
+def _ptr_table(ptrs):
+    return (C.c_void_p * len(ptrs))(*[p if p is not None else None for p in ptrs])
+
+
+# ------------------------------------------------------------------ plan
+class Plan:
+    """FlatParameter geometry of a unit: tensor shapes in order and N_d."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], world: int):
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.world = int(world)
+        ndims = (C.c_int32 * len(self.shapes))(*[len(s) for s in self.shapes])
+        flat_dims = [d for s in self.shapes for d in s]
+        dims = (C.c_int64 * max(1, len(flat_dims)))(*flat_dims)
+        h = C.c_void_p()
+        check(lib().fp_plan_create(len(self.shapes), ndims, dims, self.world, C.byref(h)))
+        self._h = h
+        t, p, s = C.c_int64(), C.c_int64(), C.c_int64()
+        check(lib().fp_plan_info(self._h, C.byref(t), C.byref(p), C.byref(s)))
+        self.numel, self.padded, self.shard = t.value, p.value, s.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().fp_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def view_descriptors(self, rank: int = -1):
+        """One dict per tensor: buf_offset, numel, tensor_offset, shape (see fp_unpack_views)."""
+        n = len(self.shapes)
+        out = (_lib.fp_view * n)()
+        n_out = C.c_int32()
+        check(lib().fp_unpack_views(self._h, int(rank), out, n, C.byref(n_out)))
+        return [{"tensor": v.tensor, "buf_offset": v.buf_offset, "numel": v.numel,
+                 "tensor_offset": v.tensor_offset, "shape": tuple(v.shape[:v.ndim])} for v in out]
+
+    def pack(self, tensors, flat=None):
+        """FlatParameter of `tensors` (one 2- or 4-byte dtype) on the GPU."""
+        torch = _torch()
+        if len(tensors) != len(self.shapes):
+            raise ValueError("tensor count differs from the plan")
+        dtype = tensors[0].dtype
+        esize = tensors[0].element_size()
+        ptrs = []
+        for i, (t, s) in enumerate(zip(tensors, self.shapes)):
+            if tuple(t.shape) != s or t.dtype != dtype:
+                raise ValueError(f"tensor {i}: shape {tuple(t.shape)} / dtype {t.dtype} differ from the plan")
+            ptrs.append(_dev_ptr(t, (dtype,), math.prod(s), f"tensors[{i}]") if t.numel() else None)
+        if flat is None:
+            flat = torch.empty(self.padded, dtype=dtype, device=tensors[0].device)
+        fptr = _dev_ptr(flat, (dtype,), self.padded, "flat")
+        check(lib().fp_pack(self._h, esize, _ptr_table(ptrs), C.c_void_p(fptr), _stream(flat)))
+        return flat
+
+    def views(self, buf, rank: int = -1):
+        """Views of the original tensors on `buf` (aliasing, no copy).
+
+        rank = -1: `buf` is the FlatParameter; each view has its tensor's shape.
+        rank = q : `buf` is rank q's shard; each view is a 1-D fragment, empty
+                   when the rank holds none of the tensor.
+        """
+        out = []
+        for d in self.view_descriptors(rank):
+            v = buf.narrow(0, d["buf_offset"], d["numel"])
+            out.append(v.view(d["shape"]) if rank < 0 else v)
+        return out
+
+
+# ------------------------------------------------------------------ reduce
+def workspace_bytes() -> int:
+    return int(lib().fp_workspace_bytes())
+
+
+def new_workspace(device):
+    torch = _torch()
+    return torch.zeros(workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def reduce_shard(grads, acc, *, scale: float, accumulate: bool = False, found_inf=None,
+                 sq_norm=None, workspace=None):
+    """acc (= or +=) scale * sum of the ranks' bf16 gradients, fixed rank order."""
+    torch = _torch()
+    S = acc.numel()
+    ptrs = _rank_ptrs(grads, S, "grads")
+    fi = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf") if found_inf is not None else None
+    sq = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
+    ws = _dev_ptr(workspace, (torch.uint8,), workspace_bytes(), "workspace") if workspace is not None else None
+    check(lib().fp_reduce_shard(S, len(ptrs), _ptr_table(ptrs), float(scale), int(bool(accumulate)),
+                                C.c_void_p(_f32(acc, S, "acc")), fi, sq, ws, _stream(acc)))
+    return acc
+
+
+# ------------------------------------------------------------------ adamw
+def _hparams(lr, beta1, beta2, eps, weight_decay, step):
+    return _lib.fp_adamw_hparams(float(lr), float(beta1), float(beta2), float(eps),
+                                 float(weight_decay), int(step))
+
+
+def adamw_shard(grad, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps, weight_decay,
+                step: int, found_inf=None, param_bf16=None):
+    """In-place AdamW on fp32 master / exp_avg / exp_avg_sq; bf16 copy to param_bf16."""
+    torch = _torch()
+    S = master.numel()
+    hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
+    fi = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf") if found_inf is not None else None
+    out = _bf16(param_bf16, S, "param_bf16") if param_bf16 is not None else None
+    check(lib().fp_adamw_shard(S, C.byref(hp), _f32(grad, S, "grad"), _f32(master, S, "master"),
+                               _f32(exp_avg, S, "exp_avg"), _f32(exp_avg_sq, S, "exp_avg_sq"),
+                               fi, out, _stream(master)))
+
+
+# ------------------------------------------------------------------ unshard
+def unshard(shards, full):
+    """full[q*S:(q+1)*S] = shards[q]; a None entry leaves that range untouched."""
+    world = len(shards) if not hasattr(shards, "dim") else shards.shape[0]
+    S = full.numel() // world
+    if S * world != full.numel():
+        raise ValueError("full is not world * S elements")
+    ptrs = _rank_ptrs(shards, S, "shards", allow_none=True)
+    check(lib().fp_unshard(S, world, _ptr_table(ptrs), C.c_void_p(_bf16(full, S * world, "full")),
+                           _stream(full)))
+    return full
+
+
+# ------------------------------------------------------------------ step
+def shard_step(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *, scale: float,
+               lr, beta1, beta2, eps, weight_decay, step: int, found_inf, accumulate: bool = False,
+               sq_norm=None, workspace=None, flags: int = FP_STEP_EXACT_SKIP):
+    """Reduce (last micro-batch) + AdamW + bf16 cast + unshard for this rank."""
+    torch = _torch()
+    S = master.numel()
+    gptr = _rank_ptrs(grads, S, "grads")
+    world = len(gptr)
+    sptr = _rank_ptrs(shards, S, "shards", allow_none=True)
+    if len(sptr) != world:
+        raise ValueError("shards and grads differ in length")
+    a = _lib.fp_step_args()
+    gt, st = _ptr_table(gptr), _ptr_table(sptr)
+    a.shard, a.world, a.rank = S, world, int(rank)
+    a.grads = C.cast(gt, C.c_void_p)
+    a.scale, a.accumulate = float(scale), int(bool(accumulate))
+    a.acc = _f32(acc, S, "acc")
+    a.master = _f32(master, S, "master")
+    a.exp_avg = _f32(exp_avg, S, "exp_avg")
+    a.exp_avg_sq = _f32(exp_avg_sq, S, "exp_avg_sq")
+    a.hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
+    a.shards = C.cast(st, C.c_void_p)
+    a.full = _bf16(full, S * world, "full")
+    a.found_inf = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf")
+    a.sq_norm = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
+    a.workspace = (_dev_ptr(workspace, (torch.uint8,), workspace_bytes(), "workspace")
+                   if workspace is not None else None)
+    a.flags = int(flags)
+    check(lib().fp_shard_step(C.byref(a), _stream(master)))
+
+
+# ------------------------------------------------------------------ helpers
+def state_bytes(psi: float, world: int, k: float = 12.0, stage: int = 3) -> float:
+    """Model-state bytes per GPU for ZeRO stage 0..3 (fp_state_bytes)."""
+    out = C.c_double()
+    check(lib().fp_state_bytes(float(psi), int(world), float(k), int(stage), C.byref(out)))
+    return out.value

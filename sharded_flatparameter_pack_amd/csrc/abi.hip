@@ -1,0 +1,556 @@
+// abi.hip -- the extern "C" entry points of libflatparam.so: argument
+// validation, FlatParameter plans, launch geometry and error reporting.
+// Every check runs before anything is enqueued, so a rejected call leaves
+// the device untouched.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "fp_internal.h"
+
+using namespace fpk;
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+fp_status fail(fp_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fp_status device_fail(hipError_t e, const char* what) {
+    return fail(FP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int clamp_grid(int64_t want, int64_t cap) {
+    if (want < 1) want = 1;
+    if (want > cap) want = cap;
+    return (int)want;
+}
+
+// Grid of a grid-stride stream over S elements in 8-element chunks.
+int stream_grid(int64_t shard) { return clamp_grid(ceil_div(shard >> 3, kThreads), kMaxGrid); }
+
+fp_status check_hparams(const fp_adamw_hparams* hp, AdamCoef* c) {
+    if (hp == nullptr) return fail(FP_ERR_INVALID, "hparams is NULL");
+    if (hp->step < 1) return fail(FP_ERR_RANGE, "step must be >= 1 (got %lld)", (long long)hp->step);
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+        return fail(FP_ERR_RANGE, "betas must lie in [0, 1)");
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) ||
+        hp->eps < 0.0)
+        return fail(FP_ERR_RANGE, "lr, eps and weight_decay must be finite, eps >= 0");
+    c->decay = 1.0 - hp->lr * hp->weight_decay;
+    c->beta1 = hp->beta1;
+    c->one_m_beta1 = 1.0 - hp->beta1;
+    c->beta2 = hp->beta2;
+    c->one_m_beta2 = 1.0 - hp->beta2;
+    c->bias1 = 1.0 - std::pow(hp->beta1, (double)hp->step);
+    c->bias2 = 1.0 - std::pow(hp->beta2, (double)hp->step);
+    c->lr = hp->lr;
+    c->eps = hp->eps;
+    return FP_OK;
+}
+
+fp_status check_ptr_table(const uint16_t* const* t, int32_t world, int64_t shard, bool allow_null,
+                          const char* name) {
+    if (t == nullptr) return fail(FP_ERR_INVALID, "%s table is NULL", name);
+    for (int32_t q = 0; q < world; ++q) {
+        if (t[q] == nullptr) {
+            if (allow_null || shard == 0) continue;
+            return fail(FP_ERR_INVALID, "%s[%d] is NULL", name, q);
+        }
+        if (!aligned(t[q], 2)) return fail(FP_ERR_ALIGN, "%s[%d] is not 2-byte aligned", name, q);
+    }
+    return FP_OK;
+}
+
+fp_status check_f32(const void* p, int64_t shard, const char* name) {
+    if (p == nullptr && shard > 0) return fail(FP_ERR_INVALID, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(FP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return FP_OK;
+}
+
+fp_status check_world(int32_t world) {
+    if (world < 1 || world > FP_MAX_WORLD)
+        return fail(FP_ERR_RANGE, "world %d outside [1, %d]", world, FP_MAX_WORLD);
+    return FP_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------- plan
+
+namespace {
+struct DeviceTables {
+    int device = -1;
+    int64_t* offsets = nullptr;
+    int32_t* group_first = nullptr;
+    const void** src = nullptr;        // device copy of the per-call pointer table
+    const void** src_staging = nullptr; // pinned host staging of that table
+    hipEvent_t uploaded = nullptr;      // completion of the last upload from staging
+};
+}  // namespace
+
+struct fp_plan {
+    int32_t n = 0;
+    int32_t world = 1;
+    std::vector<int32_t> ndims;
+    std::vector<int64_t> dim_start;  // first dim of tensor i in `dims`
+    std::vector<int64_t> dims;
+    std::vector<int64_t> numel;
+    std::vector<int64_t> offsets;    // n + 1
+    std::vector<int32_t> group_first;
+    int64_t total = 0, padded = 0, shard = 0;
+    std::mutex mu;
+    std::vector<DeviceTables> tables;
+};
+
+namespace {
+void free_tables(DeviceTables& t) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (t.device >= 0) (void)hipSetDevice(t.device);
+    if (t.uploaded) (void)hipEventSynchronize(t.uploaded), (void)hipEventDestroy(t.uploaded);
+    if (t.offsets) (void)hipFree(t.offsets);
+    if (t.group_first) (void)hipFree(t.group_first);
+    if (t.src) (void)hipFree((void*)t.src);
+    if (t.src_staging) (void)hipHostFree((void*)t.src_staging);
+    if (cur >= 0) (void)hipSetDevice(cur);
+    t = DeviceTables();
+}
+}  // namespace
+
+extern "C" fp_status fp_plan_create(int32_t n_tensors, const int32_t* ndims, const int64_t* shapes,
+                                    int32_t world, fp_plan** out) {
+    if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (n_tensors < 1) return fail(FP_ERR_RANGE, "n_tensors must be >= 1");
+    if (ndims == nullptr) return fail(FP_ERR_INVALID, "ndims is NULL");
+    if (world < 1 || world > (1 << 20)) return fail(FP_ERR_RANGE, "world %d outside [1, 2^20]", world);
+    int64_t n_dims = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (ndims[i] < 0 || ndims[i] > FP_MAX_NDIM)
+            return fail(FP_ERR_RANGE, "tensor %d: ndim %d outside [0, %d]", i, ndims[i], FP_MAX_NDIM);
+        n_dims += ndims[i];
+    }
+    if (n_dims > 0 && shapes == nullptr) return fail(FP_ERR_INVALID, "shapes is NULL");
+    fp_plan* p = new (std::nothrow) fp_plan();
+    if (p == nullptr) return fail(FP_ERR_DEVICE, "out of host memory");
+    p->n = n_tensors;
+    p->world = world;
+    p->ndims.assign(ndims, ndims + n_tensors);
+    p->dims.assign(shapes, shapes + n_dims);
+    p->offsets.push_back(0);
+    const int64_t limit = (int64_t)1 << 62;
+    int64_t d = 0, total = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        p->dim_start.push_back(d);
+        int64_t ne = 1;
+        for (int32_t k = 0; k < ndims[i]; ++k, ++d) {
+            const int64_t s = shapes[d];
+            if (s < 0) {
+                delete p;
+                return fail(FP_ERR_RANGE, "tensor %d: negative dimension", i);
+            }
+            if (s != 0 && ne > limit / s) {
+                delete p;
+                return fail(FP_ERR_RANGE, "tensor %d: too many elements", i);
+            }
+            ne *= s;
+        }
+        if (total > limit - ne) {
+            delete p;
+            return fail(FP_ERR_RANGE, "FlatParameter exceeds 2^62 elements");
+        }
+        total += ne;
+        p->numel.push_back(ne);
+        p->offsets.push_back(total);
+    }
+    p->total = total;
+    p->padded = ceil_div(total, world) * world;
+    p->shard = p->padded / world;
+    // first tensor overlapping each pack workgroup's element range
+    const int64_t n_groups = ceil_div(p->padded, kPackBlockElems);
+    p->group_first.resize(n_groups + 1);
+    int32_t t = 0;
+    for (int64_t g = 0; g <= n_groups; ++g) {
+        const int64_t e = g * kPackBlockElems;
+        while (t < n_tensors && p->offsets[t + 1] <= e) ++t;  // also skips empty tensors
+        p->group_first[g] = e < total ? t : n_tensors;
+    }
+    *out = p;
+    return FP_OK;
+}
+
+extern "C" void fp_plan_destroy(fp_plan* plan) {
+    if (plan == nullptr) return;
+    for (auto& t : plan->tables) free_tables(t);
+    delete plan;
+}
+
+extern "C" fp_status fp_plan_info(const fp_plan* plan, int64_t* numel, int64_t* padded, int64_t* shard) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (numel) *numel = plan->total;
+    if (padded) *padded = plan->padded;
+    if (shard) *shard = plan->shard;
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------- views
+
+extern "C" fp_status fp_unpack_views(const fp_plan* plan, int32_t rank, fp_view* out, int32_t cap,
+                                     int32_t* n_out) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (rank < -1 || rank >= plan->world) return fail(FP_ERR_RANGE, "rank %d outside [-1, %d)", rank, plan->world);
+    if (n_out) *n_out = plan->n;
+    if (cap < plan->n) return fail(FP_ERR_RANGE, "cap %d < %d tensors", cap, plan->n);
+    if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+    const int64_t S = plan->shard;
+    for (int32_t i = 0; i < plan->n; ++i) {
+        fp_view v;
+        std::memset(&v, 0, sizeof v);
+        v.tensor = i;
+        const int64_t o = plan->offsets[i], ne = plan->numel[i];
+        if (rank < 0) {
+            v.ndim = plan->ndims[i];
+            v.buf_offset = o;
+            v.numel = ne;
+            for (int32_t k = 0; k < v.ndim; ++k) v.shape[k] = plan->dims[plan->dim_start[i] + k];
+        } else {
+            const int64_t lo = o > rank * S ? o : rank * S;
+            const int64_t hi = (o + ne) < (rank + 1) * S ? (o + ne) : (rank + 1) * S;
+            v.ndim = 1;
+            if (hi > lo) {
+                v.buf_offset = lo - rank * S;
+                v.numel = hi - lo;
+                v.tensor_offset = lo - o;
+                v.shape[0] = hi - lo;
+            }
+        }
+        out[i] = v;
+    }
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------- pack
+
+extern "C" fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const* src, void* flat,
+                             void* stream) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
+    if (src == nullptr) return fail(FP_ERR_INVALID, "src table is NULL");
+    if (flat == nullptr) return fail(FP_ERR_INVALID, "flat is NULL");
+    if (!aligned(flat, 16)) return fail(FP_ERR_ALIGN, "flat is not 16-byte aligned");
+    const int64_t flat_bytes = plan->padded * elem_size;
+    for (int32_t i = 0; i < plan->n; ++i) {
+        if (plan->numel[i] == 0) continue;
+        if (src[i] == nullptr) return fail(FP_ERR_INVALID, "src[%d] is NULL", i);
+        if (!aligned(src[i], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "src[%d] misaligned", i);
+        if (overlap(src[i], plan->numel[i] * elem_size, flat, flat_bytes))
+            return fail(FP_ERR_INVALID, "src[%d] overlaps flat", i);
+    }
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    DeviceTables* t = nullptr;
+    for (auto& x : plan->tables)
+        if (x.device == device) t = &x;
+    const int64_t n_groups = (int64_t)plan->group_first.size() - 1;
+    if (t == nullptr) {  // first pack on this device: allocate and upload the static tables
+        DeviceTables nt;
+        nt.device = device;
+        const size_t off_b = (plan->n + 1) * sizeof(int64_t);
+        const size_t grp_b = (n_groups + 1) * sizeof(int32_t);
+        const size_t src_b = plan->n * sizeof(void*);
+        if ((e = hipMalloc((void**)&nt.offsets, off_b)) != hipSuccess ||
+            (e = hipMalloc((void**)&nt.group_first, grp_b)) != hipSuccess ||
+            (e = hipMalloc((void**)&nt.src, src_b)) != hipSuccess ||
+            (e = hipHostMalloc((void**)&nt.src_staging, src_b, hipHostMallocDefault)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&nt.uploaded, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipMemcpy(nt.offsets, plan->offsets.data(), off_b, hipMemcpyHostToDevice)) != hipSuccess ||
+            (e = hipMemcpy(nt.group_first, plan->group_first.data(), grp_b, hipMemcpyHostToDevice)) !=
+                hipSuccess) {
+            free_tables(nt);
+            return device_fail(e, "allocating the plan's device tables");
+        }
+        plan->tables.push_back(nt);
+        t = &plan->tables.back();
+    }
+    // the staging buffer may still feed the previous call's upload
+    if ((e = hipEventSynchronize(t->uploaded)) != hipSuccess) return device_fail(e, "hipEventSynchronize");
+    for (int32_t i = 0; i < plan->n; ++i) t->src_staging[i] = src[i];
+    if ((e = hipMemcpyAsync((void*)t->src, (const void*)t->src_staging, plan->n * sizeof(void*),
+                            hipMemcpyHostToDevice, s)) != hipSuccess)
+        return device_fail(e, "uploading the source pointer table");
+    if ((e = hipEventRecord(t->uploaded, s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    PackArgs a;
+    a.offsets = t->offsets;
+    a.group_first = t->group_first;
+    a.src = t->src;
+    a.flat = flat;
+    a.total = plan->total;
+    a.padded = plan->padded;
+    a.n_tensors = plan->n;
+    if (n_groups == 0) return FP_OK;
+    if ((e = launch_pack(a, elem_size, n_groups, s)) != hipSuccess) return device_fail(e, "pack launch");
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------- reduce
+
+extern "C" int64_t fp_workspace_bytes(void) { return kWorkspaceBytes; }
+
+extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_t* const* grads,
+                                     float scale, int32_t accumulate, float* acc, int32_t* found_inf,
+                                     double* sq_norm, void* workspace, void* stream) {
+    fp_status st;
+    if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
+    if ((st = check_world(world)) != FP_OK) return st;
+    if ((st = check_ptr_table(grads, world, shard, false, "grads")) != FP_OK) return st;
+    if ((st = check_f32(acc, shard, "acc")) != FP_OK) return st;
+    if (found_inf != nullptr && !aligned(found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
+    if (sq_norm != nullptr) {
+        if (!aligned(sq_norm, 8)) return fail(FP_ERR_ALIGN, "sq_norm misaligned");
+        if (workspace == nullptr) return fail(FP_ERR_INVALID, "sq_norm needs a workspace");
+        if (!aligned(workspace, 16)) return fail(FP_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    for (int32_t q = 0; q < world; ++q)
+        if (overlap(grads[q], shard * 2, acc, shard * 4)) return fail(FP_ERR_INVALID, "grads[%d] overlaps acc", q);
+    ReduceArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int32_t q = 0; q < world; ++q) a.grads[q] = grads[q];
+    a.acc = acc;
+    a.found_inf = found_inf;
+    a.partials = sq_norm != nullptr ? static_cast<double*>(workspace) : nullptr;
+    a.shard = shard;
+    a.scale = scale;
+    a.world = world;
+    a.accumulate = accumulate ? 1 : 0;
+    const int grid = stream_grid(shard);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_reduce(a, grid, s);
+    if (e != hipSuccess) return device_fail(e, "reduce launch");
+    if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, sq_norm, s)) != hipSuccess)
+        return device_fail(e, "norm launch");
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------- adamw
+
+extern "C" fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, const float* grad,
+                                    float* master, float* exp_avg, float* exp_avg_sq,
+                                    const int32_t* found_inf, uint16_t* param_bf16, void* stream) {
+    fp_status st;
+    if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
+    AdamArgs a;
+    std::memset(&a, 0, sizeof a);
+    if ((st = check_hparams(hp, &a.c)) != FP_OK) return st;
+    if ((st = check_f32(grad, shard, "grad")) != FP_OK || (st = check_f32(master, shard, "master")) != FP_OK ||
+        (st = check_f32(exp_avg, shard, "exp_avg")) != FP_OK ||
+        (st = check_f32(exp_avg_sq, shard, "exp_avg_sq")) != FP_OK)
+        return st;
+    const int64_t b = shard * 4;
+    if (overlap(master, b, exp_avg, b) || overlap(master, b, exp_avg_sq, b) ||
+        overlap(exp_avg, b, exp_avg_sq, b) || overlap(grad, b, master, b) || overlap(grad, b, exp_avg, b) ||
+        overlap(grad, b, exp_avg_sq, b))
+        return fail(FP_ERR_INVALID, "grad / master / exp_avg / exp_avg_sq overlap");
+    if (param_bf16 != nullptr) {
+        if (!aligned(param_bf16, 2)) return fail(FP_ERR_ALIGN, "param_bf16 misaligned");
+        if (overlap(param_bf16, shard * 2, master, b) || overlap(param_bf16, shard * 2, exp_avg, b) ||
+            overlap(param_bf16, shard * 2, exp_avg_sq, b) || overlap(param_bf16, shard * 2, grad, b))
+            return fail(FP_ERR_INVALID, "param_bf16 overlaps the fp32 buffers");
+    }
+    if (found_inf != nullptr && !aligned(found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
+    a.grad = grad;
+    a.master = master;
+    a.exp_avg = exp_avg;
+    a.exp_avg_sq = exp_avg_sq;
+    a.param_bf16 = param_bf16;
+    a.found_inf = found_inf;
+    a.shard = shard;
+    hipError_t e = launch_adamw(a, stream_grid(shard), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "adamw launch");
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------- unshard
+
+extern "C" fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* const* shards,
+                                uint16_t* full, void* stream) {
+    fp_status st;
+    if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
+    if ((st = check_world(world)) != FP_OK) return st;
+    if ((st = check_ptr_table(shards, world, shard, true, "shards")) != FP_OK) return st;
+    if (full == nullptr && shard > 0) return fail(FP_ERR_INVALID, "full is NULL");
+    if (!aligned(full, 2)) return fail(FP_ERR_ALIGN, "full misaligned");
+    for (int32_t q = 0; q < world; ++q)
+        if (shards[q] != nullptr && overlap(shards[q], shard * 2, full, shard * world * 2))
+            return fail(FP_ERR_INVALID, "shards[%d] overlaps full", q);
+    if (shard == 0) return FP_OK;
+    UnshardArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int32_t q = 0; q < world; ++q) a.shards[q] = shards[q];
+    a.full = full;
+    a.shard = shard;
+    a.world = world;
+    const int gx = clamp_grid(ceil_div(ceil_div(shard, 8), kThreads), kMaxGrid / world > 0 ? kMaxGrid / world : 1);
+    hipError_t e = launch_unshard(a, gx, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "unshard launch");
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------- step
+
+extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
+    if (args == nullptr) return fail(FP_ERR_INVALID, "args is NULL");
+    const fp_step_args& x = *args;
+    fp_status st;
+    const int64_t S = x.shard;
+    if (S < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
+    if ((st = check_world(x.world)) != FP_OK) return st;
+    if (x.rank < 0 || x.rank >= x.world) return fail(FP_ERR_RANGE, "rank %d outside [0, %d)", x.rank, x.world);
+    if (x.flags & ~(FP_STEP_NO_SKIP | FP_STEP_KEEP_GRAD)) return fail(FP_ERR_INVALID, "unknown flags");
+    StepArgs a;
+    std::memset(&a, 0, sizeof a);
+    if ((st = check_hparams(&x.hp, &a.c)) != FP_OK) return st;
+    if ((st = check_ptr_table(x.grads, x.world, S, false, "grads")) != FP_OK) return st;
+    if ((st = check_ptr_table(x.shards, x.world, S, true, "shards")) != FP_OK) return st;
+    for (int32_t q = 0; q < x.world; ++q)
+        if (q != x.rank && x.shards[q] == nullptr && S > 0) return fail(FP_ERR_INVALID, "shards[%d] is NULL", q);
+    if ((st = check_f32(x.acc, S, "acc")) != FP_OK || (st = check_f32(x.master, S, "master")) != FP_OK ||
+        (st = check_f32(x.exp_avg, S, "exp_avg")) != FP_OK || (st = check_f32(x.exp_avg_sq, S, "exp_avg_sq")) != FP_OK)
+        return st;
+    if (x.full == nullptr && S > 0) return fail(FP_ERR_INVALID, "full is NULL");
+    if (!aligned(x.full, 2)) return fail(FP_ERR_ALIGN, "full misaligned");
+    if (x.found_inf == nullptr) return fail(FP_ERR_INVALID, "found_inf is NULL");
+    if (!aligned(x.found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
+    if (x.sq_norm != nullptr) {
+        if (!aligned(x.sq_norm, 8)) return fail(FP_ERR_ALIGN, "sq_norm misaligned");
+        if (x.workspace == nullptr || !aligned(x.workspace, 16))
+            return fail(FP_ERR_INVALID, "sq_norm needs a 16-byte aligned workspace");
+    }
+    const int64_t b4 = S * 4, b2 = S * 2, bf = S * x.world * 2;
+    const void* f32s[4] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(f32s[i], b4, f32s[j], b4)) return fail(FP_ERR_INVALID, "fp32 buffers overlap");
+        if (overlap(f32s[i], b4, x.full, bf)) return fail(FP_ERR_INVALID, "an fp32 buffer overlaps full");
+    }
+    for (int32_t q = 0; q < x.world; ++q) {
+        if (overlap(x.grads[q], b2, x.full, bf)) return fail(FP_ERR_INVALID, "grads[%d] overlaps full", q);
+        for (int i = 0; i < 4; ++i)
+            if (overlap(x.grads[q], b2, f32s[i], b4)) return fail(FP_ERR_INVALID, "grads[%d] overlaps state", q);
+        if (q != x.rank && overlap(x.shards[q], b2, x.full, bf))
+            return fail(FP_ERR_INVALID, "shards[%d] overlaps full", q);
+    }
+
+    const bool fused = (x.flags & FP_STEP_NO_SKIP) != 0;
+    for (int32_t q = 0; q < x.world; ++q) {
+        a.grads[q] = x.grads[q];
+        a.shards[q] = q == x.rank ? nullptr : x.shards[q];
+    }
+    a.acc = x.acc;
+    a.master = x.master;
+    a.exp_avg = x.exp_avg;
+    a.exp_avg_sq = x.exp_avg_sq;
+    a.full = x.full;
+    a.found_inf = x.found_inf;
+    a.partials = x.sq_norm != nullptr ? static_cast<double*>(x.workspace) : nullptr;
+    a.shard = S;
+    a.scale = x.scale;
+    a.world = x.world;
+    a.rank = x.rank;
+    a.accumulate = x.accumulate ? 1 : 0;
+    a.keep_grad = (x.flags & FP_STEP_KEEP_GRAD) ? 1 : 0;
+
+    // Split one launch between the reduce role and the copy role in
+    // proportion to the bytes each moves per shard element.
+    const int64_t n = x.world;
+    const double reduce_bytes = 2.0 * n + (a.accumulate ? 4 : 0) +
+                                (fused ? 24.0 + 2.0 + (a.keep_grad ? 4 : 0) : 4.0);
+    const double copy_bytes = 4.0 * (n - 1);
+    const int64_t reduce_need = ceil_div(ceil_div(S, 8), kThreads);
+    const int64_t copy_need = n > 1 ? ceil_div((n - 1) * ceil_div(S, 8), kThreads) : 0;
+    int64_t g_r = (int64_t)std::llround(kMaxGrid * reduce_bytes / (reduce_bytes + copy_bytes));
+    g_r = g_r < 1 ? 1 : (g_r > reduce_need ? reduce_need : g_r);
+    if (g_r < 1) g_r = 1;
+    int64_t g_u = n > 1 ? kMaxGrid - g_r : 0;
+    if (g_u > copy_need) g_u = copy_need;
+    if (n > 1 && g_u < 1) g_u = 1;
+    a.reduce_groups = (int32_t)g_r;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_step_phase1(a, (int)(g_r + g_u), fused, s);
+    if (e != hipSuccess) return device_fail(e, "step launch");
+    if (fused) {
+        if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)g_r, x.sq_norm, s)) != hipSuccess)
+            return device_fail(e, "norm launch");
+        return FP_OK;
+    }
+    AdamArgs d;
+    std::memset(&d, 0, sizeof d);
+    d.grad = x.acc;
+    d.master = x.master;
+    d.exp_avg = x.exp_avg;
+    d.exp_avg_sq = x.exp_avg_sq;
+    d.param_bf16 = x.full + (int64_t)x.rank * S;
+    d.found_inf = x.found_inf;
+    d.shard = S;
+    d.c = a.c;
+    d.partials = a.partials;
+    d.sq_norm = x.sq_norm;
+    d.n_partials = (int32_t)g_r;
+    if ((e = launch_adamw(d, stream_grid(S), s)) != hipSuccess) return device_fail(e, "adamw launch");
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------- helpers
+
+extern "C" fp_status fp_state_bytes(double psi, int32_t world, double k, int32_t stage, double* out) {
+    if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+    if (!(psi >= 0.0) || !(k >= 0.0) || world < 1) return fail(FP_ERR_INVALID, "psi, k >= 0 and world >= 1");
+    const double n = world;
+    switch (stage) {
+        case 0: *out = (2.0 + 2.0 + k) * psi; break;
+        case 1: *out = 4.0 * psi + k * psi / n; break;
+        case 2: *out = 2.0 * psi + (2.0 + k) * psi / n; break;
+        case 3: *out = (4.0 + k) * psi / n; break;
+        default: return fail(FP_ERR_INVALID, "stage %d outside [0, 3]", stage);
+    }
+    return FP_OK;
+}
+
+extern "C" const char* fp_status_string(fp_status status) {
+    switch (status) {
+        case FP_OK: return "ok";
+        case FP_ERR_INVALID: return "invalid argument";
+        case FP_ERR_RANGE: return "argument out of range";
+        case FP_ERR_ALIGN: return "misaligned pointer";
+        case FP_ERR_DEVICE: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* fp_last_error(void) { return g_error; }

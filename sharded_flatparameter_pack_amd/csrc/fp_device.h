@@ -1,0 +1,109 @@
+// fp_device.h -- device helpers for the gfx950 kernels: bf16 conversions,
+// realigning 16-byte loads, 16-byte stores to 2-byte-aligned addresses, and
+// wave / workgroup reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp_internal.h"
+
+namespace fpk {
+
+// bf16 -> fp32 is exact: the bf16 pattern is the upper half of the fp32 one.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (gfx950 converts two values with one
+// v_cvt_pk_bf16_f32); NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo;
+    const __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 w, float f[8]) {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+    f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+    f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+__device__ __forceinline__ uint4 f32x8_to_bf16(const float f[8]) {
+    return make_uint4(bf16x2(f[0], f[1]), bf16x2(f[2], f[3]),
+                      bf16x2(f[4], f[5]), bf16x2(f[6], f[7]));
+}
+
+// 16 bytes starting at any 2-byte-aligned address.  A misaligned address is
+// served by the two aligned 16-byte words that hold the wanted bytes (both
+// hold at least one wanted byte, so neither leaves the mapped pages of the
+// buffer) and a byte funnel shift (v_alignbyte_b32).
+__device__ __forceinline__ uint4 load16_any(const void* p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t mis = static_cast<uint32_t>(a & 15u);
+    if (mis == 0) return *reinterpret_cast<const uint4*>(p);
+    const uint4* base = reinterpret_cast<const uint4*>(a - mis);
+    const uint4 lo = base[0];
+    const uint4 hi = base[1];
+    const uint32_t ds = mis >> 2;        // whole dwords to skip
+    const uint32_t bs = mis & 3u;        // then bytes to skip
+    uint32_t w0, w1, w2, w3, w4;
+    if (ds == 0)      { w0 = lo.x; w1 = lo.y; w2 = lo.z; w3 = lo.w; w4 = hi.x; }
+    else if (ds == 1) { w0 = lo.y; w1 = lo.z; w2 = lo.w; w3 = hi.x; w4 = hi.y; }
+    else if (ds == 2) { w0 = lo.z; w1 = lo.w; w2 = hi.x; w3 = hi.y; w4 = hi.z; }
+    else              { w0 = lo.w; w1 = hi.x; w2 = hi.y; w3 = hi.z; w4 = hi.w; }
+    return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, bs), __builtin_amdgcn_alignbyte(w2, w1, bs),
+                      __builtin_amdgcn_alignbyte(w3, w2, bs), __builtin_amdgcn_alignbyte(w4, w3, bs));
+}
+
+// 16 bytes to any 2-byte-aligned address: one dwordx4 store when aligned,
+// else four dword or eight short stores (all inside the 16 target bytes).
+__device__ __forceinline__ void store16_any(void* p, const uint4 v) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if ((a & 15u) == 0) {
+        *reinterpret_cast<uint4*>(p) = v;
+    } else if ((a & 3u) == 0) {
+        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+        q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+    } else {
+        uint16_t* q = reinterpret_cast<uint16_t*>(p);
+        q[0] = (uint16_t)v.x; q[1] = (uint16_t)(v.x >> 16);
+        q[2] = (uint16_t)v.y; q[3] = (uint16_t)(v.y >> 16);
+        q[4] = (uint16_t)v.z; q[5] = (uint16_t)(v.z >> 16);
+        q[6] = (uint16_t)v.w; q[7] = (uint16_t)(v.w >> 16);
+    }
+}
+
+__device__ __forceinline__ bool finite_f32(float x) {
+    return (__float_as_uint(x) & 0x7F800000u) != 0x7F800000u;
+}
+
+// Sum over the 64 lanes of a wave (butterfly; the same tree every call).
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Sum over the workgroup in a fixed order; the result is valid in thread 0.
+__device__ __forceinline__ double group_sum(double x) {
+    __shared__ double lds[kWaves];
+    x = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) r += lds[w];
+    }
+    return r;
+}
+
+// Raise the overflow flag if any lane of the wave saw a non-finite value.
+// The flag is only ever set to 1, so concurrent stores of 1 are benign.
+__device__ __forceinline__ void flag_if_any(bool bad, int32_t* flag) {
+    if (flag != nullptr && __ballot(bad) != 0ull && (threadIdx.x & 63) == 0) *flag = 1;
+}
+
+}  // namespace fpk

@@ -28,3 +28,27 @@ def load_golden(name):
     import json
     with open(os.path.join(GOLDEN, name)) as f:
         return json.load(f)
+
+
+def _gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(autouse=True)
+def _skip_gpu_without_device(request):
+    if "gpu" in request.keywords and not _gpu_available():
+        pytest.skip("no GPU in this environment")
+
+
+@pytest.fixture(scope="session")
+def fp():
+    """The HIP library's binding; raises if libflatparam.so is not built."""
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    import sharded_flatparameter_pack_amd as fp
+    fp.lib()
+    return fp
