@@ -36,7 +36,9 @@
  *   enqueued, except FP_ERR_DEVICE after a failed launch.  Faults inside a
  *   kernel surface at the caller's next synchronisation.  fp_last_error()
  *   returns a message for the calling thread's most recent failure.
- * The library keeps no global mutable state apart from that message.
+ * The library keeps no global mutable state apart from that message and a
+ * per-device cache of occupancy figures (fixed properties of the device and
+ * the code object, computed on first use).
  */
 #ifndef FLATPARAM_H
 #define FLATPARAM_H
@@ -135,9 +137,20 @@ fp_status fp_unpack_views(const fp_plan* plan, int32_t rank, fp_view* out, int32
 
 /* ------------------------------------------------------------------ reduce */
 
-/* Size in bytes of the device workspace fp_reduce_shard and fp_shard_step
- * need for the optional gradient norm (a fixed size, independent of S). */
-int64_t fp_workspace_bytes(void);
+/* Size in bytes of the device workspace that fp_reduce_shard (for the
+ * gradient norm) and fp_shard_step (norm and one-pass grid barrier) use for
+ * a shard of S elements: a small header plus 8 bytes per 2048 elements.
+ * The caller allocates it, zero-fills it once before its first use and then
+ * passes it unchanged to later calls; every completed call leaves it
+ * reusable.  Calls that may run concurrently need separate workspaces. */
+int64_t fp_workspace_bytes(int64_t shard);
+
+/* Byte offset, in the workspace, of a uint32 that counts grid-barrier waits
+ * of the one-pass step that gave up.  It stays 0 as long as the step's
+ * workgroups are co-resident, which the library sizes the grid for; a
+ * caller that runs other kernels concurrently on the GPU can check it, or
+ * pass FP_STEP_NO_COOP. */
+#define FP_WORKSPACE_TIMEOUTS_OFFSET 8320
 
 /* One micro-batch of the reduce-scatter arithmetic for this rank's shard.
  * [GUIDE] section 2 (equation for the averaged gradient): the synchronised
@@ -216,6 +229,7 @@ fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* const* shards
 #define FP_STEP_EXACT_SKIP 0 /* default: on overflow nothing is updated    */
 #define FP_STEP_NO_SKIP 1    /* one fused pass; state updated regardless   */
 #define FP_STEP_KEEP_GRAD 2  /* also leave the reduced gradient in acc     */
+#define FP_STEP_NO_COOP 4    /* never use the cooperative one-pass kernel  */
 
 /* One rank's whole shard step for the last micro-batch: reduce (as
  * fp_reduce_shard), AdamW with the bf16 cast into full + rank*S (as
@@ -226,11 +240,19 @@ fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* const* shards
  *   FP_STEP_EXACT_SKIP -- the overflow check over the whole shard (with the
  *     flag from earlier micro-batches) decides before any state is written;
  *     on overflow master / exp_avg / exp_avg_sq are untouched and full
- *     receives bf16 of the unchanged master.
+ *     receives bf16 of the unchanged master.  When the shard fits the GPU's
+ *     co-resident grid (S up to a few million elements) and a workspace
+ *     is given, this runs as one kernel whose workgroups keep the reduced
+ *     gradient in registers across a grid barrier (the overflow bit rides
+ *     on the barrier's counters); otherwise as two kernels that pass the
+ *     reduced gradient through acc.
  *   FP_STEP_NO_SKIP -- reduce and update in one pass without a gate; the
  *     flag is still reported (for callers without a loss scaler).
  *   FP_STEP_KEEP_GRAD (may be or-ed in) -- acc holds the reduced gradient
  *     afterwards; without it acc's contents afterwards are unspecified.
+ *   FP_STEP_NO_COOP (may be or-ed in) -- use the two-kernel form even when
+ *     the one-pass cooperative kernel would fit (for callers that share the
+ *     GPU with concurrent kernels).
  * On return *found_inf is the OR of its input and this call's check. */
 typedef struct fp_step_args {
     int64_t shard;                 /* S */
@@ -248,9 +270,16 @@ typedef struct fp_step_args {
     uint16_t* full;                /* device bf16[world * S] */
     int32_t* found_inf;            /* device int32, required */
     double* sq_norm;               /* device double, may be NULL */
-    void* workspace;               /* device, fp_workspace_bytes(); may be NULL if sq_norm is */
+    void* workspace;               /* device, fp_workspace_bytes(S), zero-filled before first
+                                      use; NULL disables the norm and the one-pass path */
     int32_t flags;
+    /* NULL, or a host array of FP_STEP_EVENTS hipEvent_t (as void*) that the
+     * call records on `stream`: before its first kernel, between its first
+     * and second kernel, and after its last kernel -- per-kernel timing. */
+    void* const* profile_events;
 } fp_step_args;
+
+#define FP_STEP_EVENTS 3
 
 fp_status fp_shard_step(const fp_step_args* args, void* stream);
 

@@ -21,11 +21,11 @@ from typing import Optional, Sequence
 
 from . import _lib
 from ._lib import (FP_MAX_WORLD, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD,  # noqa: F401
-                   FP_STEP_NO_SKIP, FlatParamError, check, lib)
+                   FP_STEP_NO_COOP, FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
-__all__ = ["Plan", "reduce_shard", "adamw_shard", "unshard", "shard_step", "state_bytes",
-           "workspace_bytes", "new_workspace", "FlatParamError", "FP_STEP_EXACT_SKIP",
-           "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "library_path"]
+__all__ = ["Plan", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
+           "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
+           "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "library_path"]
 
 
 def library_path() -> str:
@@ -49,7 +49,8 @@ def _bf16_dtypes():
 
 
 def _stream(t):
-    return C.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
+    device = t if isinstance(t, _torch().device) else t.device
+    return C.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
 
 def _dev_ptr(t, dtypes, n, name):
@@ -164,13 +165,20 @@ class Plan:
 
 
 # ------------------------------------------------------------------ reduce
-def workspace_bytes() -> int:
-    return int(lib().fp_workspace_bytes())
+def workspace_bytes(shard: int) -> int:
+    return int(lib().fp_workspace_bytes(int(shard)))
 
 
-def new_workspace(device):
+def new_workspace(device, shard: int):
+    """Zero-filled device workspace for shards of up to `shard` elements."""
     torch = _torch()
-    return torch.zeros(workspace_bytes(), dtype=torch.uint8, device=device)
+    return torch.zeros(workspace_bytes(shard), dtype=torch.uint8, device=device)
+
+
+def workspace_timeouts(workspace) -> int:
+    """Grid-barrier waits of the one-pass step that gave up (0 in correct operation)."""
+    off = _lib.FP_WORKSPACE_TIMEOUTS_OFFSET
+    return int(workspace[off:off + 4].view(_torch().int32).item())
 
 
 def reduce_shard(grads, acc, *, scale: float, accumulate: bool = False, found_inf=None,
@@ -181,7 +189,7 @@ def reduce_shard(grads, acc, *, scale: float, accumulate: bool = False, found_in
     ptrs = _rank_ptrs(grads, S, "grads")
     fi = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf") if found_inf is not None else None
     sq = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
-    ws = _dev_ptr(workspace, (torch.uint8,), workspace_bytes(), "workspace") if workspace is not None else None
+    ws = _dev_ptr(workspace, (torch.uint8,), workspace_bytes(S), "workspace") if workspace is not None else None
     check(lib().fp_reduce_shard(S, len(ptrs), _ptr_table(ptrs), float(scale), int(bool(accumulate)),
                                 C.c_void_p(_f32(acc, S, "acc")), fi, sq, ws, _stream(acc)))
     return acc
@@ -222,7 +230,7 @@ def unshard(shards, full):
 # ------------------------------------------------------------------ step
 def shard_step(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *, scale: float,
                lr, beta1, beta2, eps, weight_decay, step: int, found_inf, accumulate: bool = False,
-               sq_norm=None, workspace=None, flags: int = FP_STEP_EXACT_SKIP):
+               sq_norm=None, workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None):
     """Reduce (last micro-batch) + AdamW + bf16 cast + unshard for this rank."""
     torch = _torch()
     S = master.numel()
@@ -245,10 +253,67 @@ def shard_step(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int,
     a.full = _bf16(full, S * world, "full")
     a.found_inf = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf")
     a.sq_norm = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
-    a.workspace = (_dev_ptr(workspace, (torch.uint8,), workspace_bytes(), "workspace")
+    a.workspace = (_dev_ptr(workspace, (torch.uint8,), workspace_bytes(S), "workspace")
                    if workspace is not None else None)
     a.flags = int(flags)
+    ev = None
+    if profile_events is not None:
+        if len(profile_events) != _lib.FP_STEP_EVENTS:
+            raise ValueError(f"profile_events needs {_lib.FP_STEP_EVENTS} hipEvent_t handles")
+        ev = (C.c_void_p * _lib.FP_STEP_EVENTS)(*profile_events)
+        a.profile_events = C.cast(ev, C.c_void_p)
     check(lib().fp_shard_step(C.byref(a), _stream(master)))
+
+
+class ShardStep:
+    """shard_step with its arguments marshalled once, for tight step loops.
+
+    The tensors are checked and their pointers captured at construction;
+    each call only sets the step count (and the optional profile events)
+    and makes one library call on the current stream of master's device.
+    The caller keeps the tensors alive and unchanged in size.
+    """
+
+    def __init__(self, grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *,
+                 scale: float, lr, beta1, beta2, eps, weight_decay, found_inf,
+                 accumulate: bool = False, sq_norm=None, workspace=None,
+                 flags: int = FP_STEP_EXACT_SKIP):
+        torch = _torch()
+        S = master.numel()
+        gptr = _rank_ptrs(grads, S, "grads")
+        sptr = _rank_ptrs(shards, S, "shards", allow_none=True)
+        if len(sptr) != len(gptr):
+            raise ValueError("shards and grads differ in length")
+        self._tables = (_ptr_table(gptr), _ptr_table(sptr))
+        self._events = (C.c_void_p * _lib.FP_STEP_EVENTS)()
+        a = _lib.fp_step_args()
+        a.shard, a.world, a.rank = S, len(gptr), int(rank)
+        a.grads = C.cast(self._tables[0], C.c_void_p)
+        a.shards = C.cast(self._tables[1], C.c_void_p)
+        a.scale, a.accumulate = float(scale), int(bool(accumulate))
+        a.acc, a.master = _f32(acc, S, "acc"), _f32(master, S, "master")
+        a.exp_avg, a.exp_avg_sq = _f32(exp_avg, S, "exp_avg"), _f32(exp_avg_sq, S, "exp_avg_sq")
+        a.hp = _hparams(lr, beta1, beta2, eps, weight_decay, 1)
+        a.full = _bf16(full, S * len(gptr), "full")
+        a.found_inf = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf")
+        a.sq_norm = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
+        a.workspace = (_dev_ptr(workspace, (torch.uint8,), workspace_bytes(S), "workspace")
+                       if workspace is not None else None)
+        a.flags = int(flags)
+        self._args = a
+        self._device = master.device
+        self._fn = lib().fp_shard_step
+
+    def __call__(self, step: int, profile_events=None):
+        a = self._args
+        a.hp.step = int(step)
+        if profile_events is None:
+            a.profile_events = None
+        else:
+            for i, e in enumerate(profile_events):
+                self._events[i] = e
+            a.profile_events = C.cast(self._events, C.c_void_p)
+        check(self._fn(C.byref(a), _stream(self._device)))
 
 
 # ------------------------------------------------------------------ helpers

@@ -22,6 +22,9 @@ FP_MAX_NDIM = 8
 FP_STEP_EXACT_SKIP = 0
 FP_STEP_NO_SKIP = 1
 FP_STEP_KEEP_GRAD = 2
+FP_STEP_NO_COOP = 4
+FP_STEP_EVENTS = 3
+FP_WORKSPACE_TIMEOUTS_OFFSET = 8320
 
 _i32, _i64, _f32, _f64, _vp = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p
 
@@ -41,7 +44,7 @@ class fp_step_args(C.Structure):
                 ("scale", _f32), ("accumulate", _i32), ("acc", _vp), ("master", _vp),
                 ("exp_avg", _vp), ("exp_avg_sq", _vp), ("hp", fp_adamw_hparams),
                 ("shards", _vp), ("full", _vp), ("found_inf", _vp), ("sq_norm", _vp),
-                ("workspace", _vp), ("flags", _i32)]
+                ("workspace", _vp), ("flags", _i32), ("profile_events", _vp)]
 
 
 # name -> (restype, argtypes); the export test compares this table with the header
@@ -51,7 +54,7 @@ SIGNATURES = {
     "fp_plan_info": (_i32, [_vp, _vp, _vp, _vp]),
     "fp_pack": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "fp_unpack_views": (_i32, [_vp, _i32, _vp, _i32, _vp]),
-    "fp_workspace_bytes": (_i64, []),
+    "fp_workspace_bytes": (_i64, [_i64]),
     "fp_reduce_shard": (_i32, [_i64, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "fp_adamw_shard": (_i32, [_i64, C.POINTER(fp_adamw_hparams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp_unshard": (_i32, [_i64, _i32, _vp, _vp, _vp]),
@@ -77,6 +80,10 @@ def lib():
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -c \"import __graft_entry__; "
                 f"__graft_entry__.build()\"` (hipcc, gfx950). There is no fallback.")
+        try:  # share torch's HIP runtime (same SONAME) when torch is present
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = C.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)

@@ -42,14 +42,15 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int clamp_grid(int64_t want, int64_t cap) {
-    if (want < 1) want = 1;
-    if (want > cap) want = cap;
-    return (int)want;
+// Workgroups of a tiled stream over S elements in 8-element chunks.
+int64_t stream_grid(int64_t shard) {
+    const int64_t t = tiles_of(shard >> 3);
+    return t > 0 ? t : 1;
 }
 
-// Grid of a grid-stride stream over S elements in 8-element chunks.
-int stream_grid(int64_t shard) { return clamp_grid(ceil_div(shard >> 3, kThreads), kMaxGrid); }
+double* partials_of(void* workspace) {
+    return reinterpret_cast<double*>(static_cast<char*>(workspace) + kWorkspaceHeader);
+}
 
 fp_status check_hparams(const fp_adamw_hparams* hp, AdamCoef* c) {
     if (hp == nullptr) return fail(FP_ERR_INVALID, "hparams is NULL");
@@ -320,7 +321,10 @@ extern "C" fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const
 
 // ---------------------------------------------------------------------- reduce
 
-extern "C" int64_t fp_workspace_bytes(void) { return kWorkspaceBytes; }
+extern "C" int64_t fp_workspace_bytes(int64_t shard) {
+    if (shard < 0) shard = 0;
+    return kWorkspaceHeader + 8 * partial_slots(shard);
+}
 
 extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_t* const* grads,
                                      float scale, int32_t accumulate, float* acc, int32_t* found_inf,
@@ -343,16 +347,16 @@ extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_
     for (int32_t q = 0; q < world; ++q) a.grads[q] = grads[q];
     a.acc = acc;
     a.found_inf = found_inf;
-    a.partials = sq_norm != nullptr ? static_cast<double*>(workspace) : nullptr;
+    a.partials = sq_norm != nullptr ? partials_of(workspace) : nullptr;
     a.shard = shard;
     a.scale = scale;
     a.world = world;
     a.accumulate = accumulate ? 1 : 0;
-    const int grid = stream_grid(shard);
+    const int64_t grid = stream_grid(shard);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_reduce(a, grid, s);
     if (e != hipSuccess) return device_fail(e, "reduce launch");
-    if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, sq_norm, s)) != hipSuccess)
+    if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)grid, sq_norm, s)) != hipSuccess)
         return device_fail(e, "norm launch");
     return FP_OK;
 }
@@ -415,8 +419,7 @@ extern "C" fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* co
     a.full = full;
     a.shard = shard;
     a.world = world;
-    const int gx = clamp_grid(ceil_div(ceil_div(shard, 8), kThreads), kMaxGrid / world > 0 ? kMaxGrid / world : 1);
-    hipError_t e = launch_unshard(a, gx, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_unshard(a, copy_tiles_per_shard(shard), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "unshard launch");
     return FP_OK;
 }
@@ -431,7 +434,8 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     if (S < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
     if ((st = check_world(x.world)) != FP_OK) return st;
     if (x.rank < 0 || x.rank >= x.world) return fail(FP_ERR_RANGE, "rank %d outside [0, %d)", x.rank, x.world);
-    if (x.flags & ~(FP_STEP_NO_SKIP | FP_STEP_KEEP_GRAD)) return fail(FP_ERR_INVALID, "unknown flags");
+    if (x.flags & ~(FP_STEP_NO_SKIP | FP_STEP_KEEP_GRAD | FP_STEP_NO_COOP))
+        return fail(FP_ERR_INVALID, "unknown flags");
     StepArgs a;
     std::memset(&a, 0, sizeof a);
     if ((st = check_hparams(&x.hp, &a.c)) != FP_OK) return st;
@@ -446,10 +450,11 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     if (!aligned(x.full, 2)) return fail(FP_ERR_ALIGN, "full misaligned");
     if (x.found_inf == nullptr) return fail(FP_ERR_INVALID, "found_inf is NULL");
     if (!aligned(x.found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
+    if (x.workspace != nullptr && !aligned(x.workspace, 16))
+        return fail(FP_ERR_ALIGN, "workspace is not 16-byte aligned");
     if (x.sq_norm != nullptr) {
         if (!aligned(x.sq_norm, 8)) return fail(FP_ERR_ALIGN, "sq_norm misaligned");
-        if (x.workspace == nullptr || !aligned(x.workspace, 16))
-            return fail(FP_ERR_INVALID, "sq_norm needs a 16-byte aligned workspace");
+        if (x.workspace == nullptr) return fail(FP_ERR_INVALID, "sq_norm needs a workspace");
     }
     const int64_t b4 = S * 4, b2 = S * 2, bf = S * x.world * 2;
     const void* f32s[4] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq};
@@ -466,7 +471,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
             return fail(FP_ERR_INVALID, "shards[%d] overlaps full", q);
     }
 
-    const bool fused = (x.flags & FP_STEP_NO_SKIP) != 0;
+    const bool no_skip = (x.flags & FP_STEP_NO_SKIP) != 0;
     for (int32_t q = 0; q < x.world; ++q) {
         a.grads[q] = x.grads[q];
         a.shards[q] = q == x.rank ? nullptr : x.shards[q];
@@ -477,38 +482,45 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     a.exp_avg_sq = x.exp_avg_sq;
     a.full = x.full;
     a.found_inf = x.found_inf;
-    a.partials = x.sq_norm != nullptr ? static_cast<double*>(x.workspace) : nullptr;
+    a.partials = x.sq_norm != nullptr ? partials_of(x.workspace) : nullptr;
+    a.sq_norm = x.sq_norm;
     a.shard = S;
     a.scale = x.scale;
     a.world = x.world;
     a.rank = x.rank;
     a.accumulate = x.accumulate ? 1 : 0;
     a.keep_grad = (x.flags & FP_STEP_KEEP_GRAD) ? 1 : 0;
-
-    // Split one launch between the reduce role and the copy role in
-    // proportion to the bytes each moves per shard element.
-    const int64_t n = x.world;
-    const double reduce_bytes = 2.0 * n + (a.accumulate ? 4 : 0) +
-                                (fused ? 24.0 + 2.0 + (a.keep_grad ? 4 : 0) : 4.0);
-    const double copy_bytes = 4.0 * (n - 1);
-    const int64_t reduce_need = ceil_div(ceil_div(S, 8), kThreads);
-    const int64_t copy_need = n > 1 ? ceil_div((n - 1) * ceil_div(S, 8), kThreads) : 0;
-    int64_t g_r = (int64_t)std::llround(kMaxGrid * reduce_bytes / (reduce_bytes + copy_bytes));
-    g_r = g_r < 1 ? 1 : (g_r > reduce_need ? reduce_need : g_r);
-    if (g_r < 1) g_r = 1;
-    int64_t g_u = n > 1 ? kMaxGrid - g_r : 0;
-    if (g_u > copy_need) g_u = copy_need;
-    if (n > 1 && g_u < 1) g_u = 1;
-    a.reduce_groups = (int32_t)g_r;
+    a.sync = x.workspace != nullptr ? static_cast<GridSync*>(x.workspace) : nullptr;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_step_phase1(a, (int)(g_r + g_u), fused, s);
-    if (e != hipSuccess) return device_fail(e, "step launch");
-    if (fused) {
-        if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)g_r, x.sq_norm, s)) != hipSuccess)
-            return device_fail(e, "norm launch");
-        return FP_OK;
+    hipEvent_t ev[FP_STEP_EVENTS] = {nullptr, nullptr, nullptr};
+    if (x.profile_events != nullptr)
+        for (int i = 0; i < FP_STEP_EVENTS; ++i) ev[i] = static_cast<hipEvent_t>(x.profile_events[i]);
+    hipError_t e;
+
+    if (!no_skip && a.sync != nullptr && !(x.flags & FP_STEP_NO_COOP)) {  // one pass, if it fits
+        int variant = -1, grid = 0;
+        if ((e = plan_step_coop(S, &variant, &grid)) != hipSuccess) return device_fail(e, "occupancy query");
+        if (variant >= 0) {
+            if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+            if ((e = launch_step_coop(a, variant, grid, s)) != hipSuccess)
+                return device_fail(e, "one-pass step launch");
+            if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+            if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, x.sq_norm, s)) != hipSuccess)
+                return device_fail(e, "norm launch");
+            if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+            return FP_OK;
+        }
     }
+    if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+
+    // Reduce (and, without the gate, update) tiles plus the copy of the other
+    // ranks' shards as (shard, tile) pairs, in one launch.
+    const int64_t reduce_groups = stream_grid(S);
+    a.reduce_groups = (int32_t)reduce_groups;
+    a.copy_tiles = (int32_t)copy_tiles_per_shard(S);
+    const int64_t grid = reduce_groups + (int64_t)(x.world - 1) * a.copy_tiles;
+    if (grid > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "shard too large for one launch");
     AdamArgs d;
     std::memset(&d, 0, sizeof d);
     d.grad = x.acc;
@@ -521,8 +533,17 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     d.c = a.c;
     d.partials = a.partials;
     d.sq_norm = x.sq_norm;
-    d.n_partials = (int32_t)g_r;
-    if ((e = launch_adamw(d, stream_grid(S), s)) != hipSuccess) return device_fail(e, "adamw launch");
+    d.n_partials = (int32_t)reduce_groups;
+    if ((e = launch_step_phase1(a, grid, no_skip, s)) != hipSuccess) return device_fail(e, "step launch");
+    if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (no_skip) {
+        if (x.sq_norm != nullptr &&
+            (e = launch_norm_finalize(a.partials, (int)reduce_groups, x.sq_norm, s)) != hipSuccess)
+            return device_fail(e, "norm launch");
+    } else {
+        if ((e = launch_adamw(d, stream_grid(S), s)) != hipSuccess) return device_fail(e, "adamw launch");
+    }
+    if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     return FP_OK;
 }
 

@@ -3,19 +3,47 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/flatparam.h"
 
 namespace fpk {
 
+#ifndef FP_UNROLL
+#define FP_UNROLL 2
+#endif
+
 constexpr int kThreads = 256;          // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kElemsPerChunk = 8;      // one 16-byte bf16 word, two 16-byte fp32 words
-constexpr int kMaxGrid = 4096;         // cap of grid-stride launches = norm partial slots
-constexpr int64_t kWorkspaceBytes = 64 * 1024;   // >= kMaxGrid doubles
+// A workgroup of a streaming kernel owns one tile of kTileChunks consecutive
+// chunks (lane t takes chunks t, t + 256, ...), and tiles are numbered in
+// dispatch order, so the workgroups in flight cover one contiguous window of
+// every stream -- on MI355X this keeps HBM pages open far better than
+// grid-stride loops, whose concurrent accesses spread over the whole buffer.
+constexpr int kUnroll = FP_UNROLL;
+constexpr int kTileChunks = kThreads * kUnroll;
 constexpr int kPackBlockElems = 8192;  // flat elements per pack workgroup
 constexpr int kPackLdsTensors = 1024;  // tensor descriptors a pack workgroup stages in LDS
+constexpr int kMaxCoopChunks = 2;      // chunks a lane keeps in registers in the one-pass step
+constexpr int kSyncGroups = 32;        // first level of the grid barrier
+constexpr int kLineWords = 32;         // 128-byte cache line in 32-bit words
+
+// Grid-barrier state at the start of the workspace (zero-filled by the
+// caller before first use; every completed barrier leaves the counters at
+// 0).  Each counter and each copy of the generation word has a cache line
+// of its own.
+struct GridSync {
+    unsigned int group[kSyncGroups * kLineWords];  // arrivals per group (+ overflow bit 16)
+    unsigned int top[kLineWords];                  // groups complete (+ overflow bit 16)
+    unsigned int gen[kSyncGroups * kLineWords];    // per-group copy: generation | flag << 31
+    unsigned int timeouts;                         // waits that gave up
+    unsigned int pad[kLineWords - 1];
+};
+constexpr int64_t kWorkspaceHeader = 16384;  // GridSync, then one double per workgroup
+static_assert(sizeof(GridSync) <= kWorkspaceHeader, "barrier state exceeds the header");
+static_assert(offsetof(GridSync, timeouts) == FP_WORKSPACE_TIMEOUTS_OFFSET, "timeouts offset");
 
 // fp64 coefficients of one AdamW step, all derived on the host in fp64.
 struct AdamCoef {
@@ -40,6 +68,14 @@ struct ReduceArgs {
     int32_t world;
     int32_t accumulate;
 };
+
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t tiles_of(int64_t chunks) { return ceil_div64(chunks, kTileChunks); }
+// Copy tiles per shard: the whole 16-byte words of a shard number at most S/8 + 1.
+inline int64_t copy_tiles_per_shard(int64_t S) { return ceil_div64(S / 8 + 1, kTileChunks); }
+// Norm partial slots the workspace provides for a shard of S elements (one
+// per workgroup of any launch geometry used for that shard).
+inline int64_t partial_slots(int64_t S) { return ceil_div64(S / 8, kThreads) + 1; }
 
 struct AdamArgs {
     const float* grad;
@@ -76,6 +112,7 @@ struct StepArgs {
     uint16_t* full;
     int32_t* found_inf;
     double* partials;
+    double* sq_norm;         // one-pass: finalised by workgroup 0 after the barrier
     int64_t shard;
     AdamCoef c;
     float scale;
@@ -83,7 +120,9 @@ struct StepArgs {
     int32_t rank;
     int32_t accumulate;
     int32_t keep_grad;
-    int32_t reduce_groups;
+    int32_t reduce_groups;   // two-phase / no-skip: workgroups of the reduce role
+    int32_t copy_tiles;      // two-phase / no-skip: copy tiles per shard
+    GridSync* sync;          // one-pass: barrier state in the workspace
 };
 
 struct PackArgs {
@@ -97,11 +136,16 @@ struct PackArgs {
 };
 
 // Launchers (return the HIP error of the launch).
-hipError_t launch_reduce(const ReduceArgs& a, int grid, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, hipStream_t s);
 hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipStream_t s);
-hipError_t launch_adamw(const AdamArgs& a, int grid, hipStream_t s);
-hipError_t launch_unshard(const UnshardArgs& a, int grid_x, hipStream_t s);
-hipError_t launch_step_phase1(const StepArgs& a, int grid, bool fused_update, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs& a, int64_t grid, hipStream_t s);
+hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, hipStream_t s);
+hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, hipStream_t s);
+// One-pass exact-skip step: plan_step_coop picks the variant (lanes keep
+// 1, 2 or 4 chunks in registers) and a grid that fits the device's
+// co-resident capacity, or sets *variant = -1 when the shard is too large.
+hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
+hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
 
 }  // namespace fpk

@@ -51,7 +51,8 @@ def test_struct_layouts_match_the_header(fp):
     # fp_step_args: offsets follow the C layout rules of the header's field order
     assert _lib.fp_step_args.grads.offset == 16
     assert _lib.fp_step_args.hp.offset == 64
-    assert C.sizeof(_lib.fp_step_args) == 64 + 48 + 5 * 8 + 8
+    assert _lib.fp_step_args.flags.offset == 152
+    assert C.sizeof(_lib.fp_step_args) == 64 + 48 + 5 * 8 + 8 + 8
 
 
 def _random_shapes(r):
@@ -180,5 +181,7 @@ def test_device_entry_points_reject_bad_arguments(fp):
     assert _status(L.fp_shard_step, C.byref(a), None) == -2                      # rank out of range
     a.rank, a.flags = 0, 8
     assert _status(L.fp_shard_step, C.byref(a), None) == -1                      # unknown flag
+    assert L.fp_workspace_bytes(0) >= 256 + 8
+    assert L.fp_workspace_bytes(1 << 30) == 16384 + 8 * ((1 << 30) // 8 // 256 + 1)
     assert _status(L.fp_shard_step, None, None) == -1
     assert L.fp_status_string(-3) == b"misaligned pointer"

@@ -56,7 +56,7 @@ def test_reduce_random(fp, seed):
     acc = torch.zeros(S, dtype=torch.float32, device=dev())
     flag = torch.zeros(1, dtype=torch.int32, device=dev())
     sq = torch.zeros(1, dtype=torch.float64, device=dev())
-    ws = fp.new_workspace(dev())
+    ws = fp.new_workspace(dev(), S)
     for m in range(n_micro):
         rows = [gen.bf16_normal(S, 10.0 ** -int(r.integers(0, 4)), seed, gen.STREAM_GRAD, 0, m, q)
                 for q in range(world)]
@@ -254,7 +254,7 @@ def test_pack_worked_example_and_views(fp):
 
 
 # ------------------------------------------------------------------ whole step
-def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_off=0):
+def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_off=0, workspace=True):
     hp = HP
     scale = np.float32(1.0 / (world * n_micro))
     micro = [[gen.bf16_normal(S, 1e-3, seed, gen.STREAM_GRAD, 0, m, q) for q in range(world)]
@@ -277,8 +277,8 @@ def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_o
 
     acc = torch.zeros(S, dtype=torch.float32, device=dev())
     flag = torch.zeros(1, dtype=torch.int32, device=dev())
-    sq = torch.zeros(1, dtype=torch.float64, device=dev())
-    ws = fp.new_workspace(dev())
+    sq = torch.zeros(1, dtype=torch.float64, device=dev()) if workspace else None
+    ws = fp.new_workspace(dev(), S) if workspace else None
     for m in range(n_micro - 1):
         fp.reduce_shard(_grads_with_offset(micro[m], grad_off), acc, scale=float(scale),
                         accumulate=m > 0, found_inf=flag)
@@ -306,16 +306,27 @@ def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_o
     assert_bf16_equal(full_h[mask], full_o[mask], "other shards")
     if flags & fp.FP_STEP_KEEP_GRAD:
         assert_f32_bitexact(to_host(acc), acc_o, "kept gradient")
-    if math.isfinite(norm_o):
+    if workspace and math.isfinite(norm_o):
         assert float(sq.item()) == pytest.approx(norm_o, rel=1e-12)
+    if workspace:
+        assert fp.workspace_timeouts(ws) == 0, "grid barrier wait gave up"
     return full_h
 
 
 @pytest.mark.parametrize("rank", [0, 1])
-@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 6])
 def test_step_worked_example(fp, rank, flags):
     say(f"step C1 rank={rank} flags={flags}")
     _step_case(fp, world=2, S=12, rank=rank, n_micro=1, step=1, seed=0, flags=flags)
+
+
+@pytest.mark.parametrize("flags", [0, 4])
+def test_step_without_workspace(fp, flags):
+    say(f"step without workspace flags={flags}")
+    _step_case(fp, world=8, S=10_001, rank=5, n_micro=2, step=3, seed=3, flags=flags, inf=False,
+               workspace=False)
+    _step_case(fp, world=8, S=10_001, rank=5, n_micro=1, step=3, seed=4, flags=flags, inf=True,
+               workspace=False)
 
 
 @pytest.mark.parametrize("seed", range(14))
@@ -326,7 +337,7 @@ def test_step_random(fp, seed):
     rank = int(r.integers(0, world))
     n_micro = int(r.choice([1, 2, 4]))
     step = int(r.choice([1, 2, 7]))
-    flags = int(r.choice([0, 0, 1, 2]))
+    flags = int(r.choice([0, 0, 1, 2, 4, 6]))
     inf = seed % 4 == 3
     off = int(r.integers(0, 8)) if seed % 2 else 0
     say(f"step seed={seed} world={world} S={S} rank={rank} n_micro={n_micro} step={step} "
