@@ -34,6 +34,7 @@ fp_status device_fail(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+bool is_aligned16(const void* p) { return aligned(p, 16); }
 
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -352,9 +353,11 @@ extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_
     a.scale = scale;
     a.world = world;
     a.accumulate = accumulate ? 1 : 0;
+    bool aligned = true;
+    for (int32_t q = 0; q < world; ++q) aligned = aligned && is_aligned16(grads[q]);
     const int64_t grid = stream_grid(shard);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_reduce(a, grid, s);
+    hipError_t e = launch_reduce(a, grid, aligned, s);
     if (e != hipSuccess) return device_fail(e, "reduce launch");
     if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)grid, sq_norm, s)) != hipSuccess)
         return device_fail(e, "norm launch");
@@ -394,7 +397,8 @@ extern "C" fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, c
     a.param_bf16 = param_bf16;
     a.found_inf = found_inf;
     a.shard = shard;
-    hipError_t e = launch_adamw(a, stream_grid(shard), static_cast<hipStream_t>(stream));
+    const bool aligned = param_bf16 == nullptr || is_aligned16(param_bf16);
+    hipError_t e = launch_adamw(a, stream_grid(shard), aligned, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "adamw launch");
     return FP_OK;
 }
@@ -419,7 +423,10 @@ extern "C" fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* co
     a.full = full;
     a.shard = shard;
     a.world = world;
-    hipError_t e = launch_unshard(a, copy_tiles_per_shard(shard), static_cast<hipStream_t>(stream));
+    bool aligned = true;
+    for (int32_t q = 0; q < world; ++q)
+        if (shards[q] != nullptr) aligned = aligned && copy_source_aligned(shards[q], full, shard, q);
+    hipError_t e = launch_unshard(a, copy_tiles_per_shard(shard), aligned, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "unshard launch");
     return FP_OK;
 }
@@ -492,6 +499,13 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     a.keep_grad = (x.flags & FP_STEP_KEEP_GRAD) ? 1 : 0;
     a.sync = x.workspace != nullptr ? static_cast<GridSync*>(x.workspace) : nullptr;
 
+    uint16_t* own = x.full + (int64_t)x.rank * S;
+    bool aligned = is_aligned16(own);
+    for (int32_t q = 0; q < x.world; ++q) {
+        aligned = aligned && is_aligned16(x.grads[q]);
+        if (q != x.rank) aligned = aligned && copy_source_aligned(x.shards[q], x.full, S, q);
+    }
+
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t ev[FP_STEP_EVENTS] = {nullptr, nullptr, nullptr};
     if (x.profile_events != nullptr)
@@ -503,7 +517,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
         if ((e = plan_step_coop(S, &variant, &grid)) != hipSuccess) return device_fail(e, "occupancy query");
         if (variant >= 0) {
             if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-            if ((e = launch_step_coop(a, variant, grid, s)) != hipSuccess)
+            if ((e = launch_step_coop(a, variant, grid, aligned, s)) != hipSuccess)
                 return device_fail(e, "one-pass step launch");
             if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
             if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, x.sq_norm, s)) != hipSuccess)
@@ -527,21 +541,22 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     d.master = x.master;
     d.exp_avg = x.exp_avg;
     d.exp_avg_sq = x.exp_avg_sq;
-    d.param_bf16 = x.full + (int64_t)x.rank * S;
+    d.param_bf16 = own;
     d.found_inf = x.found_inf;
     d.shard = S;
     d.c = a.c;
     d.partials = a.partials;
     d.sq_norm = x.sq_norm;
     d.n_partials = (int32_t)reduce_groups;
-    if ((e = launch_step_phase1(a, grid, no_skip, s)) != hipSuccess) return device_fail(e, "step launch");
+    if ((e = launch_step_phase1(a, grid, no_skip, aligned, s)) != hipSuccess) return device_fail(e, "step launch");
     if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     if (no_skip) {
         if (x.sq_norm != nullptr &&
             (e = launch_norm_finalize(a.partials, (int)reduce_groups, x.sq_norm, s)) != hipSuccess)
             return device_fail(e, "norm launch");
     } else {
-        if ((e = launch_adamw(d, stream_grid(S), s)) != hipSuccess) return device_fail(e, "adamw launch");
+        if ((e = launch_adamw(d, stream_grid(S), is_aligned16(own), s)) != hipSuccess)
+            return device_fail(e, "adamw launch");
     }
     if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     return FP_OK;

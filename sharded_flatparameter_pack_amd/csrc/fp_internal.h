@@ -10,20 +10,15 @@
 
 namespace fpk {
 
-#ifndef FP_UNROLL
-#define FP_UNROLL 2
-#endif
-
 constexpr int kThreads = 256;          // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kElemsPerChunk = 8;      // one 16-byte bf16 word, two 16-byte fp32 words
 // A workgroup of a streaming kernel owns one tile of kTileChunks consecutive
-// chunks (lane t takes chunks t, t + 256, ...), and tiles are numbered in
-// dispatch order, so the workgroups in flight cover one contiguous window of
-// every stream -- on MI355X this keeps HBM pages open far better than
-// grid-stride loops, whose concurrent accesses spread over the whole buffer.
-constexpr int kUnroll = FP_UNROLL;
-constexpr int kTileChunks = kThreads * kUnroll;
+// chunks, one per lane, and tiles are numbered in dispatch order, so the
+// workgroups in flight cover one contiguous window of every stream -- on
+// MI355X this keeps HBM pages open far better than grid-stride loops, whose
+// concurrent accesses spread over the whole buffer.
+constexpr int kTileChunks = kThreads;
 constexpr int kPackBlockElems = 8192;  // flat elements per pack workgroup
 constexpr int kPackLdsTensors = 1024;  // tensor descriptors a pack workgroup stages in LDS
 constexpr int kMaxCoopChunks = 2;      // chunks a lane keeps in registers in the one-pass step
@@ -73,6 +68,33 @@ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t tiles_of(int64_t chunks) { return ceil_div64(chunks, kTileChunks); }
 // Copy tiles per shard: the whole 16-byte words of a shard number at most S/8 + 1.
 inline int64_t copy_tiles_per_shard(int64_t S) { return ceil_div64(S / 8 + 1, kTileChunks); }
+
+// Shard q occupies full[qS, (q+1)S).  [lo, a) and [b, hi) are its edge
+// elements that share a 16-byte word of `full` with a neighbouring shard;
+// [a, b) are whole, aligned words of `full`.
+struct ShardSpan {
+    int64_t lo, a, b, hi;
+};
+
+__host__ __device__ inline ShardSpan shard_span(const uint16_t* full, int64_t S, int q) {
+    // element index e is 16-byte aligned in `full` when e % 8 == phase
+    const int64_t phase = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(full) & 15u)) & 15u) >> 1);
+    ShardSpan s;
+    s.lo = (int64_t)q * S;
+    s.hi = s.lo + S;
+    const int64_t up = s.lo + (((phase - s.lo) % 8) + 8) % 8;     // first aligned >= lo
+    s.a = up < s.hi ? up : s.hi;
+    const int64_t down = s.hi - (((s.hi - phase) % 8) + 8) % 8;   // last aligned <= hi
+    s.b = down > s.a ? down : s.a;
+    return s;
+}
+
+// True when shard q's source, read from its first whole word of `full` on,
+// is 16-byte aligned (then the copy needs no realignment).
+inline bool copy_source_aligned(const uint16_t* src, const uint16_t* full, int64_t S, int q) {
+    const ShardSpan sp = shard_span(full, S, q);
+    return ((reinterpret_cast<uintptr_t>(src) + 2 * (uintptr_t)(sp.a - sp.lo)) & 15u) == 0;
+}
 // Norm partial slots the workspace provides for a shard of S elements (one
 // per workgroup of any launch geometry used for that shard).
 inline int64_t partial_slots(int64_t S) { return ceil_div64(S / 8, kThreads) + 1; }
@@ -120,8 +142,8 @@ struct StepArgs {
     int32_t rank;
     int32_t accumulate;
     int32_t keep_grad;
-    int32_t reduce_groups;   // two-phase / no-skip: workgroups of the reduce role
-    int32_t copy_tiles;      // two-phase / no-skip: copy tiles per shard
+    int32_t reduce_groups;   // workgroups of the reduce role (barrier members in one pass)
+    int32_t copy_tiles;      // copy tiles per shard
     GridSync* sync;          // one-pass: barrier state in the workspace
 };
 
@@ -136,16 +158,19 @@ struct PackArgs {
 };
 
 // Launchers (return the HIP error of the launch).
-hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, hipStream_t s);
+// `aligned`: every bf16 stream of the launch is 16-byte aligned at the words
+// the kernel reads or writes (then no realignment code runs).
+hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipStream_t s);
-hipError_t launch_adamw(const AdamArgs& a, int64_t grid, hipStream_t s);
-hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, hipStream_t s);
-hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s);
+hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hipStream_t s);
+hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool aligned,
+                              hipStream_t s);
 // One-pass exact-skip step: plan_step_coop picks the variant (lanes keep
 // 1, 2 or 4 chunks in registers) and a grid that fits the device's
 // co-resident capacity, or sets *variant = -1 when the shard is too large.
 hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
-hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, hipStream_t s);
+hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
 
 }  // namespace fpk

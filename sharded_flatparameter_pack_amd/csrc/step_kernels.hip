@@ -1,13 +1,17 @@
 // step_kernels.hip -- gfx950 kernels of the per-step path: reduce, AdamW with
 // the bf16 cast, unshard, and the shard step (one-pass or two-phase).
 //
-// Each lane moves 8-element chunks: one 16-byte word per bf16 stream and
+// Each lane moves one 8-element chunk: one 16-byte word per bf16 stream and
 // two per fp32 stream, so every HBM access is a 128-bit (dwordx4) load or
-// store and a wave touches 1 KiB (bf16) or 2 KiB (fp32) of contiguous
-// memory per access.  Workgroups own dispatch-ordered tiles of
-// kTileChunks chunks.  Elements past the last whole chunk are handled one
-// by one by workgroup 0.  Nothing here is a contraction, so there is no
-// MFMA; the kernels are bound by HBM.
+// store, carries the non-temporal hint (each stream is touched once per
+// step), and a wave touches 1 KiB (bf16) or 2 KiB (fp32) of contiguous
+// memory per access.  Workgroups own dispatch-ordered tiles of 256 chunks.
+// Elements past the last whole chunk are handled one by one by workgroup 0.
+// Every kernel comes in an aligned form (all bf16 streams 16-byte aligned at
+// the words it touches: plain loads, which the compiler keeps in flight
+// together) and a general form (branch-free realignment from a base whose
+// shift is uniform across the wave).  Nothing here is a contraction, so
+// there is no MFMA; the kernels are bound by HBM.
 //
 // Compiled with -ffp-contract=off: every fp32 / fp64 operation below is one
 // IEEE round-to-nearest-even operation, in the order written.
@@ -18,20 +22,66 @@
 
 namespace fpk {
 
+// Optional per-workgroup phase timestamps for tuning builds (never defined
+// in the library build): thread 0 records the 100 MHz real-time counter.
+#ifdef FP_PHASE_TRACE
+__device__ unsigned long long fp_phase_trace[1 << 16][6];
+#define FP_PHASE_MARK(k)                                                               \
+    do {                                                                               \
+        if (threadIdx.x == 0 && blockIdx.x < (1u << 16))                               \
+            fp_phase_trace[blockIdx.x][k] = __builtin_amdgcn_s_memrealtime();          \
+    } while (0)
+#else
+#define FP_PHASE_MARK(k) \
+    do {                 \
+    } while (0)
+#endif
+
+// ---------------------------------------------------------------- streams
+
+__device__ __forceinline__ void load_f32x8(const float* p, float f[8]) {
+    const uint4 u = ld16(p);
+    const uint4 v = ld16(p + 4);
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+    f[4] = __uint_as_float(v.x); f[5] = __uint_as_float(v.y);
+    f[6] = __uint_as_float(v.z); f[7] = __uint_as_float(v.w);
+}
+
+__device__ __forceinline__ void store_f32x8(float* p, const float f[8]) {
+    st16(p, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                       __float_as_uint(f[3])));
+    st16(p + 4, make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                           __float_as_uint(f[7])));
+}
+
+// Word `word` of a bf16 stream starting at `base`.
+template <bool kAligned>
+__device__ __forceinline__ uint4 ld_bf16_word(const uint16_t* base, int64_t word) {
+    if (kAligned) return ld16(base + (word << 3));
+    return ld16_realign(src16(base), word);
+}
+
+template <bool kAligned>
+__device__ __forceinline__ void st_bf16_word(uint16_t* base, int64_t word, const uint4 v) {
+    if (kAligned) st16(base + (word << 3), v);
+    else store16_any(base + (word << 3), v);
+}
+
 // ---------------------------------------------------------------- reduce
-// Ascending-rank fp32 sum of the ranks' bf16 gradients at chunk j0.  The
+// Ascending-rank fp32 sum of the ranks' bf16 gradients at chunk c.  The
 // loads of up to 8 ranks are issued before any add, so each lane has up to
 // 128 bytes in flight.  "Infra: Data Parallel", ZeRO-1/ZeRO-2 paragraphs
 // (reduce-scatter with averaging); "4.1 数据并行详解" section 2 (average of
 // the local gradients).
-template <class A>
-__device__ __forceinline__ void sum_ranks8(const A& a, int64_t j0, float s[8]) {
+template <bool kAligned, class A>
+__device__ __forceinline__ void sum_ranks8(const A& a, int64_t c, float s[8]) {
     const int world = a.world;
     for (int q0 = 0; q0 < world; q0 += 8) {
         uint4 w[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (q0 + k < world) w[k] = load16_any(a.grads[q0 + k] + j0);
+            if (q0 + k < world) w[k] = ld_bf16_word<kAligned>(a.grads[q0 + k], c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             if (q0 + k < world) {
@@ -56,27 +106,15 @@ __device__ __forceinline__ float sum_ranks1(const A& a, int64_t j) {
     return s;
 }
 
-__device__ __forceinline__ void load_f32x8(const float* p, float f[8]) {
-    const float4 u = reinterpret_cast<const float4*>(p)[0];
-    const float4 v = reinterpret_cast<const float4*>(p)[1];
-    f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
-    f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
-}
-
-__device__ __forceinline__ void store_f32x8(float* p, const float f[8]) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
-}
-
 // y = scale * (sum over ranks), then y = acc + y when accumulating.
-template <class A>
-__device__ __forceinline__ void reduce_chunk(const A& a, int64_t j0, bool accumulate, float y[8]) {
-    sum_ranks8(a, j0, y);
+template <bool kAligned, class A>
+__device__ __forceinline__ void reduce_chunk(const A& a, int64_t c, bool accumulate, float y[8]) {
+    sum_ranks8<kAligned>(a, c, y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = y[e] * a.scale;
     if (accumulate) {
         float p[8];
-        load_f32x8(a.acc + j0, p);
+        load_f32x8(a.acc + (c << 3), p);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = p[e] + y[e];
     }
@@ -120,10 +158,11 @@ __device__ __forceinline__ void adamw_elem(const AdamCoef& c, float g, float& th
     v = (float)vd;
 }
 
-// AdamW on chunk j0 with gradient y, then the bf16 cast to out + j0.
-template <class A>
-__device__ __forceinline__ void update_chunk(const A& a, int64_t j0, const float y[8], bool skip,
+// AdamW on chunk c with gradient y, then the bf16 cast to word c of out.
+template <bool kAligned, class A>
+__device__ __forceinline__ void update_chunk(const A& a, int64_t c, const float y[8], bool skip,
                                              uint16_t* out) {
+    const int64_t j0 = c << 3;
     float th[8];
     load_f32x8(a.master + j0, th);
     if (!skip) {
@@ -136,7 +175,7 @@ __device__ __forceinline__ void update_chunk(const A& a, int64_t j0, const float
         store_f32x8(a.exp_avg + j0, m);
         store_f32x8(a.exp_avg_sq + j0, v);
     }
-    if (out != nullptr) store16_any(out + j0, f32x8_to_bf16(th));
+    if (out != nullptr) st_bf16_word<kAligned>(out, c, f32x8_to_bf16(th));
 }
 
 template <class A>
@@ -153,42 +192,14 @@ __device__ __forceinline__ void update_elem(const A& a, int64_t j, float y, bool
 }
 
 // ---------------------------------------------------------------- unshard
-// Shard q occupies full[qS, (q+1)S).  Its interior 16-byte words of `full`
-// are copied with one aligned store each (the source word is realigned when
-// needed); the at most 14 edge elements that share a word with a
-// neighbouring shard are copied one by one.
-struct ShardSpan {
-    int64_t lo, a, b, hi;  // [lo, a) head, [a, b) whole words, [b, hi) tail
-};
-
-__device__ __forceinline__ ShardSpan shard_span(const uint16_t* full, int64_t S, int q) {
-    // element index e is 16-byte aligned in `full` when e % 8 == phase
-    const int64_t phase = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(full) & 15u)) & 15u) >> 1);
-    ShardSpan s;
-    s.lo = (int64_t)q * S;
-    s.hi = s.lo + S;
-    const int64_t up = s.lo + (((phase - s.lo) % 8) + 8) % 8;     // first aligned >= lo
-    s.a = up < s.hi ? up : s.hi;
-    const int64_t down = s.hi - (((s.hi - phase) % 8) + 8) % 8;   // last aligned <= hi
-    s.b = down > s.a ? down : s.a;
-    return s;
-}
-
-// Words w = w0 + u * kThreads (u < kUnroll) of shard q; loads first, then stores.
-__device__ __forceinline__ void copy_words(const uint16_t* src, uint16_t* full, const ShardSpan& sp,
-                                           int64_t w0) {
-    const int64_t n_words = (sp.b - sp.a) >> 3;
-    uint4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t w = w0 + (int64_t)u * kThreads;
-        if (w < n_words) v[u] = load16_any(src + (sp.a + (w << 3) - sp.lo));
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t w = w0 + (int64_t)u * kThreads;
-        if (w < n_words) *reinterpret_cast<uint4*>(full + sp.a + (w << 3)) = v[u];
-    }
+// Shard q's whole words of `full` are copied with one aligned store each
+// (the source realigned when needed); its at most 14 edge elements, which
+// share a word with a neighbouring shard, are copied one by one.
+template <bool kAligned>
+__device__ __forceinline__ void copy_word(const uint16_t* src, uint16_t* full, const ShardSpan& sp,
+                                          int64_t w) {
+    if (w < ((sp.b - sp.a) >> 3))
+        st16(full + sp.a + (w << 3), ld_bf16_word<kAligned>(src + (sp.a - sp.lo), w));
 }
 
 __device__ __forceinline__ void unshard_edges(const uint16_t* src, uint16_t* full, int64_t S, int q,
@@ -203,8 +214,8 @@ __device__ __forceinline__ void unshard_edges(const uint16_t* src, uint16_t* ful
 }
 
 // ---------------------------------------------------------------- grid barrier
-// Split-phase barrier over a grid whose workgroups are all resident, that
-// also ORs one bit (the overflow flag) over the grid.  Only thread 0 of a
+// Split-phase barrier over workgroups [0, n) of a grid, all resident, that
+// also ORs one bit (the overflow flag) over them.  Only thread 0 of a
 // workgroup takes part.  Arrival adds 1 (plus the bit at position 16) to
 // its group's counter; the group's last arrival resets that counter and
 // adds its group's result to the top counter; the last group resets the top
@@ -214,8 +225,8 @@ __device__ __forceinline__ void unshard_edges(const uint16_t* src, uint16_t* ful
 // relaxed agent-scope atomics suffice: no fences, no cache write-back.
 // Spreading the counters and the polled words over 32 cache lines keeps
 // arrival and polling off a single address.  The wait is bounded: should it
-// ever give up (possible only if the grid were not resident) it counts a
-// timeout in the workspace instead of hanging.
+// ever give up (possible only if the members were not resident together) it
+// counts a timeout in the workspace instead of hanging.
 constexpr unsigned kSpinLimit = 1u << 22;
 
 __device__ __forceinline__ unsigned sync_load(const unsigned* p) {
@@ -240,8 +251,7 @@ __device__ __forceinline__ BarrierTicket grid_ticket(GridSync* s) {
     return t;
 }
 
-__device__ __forceinline__ void grid_arrive(GridSync* s, const BarrierTicket& t, unsigned bit) {
-    const unsigned n = gridDim.x;
+__device__ __forceinline__ void grid_arrive(GridSync* s, const BarrierTicket& t, unsigned bit, unsigned n) {
     const unsigned n_groups = n < (unsigned)kSyncGroups ? n : (unsigned)kSyncGroups;
     const unsigned members = n / kSyncGroups + (t.group < n % kSyncGroups ? 1u : 0u);
     const unsigned inc = 1u + (bit << 16);
@@ -258,7 +268,7 @@ __device__ __forceinline__ void grid_arrive(GridSync* s, const BarrierTicket& t,
     for (unsigned k = 0; k < n_groups; ++k) sync_store(&s->gen[k * kLineWords], next);
 }
 
-// Returns the grid's OR of the arrival bits.
+// Returns the members' OR of the arrival bits.
 __device__ __forceinline__ unsigned grid_wait(GridSync* s, const BarrierTicket& t) {
     const unsigned* word = &s->gen[t.group * kLineWords];
     for (unsigned i = 0; i < kSpinLimit; ++i) {
@@ -286,24 +296,21 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* p
 
 // ---------------------------------------------------------------- kernels
 
-__device__ __forceinline__ int64_t lane_chunk(int64_t tile, int u) {
-    return tile * kTileChunks + (int64_t)u * kThreads + threadIdx.x;
+__device__ __forceinline__ int64_t lane_chunk() {
+    return (int64_t)blockIdx.x * kTileChunks + threadIdx.x;
 }
 
-template <bool kAccumulate, bool kNorm>
+template <bool kAligned, bool kAccumulate, bool kNorm>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceArgs a) {
     const int64_t n_chunks = a.shard >> 3;
     bool bad = false;
     double sq = 0.0;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t c = lane_chunk(blockIdx.x, u);
-        if (c < n_chunks) {
-            float y[8];
-            reduce_chunk(a, c << 3, kAccumulate, y);
-            store_f32x8(a.acc + (c << 3), y);
-            check_chunk(y, bad, sq, kNorm);
-        }
+    const int64_t c = lane_chunk();
+    if (c < n_chunks) {
+        float y[8];
+        reduce_chunk<kAligned>(a, c, kAccumulate, y);
+        store_f32x8(a.acc + (c << 3), y);
+        check_chunk(y, bad, sq, kNorm);
     }
     const int64_t tail0 = n_chunks << 3;
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
@@ -320,18 +327,16 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceArgs a) {
     }
 }
 
+template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
     if (a.sq_norm != nullptr && blockIdx.x == 0) finalize_norm(a.partials, a.n_partials, a.sq_norm);
     const bool skip = a.found_inf != nullptr && *a.found_inf != 0;
     const int64_t n_chunks = a.shard >> 3;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t c = lane_chunk(blockIdx.x, u);
-        if (c < n_chunks) {
-            float g[8];
-            if (!skip) load_f32x8(a.grad + (c << 3), g);
-            update_chunk(a, c << 3, g, skip, a.param_bf16);
-        }
+    const int64_t c = lane_chunk();
+    if (c < n_chunks) {
+        float g[8];
+        if (!skip) load_f32x8(a.grad + (c << 3), g);
+        update_chunk<kAligned>(a, c, g, skip, a.param_bf16);
     }
     const int64_t tail0 = n_chunks << 3;
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
@@ -340,13 +345,27 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
     }
 }
 
+template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void unshard_kernel(const UnshardArgs a) {
     const int q = blockIdx.y;
     const uint16_t* src = a.shards[q];
     if (src == nullptr) return;
     const ShardSpan sp = shard_span(a.full, a.shard, q);
-    copy_words(src, a.full, sp, (int64_t)blockIdx.x * kTileChunks + threadIdx.x);
+    copy_word<kAligned>(src, a.full, sp, lane_chunk());
     if (blockIdx.x == 0) unshard_edges(src, a.full, a.shard, q, threadIdx.x, kThreads);
+}
+
+// Copy role of the step kernels: workgroup idx takes tile idx % copy_tiles
+// of the idx / copy_tiles-th shard other than the own one.
+template <bool kAligned>
+__device__ __forceinline__ void copy_role(const StepArgs& a, unsigned idx) {
+    const unsigned qi = idx / (unsigned)a.copy_tiles;
+    const unsigned tile = idx - qi * (unsigned)a.copy_tiles;
+    const int q = (int)qi < a.rank ? (int)qi : (int)qi + 1;
+    const uint16_t* src = a.shards[q];
+    const ShardSpan sp = shard_span(a.full, a.shard, q);
+    copy_word<kAligned>(src, a.full, sp, (int64_t)tile * kTileChunks + threadIdx.x);
+    if (tile == 0) unshard_edges(src, a.full, a.shard, q, threadIdx.x, kThreads);
 }
 
 // First phase of the two-phase step (kFused = false: reduce into acc; the
@@ -354,109 +373,62 @@ __global__ __launch_bounds__(kThreads) void unshard_kernel(const UnshardArgs a) 
 // or the whole no-skip step (kFused = true: reduce, AdamW and cast in one
 // pass).  Workgroups [0, reduce_groups) take reduce tiles; the others take
 // (shard, tile) pairs of the copy of the other ranks' shards into `full`.
-template <bool kFused>
+template <bool kAligned, bool kFused>
 __global__ __launch_bounds__(kThreads) void step_phase1_kernel(const StepArgs a) {
-    if ((int)blockIdx.x < a.reduce_groups) {
-        const int64_t n_chunks = a.shard >> 3;
-        uint16_t* own = a.full + (int64_t)a.rank * a.shard;
-        const bool want_sq = a.partials != nullptr;
-        const bool acc_in = a.accumulate != 0;
-        bool bad = false;
-        double sq = 0.0;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t c = lane_chunk(blockIdx.x, u);
-            if (c < n_chunks) {
-                float y[8];
-                reduce_chunk(a, c << 3, acc_in, y);
-                check_chunk(y, bad, sq, want_sq);
-                if (!kFused || a.keep_grad) store_f32x8(a.acc + (c << 3), y);
-                if (kFused) update_chunk(a, c << 3, y, false, own);
-            }
-        }
-        const int64_t tail0 = n_chunks << 3;
-        if (blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
-            const int64_t j = tail0 + threadIdx.x;
-            const float y = reduce_elem(a, j, acc_in);
-            bad |= !finite_f32(y);
-            if (want_sq) sq += (double)y * (double)y;
-            if (!kFused || a.keep_grad) a.acc[j] = y;
-            if (kFused) update_elem(a, j, y, false, own);
-        }
-        flag_if_any(bad, a.found_inf);
-        if (want_sq) {
-            const double t = group_sum(sq);
-            if (threadIdx.x == 0) a.partials[blockIdx.x] = t;
-        }
-    } else {
-        const unsigned idx = blockIdx.x - (unsigned)a.reduce_groups;
-        const unsigned qi = idx / (unsigned)a.copy_tiles;
-        const unsigned tile = idx - qi * (unsigned)a.copy_tiles;
-        const int q = (int)qi < a.rank ? (int)qi : (int)qi + 1;
-        const uint16_t* src = a.shards[q];
-        const ShardSpan sp = shard_span(a.full, a.shard, q);
-        copy_words(src, a.full, sp, (int64_t)tile * kTileChunks + threadIdx.x);
-        if (tile == 0) unshard_edges(src, a.full, a.shard, q, threadIdx.x, kThreads);
+    if (blockIdx.x >= (unsigned)a.reduce_groups) {
+        copy_role<kAligned>(a, blockIdx.x - (unsigned)a.reduce_groups);
+        return;
+    }
+    const int64_t n_chunks = a.shard >> 3;
+    uint16_t* own = a.full + (int64_t)a.rank * a.shard;
+    const bool want_sq = a.partials != nullptr;
+    const bool acc_in = a.accumulate != 0;
+    bool bad = false;
+    double sq = 0.0;
+    const int64_t c = lane_chunk();
+    if (c < n_chunks) {
+        float y[8];
+        reduce_chunk<kAligned>(a, c, acc_in, y);
+        check_chunk(y, bad, sq, want_sq);
+        if (!kFused || a.keep_grad) store_f32x8(a.acc + (c << 3), y);
+        if (kFused) update_chunk<kAligned>(a, c, y, false, own);
+    }
+    const int64_t tail0 = n_chunks << 3;
+    if (blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
+        const int64_t j = tail0 + threadIdx.x;
+        const float y = reduce_elem(a, j, acc_in);
+        bad |= !finite_f32(y);
+        if (want_sq) sq += (double)y * (double)y;
+        if (!kFused || a.keep_grad) a.acc[j] = y;
+        if (kFused) update_elem(a, j, y, false, own);
+    }
+    flag_if_any(bad, a.found_inf);
+    if (want_sq) {
+        const double t = group_sum(sq);
+        if (threadIdx.x == 0) a.partials[blockIdx.x] = t;
     }
 }
 
-// Copy of every other rank's shard, words lane_base + u*256 (+ span), with
-// the loads of kQ shards in flight before their stores.
-template <int kC>
-__device__ __forceinline__ void copy_other_shards(const StepArgs& a, int64_t lane_base, int64_t span) {
-    constexpr int kQ = 8 / kC;
-    for (int q0 = 0; q0 < a.world; q0 += kQ) {
-        ShardSpan sp[kQ];
-        int64_t n_words[kQ];
-        bool use[kQ];
-#pragma unroll
-        for (int k = 0; k < kQ; ++k) {
-            const int q = q0 + k;
-            use[k] = q < a.world && q != a.rank;
-            if (use[k]) {
-                sp[k] = shard_span(a.full, a.shard, q);
-                n_words[k] = (sp[k].b - sp[k].a) >> 3;
-            } else {
-                n_words[k] = 0;
-            }
-        }
-        for (int64_t w0 = lane_base;; w0 += span) {
-            bool more = false;
-            uint4 v[kQ][kC];
-#pragma unroll
-            for (int k = 0; k < kQ; ++k)
-#pragma unroll
-                for (int u = 0; u < kC; ++u) {
-                    const int64_t w = w0 + (int64_t)u * kThreads;
-                    if (w < n_words[k]) {
-                        v[k][u] = load16_any(a.shards[q0 + k] + (sp[k].a + (w << 3) - sp[k].lo));
-                        more = true;
-                    }
-                }
-#pragma unroll
-            for (int k = 0; k < kQ; ++k)
-#pragma unroll
-                for (int u = 0; u < kC; ++u) {
-                    const int64_t w = w0 + (int64_t)u * kThreads;
-                    if (w < n_words[k]) *reinterpret_cast<uint4*>(a.full + sp[k].a + (w << 3)) = v[k][u];
-                }
-            if (!more) break;
-        }
-    }
-}
-
-// One-pass exact-skip step over a resident grid.  Each lane loads, for its
-// kC chunks, the ranks' gradient words and the fp32 master / moments (none
-// of which depends on the overflow flag), reduces, and computes the AdamW
-// update into registers.  The workgroup ORs its overflow bit (and the flag
-// left by earlier micro-batches) into the grid barrier and arrives; it
-// copies its share of the other ranks' shards while the barrier completes;
-// the barrier returns the grid's flag, after which the lane only stores:
-// the new state and its bf16 cast, or on overflow just the cast of the old
-// master.  The reduced gradient never leaves the registers, so the step
-// moves exactly the algorithmic bytes.
-template <int kC>
+// One-pass exact-skip step.  Workgroups [0, reduce_groups) take part in a
+// grid barrier and must be resident together (the grid is sized for it);
+// each of their lanes loads, for its kC chunks, the ranks' gradient words
+// and the fp32 master / moments (none of which depends on the overflow
+// flag), reduces, and computes the AdamW update into registers.  The
+// workgroup ORs its overflow bit (and the flag left by earlier
+// micro-batches) into the barrier and waits; the barrier returns the grid's
+// flag, after which the lanes only store: the new state and its bf16 cast,
+// or on overflow just the cast of the old master.  Workgroups past
+// reduce_groups copy the other ranks' shards meanwhile and take no part in
+// the barrier.  The reduced gradient never leaves the registers, so the
+// step moves exactly the algorithmic bytes.
+template <bool kAligned, int kC>
 __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
+    FP_PHASE_MARK(0);
+    if (blockIdx.x >= (unsigned)a.reduce_groups) {
+        copy_role<kAligned>(a, blockIdx.x - (unsigned)a.reduce_groups);
+        FP_PHASE_MARK(5);
+        return;
+    }
     __shared__ unsigned s_skip;
     const int64_t n_chunks = a.shard >> 3;
     const bool want_sq = a.partials != nullptr;
@@ -484,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
             load_f32x8(a.exp_avg + j0, m[u]);
             load_f32x8(a.exp_avg_sq + j0, v[u]);
             float y[8];
-            reduce_chunk(a, j0, acc_in, y);
+            reduce_chunk<kAligned>(a, c, acc_in, y);
             check_chunk(y, bad, sq, want_sq);
             if (a.keep_grad) store_f32x8(a.acc + j0, y);
             old_bf16[u] = f32x8_to_bf16(th[u]);
@@ -506,20 +478,19 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
         if (a.keep_grad) a.acc[j] = yt;
         adamw_elem(a.c, yt, tt, tm, tv);
     }
+    FP_PHASE_MARK(1);
     const int group_bad = __syncthreads_or(bad);
     if (want_sq) {
         const double t = group_sum(sq);
         if (threadIdx.x == 0) a.partials[blockIdx.x] = t;   // summed by a follow-up kernel
     }
-    if (threadIdx.x == 0) grid_arrive(a.sync, ticket, (group_bad || prior) ? 1u : 0u);
-
-    // the other ranks' shards, independent of the flag
-    copy_other_shards<kC>(a, base, (int64_t)gridDim.x * kThreads * kC);
-    if (blockIdx.x == 0)
-        for (int q = 0; q < a.world; ++q)
-            if (q != a.rank) unshard_edges(a.shards[q], a.full, a.shard, q, threadIdx.x, kThreads);
-
-    if (threadIdx.x == 0) s_skip = grid_wait(a.sync, ticket);
+    FP_PHASE_MARK(2);
+    if (threadIdx.x == 0) {
+        grid_arrive(a.sync, ticket, (group_bad || prior) ? 1u : 0u, (unsigned)a.reduce_groups);
+        FP_PHASE_MARK(3);
+        s_skip = grid_wait(a.sync, ticket);
+    }
+    FP_PHASE_MARK(4);
     __syncthreads();
     const bool skip = s_skip != 0u;
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.found_inf = skip ? 1 : 0;
@@ -531,12 +502,12 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
         if (c < n_chunks) {
             const int64_t j0 = c << 3;
             if (skip) {
-                store16_any(own + j0, old_bf16[u]);
+                st_bf16_word<kAligned>(own, c, old_bf16[u]);
             } else {
                 store_f32x8(a.master + j0, th[u]);
                 store_f32x8(a.exp_avg + j0, m[u]);
                 store_f32x8(a.exp_avg_sq + j0, v[u]);
-                store16_any(own + j0, f32x8_to_bf16(th[u]));
+                st_bf16_word<kAligned>(own, c, f32x8_to_bf16(th[u]));
             }
         }
     }
@@ -551,19 +522,23 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
             own[j] = (uint16_t)bf16x2(tt, 0.0f);
         }
     }
+    FP_PHASE_MARK(5);
 }
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, hipStream_t s) {
-    const bool norm = a.partials != nullptr;
-    if (a.accumulate) {
-        if (norm) reduce_kernel<true, true><<<(unsigned)grid, kThreads, 0, s>>>(a);
-        else reduce_kernel<true, false><<<(unsigned)grid, kThreads, 0, s>>>(a);
+hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStream_t s) {
+    const bool norm = a.partials != nullptr, acc = a.accumulate != 0;
+    const dim3 g((unsigned)grid);
+#define FP_REDUCE(AL, AC, NO) reduce_kernel<AL, AC, NO><<<g, kThreads, 0, s>>>(a)
+    if (aligned) {
+        if (acc) { if (norm) FP_REDUCE(true, true, true); else FP_REDUCE(true, true, false); }
+        else { if (norm) FP_REDUCE(true, false, true); else FP_REDUCE(true, false, false); }
     } else {
-        if (norm) reduce_kernel<false, true><<<(unsigned)grid, kThreads, 0, s>>>(a);
-        else reduce_kernel<false, false><<<(unsigned)grid, kThreads, 0, s>>>(a);
+        if (acc) { if (norm) FP_REDUCE(false, true, true); else FP_REDUCE(false, true, false); }
+        else { if (norm) FP_REDUCE(false, false, true); else FP_REDUCE(false, false, false); }
     }
+#undef FP_REDUCE
     return hipGetLastError();
 }
 
@@ -572,57 +547,72 @@ hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_adamw(const AdamArgs& a, int64_t grid, hipStream_t s) {
-    adamw_kernel<<<(unsigned)grid, kThreads, 0, s>>>(a);
+hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s) {
+    if (aligned) adamw_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(a);
+    else adamw_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, hipStream_t s) {
-    unshard_kernel<<<dim3((unsigned)grid_x, a.world), kThreads, 0, s>>>(a);
+hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hipStream_t s) {
+    const dim3 g((unsigned)grid_x, a.world);
+    if (aligned) unshard_kernel<true><<<g, kThreads, 0, s>>>(a);
+    else unshard_kernel<false><<<g, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, hipStream_t s) {
-    if (fused_update) step_phase1_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(a);
-    else step_phase1_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(a);
+hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool aligned,
+                              hipStream_t s) {
+    const dim3 g((unsigned)grid);
+    if (aligned) {
+        if (fused_update) step_phase1_kernel<true, true><<<g, kThreads, 0, s>>>(a);
+        else step_phase1_kernel<true, false><<<g, kThreads, 0, s>>>(a);
+    } else {
+        if (fused_update) step_phase1_kernel<false, true><<<g, kThreads, 0, s>>>(a);
+        else step_phase1_kernel<false, false><<<g, kThreads, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
 namespace {
-// Co-resident workgroups per CU of each one-pass instantiation and the CU
-// count, per device: fixed properties of the device and the code object,
-// computed on first use and kept for the life of the process.
+// Resident workgroups per CU of each one-pass variant and the CU count, per
+// device: fixed properties of the device and the code object, computed on
+// first use and kept for the life of the process.  The smaller of the
+// aligned and general forms' figures bounds both.
 constexpr int kMaxDevices = 64;
+constexpr int kVariants = 2;  // lanes keep 1 or kMaxCoopChunks chunks
 struct CoopLimits {
     std::atomic<int> state{0};  // 0 unknown, 1 computing, 2 ready
     int cus = 0;
-    int per_cu[2] = {0, 0};
+    int per_cu[kVariants] = {0, 0};
 };
 CoopLimits g_limits[kMaxDevices];
 
-const void* coop_fn(int i) {
-    return i == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<1>)
-                  : reinterpret_cast<const void*>(&step_coop_kernel<kMaxCoopChunks>);
+const void* coop_fn(int variant, bool aligned) {
+    if (aligned)
+        return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<true, 1>)
+                            : reinterpret_cast<const void*>(&step_coop_kernel<true, kMaxCoopChunks>);
+    return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<false, 1>)
+                        : reinterpret_cast<const void*>(&step_coop_kernel<false, kMaxCoopChunks>);
 }
 
 hipError_t coop_limits(int dev, const CoopLimits** out) {
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     CoopLimits& L = g_limits[dev];
-    int expect = 0;
-    if (L.state.load(std::memory_order_acquire) != 2) {
-        if (L.state.compare_exchange_strong(expect, 1)) {
+    for (;;) {
+        const int state = L.state.load(std::memory_order_acquire);
+        if (state == 2) break;
+        int expect = 0;
+        if (state == 0 && L.state.compare_exchange_strong(expect, 1)) {
             hipError_t e = hipDeviceGetAttribute(&L.cus, hipDeviceAttributeMultiprocessorCount, dev);
-            for (int i = 0; i < 2 && e == hipSuccess; ++i)
-                e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&L.per_cu[i], coop_fn(i), kThreads, 0);
-            if (e != hipSuccess) {
-                L.state.store(0, std::memory_order_release);
-                return e;
+            for (int i = 0; i < kVariants && e == hipSuccess; ++i) {
+                int a = 0, b = 0;
+                e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, coop_fn(i, true), kThreads, 0);
+                if (e == hipSuccess)
+                    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, coop_fn(i, false), kThreads, 0);
+                L.per_cu[i] = a < b ? a : b;
             }
-            L.state.store(2, std::memory_order_release);
-        } else {
-            while (L.state.load(std::memory_order_acquire) != 2) {
-                if (L.state.load(std::memory_order_acquire) == 0) return coop_limits(dev, out);
-            }
+            L.state.store(e == hipSuccess ? 2 : 0, std::memory_order_release);
+            if (e != hipSuccess) return e;
         }
     }
     *out = &L;
@@ -638,8 +628,8 @@ hipError_t plan_step_coop(int64_t shard, int* variant, int* grid) {
     if ((e = coop_limits(dev, &L)) != hipSuccess) return e;
     *variant = -1;
     const int64_t n_chunks = shard >> 3;
-    const int chunks[2] = {1, kMaxCoopChunks};
-    for (int i = 0; i < 2; ++i) {
+    const int chunks[kVariants] = {1, kMaxCoopChunks};
+    for (int i = 0; i < kVariants; ++i) {
         const int64_t g = n_chunks > 0 ? ceil_div64(n_chunks, (int64_t)kThreads * chunks[i]) : 1;
         if (g <= (int64_t)L->per_cu[i] * L->cus) {
             *variant = i;
@@ -650,12 +640,23 @@ hipError_t plan_step_coop(int64_t shard, int* variant, int* grid) {
     return hipSuccess;
 }
 
-hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, hipStream_t s) {
-    // A plain launch: the grid fits the device's resident capacity, so on a
-    // GPU not running other work every workgroup is resident at once (a
-    // cooperative launch would guarantee it at ~17 us extra per launch).
-    if (variant == 0) step_coop_kernel<1><<<grid, kThreads, 0, s>>>(a);
-    else step_coop_kernel<kMaxCoopChunks><<<grid, kThreads, 0, s>>>(a);
+hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, hipStream_t s) {
+    // A plain launch (a cooperative launch costs ~17 us more per launch on
+    // MI355X).  The barrier workgroups [0, reduce_groups) fit the device's
+    // resident capacity and are dispatched before the copy workgroups, which
+    // never wait; so on a GPU not running other work they are resident
+    // together, and otherwise they become so as the copy workgroups finish.
+    StepArgs b = a;
+    b.reduce_groups = grid;
+    b.copy_tiles = (int32_t)copy_tiles_per_shard(a.shard);
+    const dim3 g((unsigned)((int64_t)grid + (int64_t)(a.world - 1) * b.copy_tiles));
+    if (aligned) {
+        if (variant == 0) step_coop_kernel<true, 1><<<g, kThreads, 0, s>>>(b);
+        else step_coop_kernel<true, kMaxCoopChunks><<<g, kThreads, 0, s>>>(b);
+    } else {
+        if (variant == 0) step_coop_kernel<false, 1><<<g, kThreads, 0, s>>>(b);
+        else step_coop_kernel<false, kMaxCoopChunks><<<g, kThreads, 0, s>>>(b);
+    }
     return hipGetLastError();
 }
 
