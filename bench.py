@@ -143,6 +143,22 @@ def cpu_baseline(cfg, rank, budget_s: float):
                       f"N_d={world}) by the serial oracle: reduce, AdamW, bf16 cast, unshard"}
 
 
+def copy_calibration(fp, dev, launches: int) -> int:
+    """fp_unshard of 16 aligned shards of 8M bf16 elements: 256 MiB read and
+    256 MiB written per launch, the reference for scaling HBM byte counters."""
+    import torch
+    world, S = 16, 8 * 1024 * 1024
+    src = torch.ones(world * S, dtype=torch.int16, device=dev)
+    full = torch.zeros(world * S, dtype=torch.int16, device=dev)
+    shards = [src[q * S:(q + 1) * S] for q in range(world)]
+    for _ in range(max(1, launches)):
+        fp.unshard(shards, full)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "unshard_kernel", "launches": max(1, launches),
+                      "read_bytes_per_launch": 2 * world * S, "write_bytes_per_launch": 2 * world * S}))
+    return 0
+
+
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources."""
@@ -168,6 +184,8 @@ def main(argv=None) -> int:
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python with per-kernel events (launch-bound for "
                          "small shards) instead of replaying a captured HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run fp_unshard (a plain copy of known size) for counter calibration")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)
@@ -187,6 +205,8 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        return copy_calibration(fp, dev, args.steps)
     cfg = CONFIGS[args.workload]
     if cfg.shapes is None or cfg.n_micro != 1:
         print("bench.py times single-unit, single-micro-batch workloads", file=sys.stderr)
