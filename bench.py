@@ -294,14 +294,14 @@ def main(argv=None) -> int:
     if any(fp.workspace_timeouts(s["workspace"]) for s in sets):
         print("grid barrier wait gave up", file=sys.stderr)
         return 1
-    one_kernel = k2_ms < 0.2 * k1_ms          # the one-pass path launches one kernel
+    path = calls[0].path()
     step_ms = (span_ms / K) if not args.eager else (k1_ms + k2_ms)
     ms_step = elapsed * 1e3 / K
     gbs = S * B * K / elapsed / 1e9
-    if flags == fp.FP_STEP_NO_SKIP or one_kernel:
+    if path in (fp.FP_PATH_NO_SKIP, fp.FP_PATH_ONE_PASS):
         # one kernel per step: its average duration is the step's (graph span / steps)
-        nm = "step_phase1_kernel<true>" if flags == fp.FP_STEP_NO_SKIP else "step_coop_kernel"
-        kid = "step_phase1_fused" if flags == fp.FP_STEP_NO_SKIP else "step_coop"
+        nm = "step_phase1_kernel<true>" if path == fp.FP_PATH_NO_SKIP else "step_coop_kernel"
+        kid = "step_phase1_fused" if path == fp.FP_PATH_NO_SKIP else "step_coop"
         kernels = [(nm, kid, step_ms, S * B)]
     else:
         frac1 = k1_ms / (k1_ms + k2_ms)
@@ -316,7 +316,9 @@ def main(argv=None) -> int:
         "vs_baseline": None, "dtype": "f32/f64", "data": "synthetic",
         "config": {"workload": cfg.name, "N_d": world, "rank": rank, "shard_elems": S,
                    "unit_elems": T, "n_micro": 1, "mode": args.mode,
-                   "alg_bytes_per_elem": B, "buffer_sets": n_sets},
+                   "alg_bytes_per_elem": B, "buffer_sets": n_sets,
+                   "path": {fp.FP_PATH_ONE_PASS: "one-pass", fp.FP_PATH_TWO_PHASE: "two-phase",
+                            fp.FP_PATH_NO_SKIP: "fused-no-skip"}[path]},
         "params_per_s": round(S * K / elapsed, 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "kernels": [{"name": n, "avg_us": round(d * 1e3, 3), "alg_bytes": a,

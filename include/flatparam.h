@@ -199,7 +199,9 @@ typedef struct fp_adamw_hparams {
  *   m = beta1 * exp_avg[i] + (1 - beta1) * g[i]
  *   v = beta2 * exp_avg_sq[i] + (1 - beta2) * g[i]^2
  *   theta = theta - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
- * and master, exp_avg, exp_avg_sq are each rounded once to fp32.
+ * (evaluated with the bias corrections folded into lr / (1 - beta1^t) and
+ * 1 / sqrt(1 - beta2^t), derived once in fp64), and master, exp_avg,
+ * exp_avg_sq are each rounded once to fp32.
  * If found_inf != NULL and *found_inf != 0 (read on the device) the update
  * is skipped: master / exp_avg / exp_avg_sq are left untouched.
  * If param_bf16 != NULL, param_bf16[i] = bf16 round-to-nearest-even of the
@@ -282,6 +284,19 @@ typedef struct fp_step_args {
 #define FP_STEP_EVENTS 3
 
 fp_status fp_shard_step(const fp_step_args* args, void* stream);
+
+/* The kernels fp_shard_step launches for these arguments on the current
+ * device, after the same argument checks (nothing is launched):
+ *   FP_PATH_ONE_PASS  -- one kernel (then the norm finalisation if sq_norm);
+ *   FP_PATH_TWO_PHASE -- reduce + copy kernel, then the AdamW kernel;
+ *   FP_PATH_NO_SKIP   -- one fused kernel (then the norm finalisation if
+ *                        sq_norm).
+ * The one-pass choice depends on the device's co-resident capacity, hence
+ * on the device current at the call. */
+#define FP_PATH_ONE_PASS 0
+#define FP_PATH_TWO_PHASE 1
+#define FP_PATH_NO_SKIP 2
+fp_status fp_step_path(const fp_step_args* args, int32_t* path);
 
 /* ------------------------------------------------------------------ helpers */
 

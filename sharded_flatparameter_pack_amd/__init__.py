@@ -20,12 +20,14 @@ import math
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import (FP_MAX_WORLD, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD,  # noqa: F401
-                   FP_STEP_NO_COOP, FP_STEP_NO_SKIP, FlatParamError, check, lib)
+from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_ONE_PASS,  # noqa: F401
+                   FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
+                   FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
 __all__ = ["Plan", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
-           "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "library_path"]
+           "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
+           "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "library_path"]
 
 
 def library_path() -> str:
@@ -232,37 +234,10 @@ def shard_step(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int,
                lr, beta1, beta2, eps, weight_decay, step: int, found_inf, accumulate: bool = False,
                sq_norm=None, workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None):
     """Reduce (last micro-batch) + AdamW + bf16 cast + unshard for this rank."""
-    torch = _torch()
-    S = master.numel()
-    gptr = _rank_ptrs(grads, S, "grads")
-    world = len(gptr)
-    sptr = _rank_ptrs(shards, S, "shards", allow_none=True)
-    if len(sptr) != world:
-        raise ValueError("shards and grads differ in length")
-    a = _lib.fp_step_args()
-    gt, st = _ptr_table(gptr), _ptr_table(sptr)
-    a.shard, a.world, a.rank = S, world, int(rank)
-    a.grads = C.cast(gt, C.c_void_p)
-    a.scale, a.accumulate = float(scale), int(bool(accumulate))
-    a.acc = _f32(acc, S, "acc")
-    a.master = _f32(master, S, "master")
-    a.exp_avg = _f32(exp_avg, S, "exp_avg")
-    a.exp_avg_sq = _f32(exp_avg_sq, S, "exp_avg_sq")
-    a.hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
-    a.shards = C.cast(st, C.c_void_p)
-    a.full = _bf16(full, S * world, "full")
-    a.found_inf = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf")
-    a.sq_norm = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
-    a.workspace = (_dev_ptr(workspace, (torch.uint8,), workspace_bytes(S), "workspace")
-                   if workspace is not None else None)
-    a.flags = int(flags)
-    ev = None
-    if profile_events is not None:
-        if len(profile_events) != _lib.FP_STEP_EVENTS:
-            raise ValueError(f"profile_events needs {_lib.FP_STEP_EVENTS} hipEvent_t handles")
-        ev = (C.c_void_p * _lib.FP_STEP_EVENTS)(*profile_events)
-        a.profile_events = C.cast(ev, C.c_void_p)
-    check(lib().fp_shard_step(C.byref(a), _stream(master)))
+    ShardStep(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank, scale=scale, lr=lr,
+              beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay, found_inf=found_inf,
+              accumulate=accumulate, sq_norm=sq_norm, workspace=workspace,
+              flags=flags)(step, profile_events)
 
 
 class ShardStep:
@@ -310,10 +285,21 @@ class ShardStep:
         if profile_events is None:
             a.profile_events = None
         else:
+            if len(profile_events) != _lib.FP_STEP_EVENTS:
+                raise ValueError(f"profile_events needs {_lib.FP_STEP_EVENTS} hipEvent_t handles")
             for i, e in enumerate(profile_events):
                 self._events[i] = e
             a.profile_events = C.cast(self._events, C.c_void_p)
         check(self._fn(C.byref(a), _stream(self._device)))
+
+    def path(self) -> int:
+        """FP_PATH_ONE_PASS, FP_PATH_TWO_PHASE or FP_PATH_NO_SKIP: the kernels
+        a call launches on this device."""
+        torch = _torch()
+        out = C.c_int32(-1)
+        with torch.cuda.device(self._device):
+            check(lib().fp_step_path(C.byref(self._args), C.byref(out)))
+        return out.value
 
 
 # ------------------------------------------------------------------ helpers

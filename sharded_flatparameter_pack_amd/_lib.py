@@ -24,6 +24,9 @@ FP_STEP_NO_SKIP = 1
 FP_STEP_KEEP_GRAD = 2
 FP_STEP_NO_COOP = 4
 FP_STEP_EVENTS = 3
+FP_PATH_ONE_PASS = 0
+FP_PATH_TWO_PHASE = 1
+FP_PATH_NO_SKIP = 2
 FP_WORKSPACE_TIMEOUTS_OFFSET = 8320
 
 _i32, _i64, _f32, _f64, _vp = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p
@@ -59,6 +62,7 @@ SIGNATURES = {
     "fp_adamw_shard": (_i32, [_i64, C.POINTER(fp_adamw_hparams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp_unshard": (_i32, [_i64, _i32, _vp, _vp, _vp]),
     "fp_shard_step": (_i32, [C.POINTER(fp_step_args), _vp]),
+    "fp_step_path": (_i32, [C.POINTER(fp_step_args), C.POINTER(C.c_int32)]),
     "fp_state_bytes": (_i32, [_f64, _i32, _f64, _i32, C.POINTER(_f64)]),
     "fp_status_string": (C.c_char_p, [_i32]),
     "fp_last_error": (C.c_char_p, []),

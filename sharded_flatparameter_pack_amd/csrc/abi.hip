@@ -34,7 +34,7 @@ fp_status device_fail(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
-bool is_aligned16(const void* p) { return aligned(p, 16); }
+bool is_aligned8(const void* p) { return aligned(p, 8); }
 
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -43,9 +43,9 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workgroups of a tiled stream over S elements in 8-element chunks.
+// Workgroups of a tiled stream over S elements in 4-element quads.
 int64_t stream_grid(int64_t shard) {
-    const int64_t t = tiles_of(shard >> 3);
+    const int64_t t = tiles_of(shard >> 2);
     return t > 0 ? t : 1;
 }
 
@@ -66,9 +66,10 @@ fp_status check_hparams(const fp_adamw_hparams* hp, AdamCoef* c) {
     c->one_m_beta1 = 1.0 - hp->beta1;
     c->beta2 = hp->beta2;
     c->one_m_beta2 = 1.0 - hp->beta2;
-    c->bias1 = 1.0 - std::pow(hp->beta1, (double)hp->step);
-    c->bias2 = 1.0 - std::pow(hp->beta2, (double)hp->step);
-    c->lr = hp->lr;
+    const double bias1 = 1.0 - std::pow(hp->beta1, (double)hp->step);
+    const double bias2 = 1.0 - std::pow(hp->beta2, (double)hp->step);
+    c->step_size = hp->lr / bias1;
+    c->inv_sqrt_bias2 = 1.0 / std::sqrt(bias2);
     c->eps = hp->eps;
     return FP_OK;
 }
@@ -354,7 +355,7 @@ extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_
     a.world = world;
     a.accumulate = accumulate ? 1 : 0;
     bool aligned = true;
-    for (int32_t q = 0; q < world; ++q) aligned = aligned && is_aligned16(grads[q]);
+    for (int32_t q = 0; q < world; ++q) aligned = aligned && is_aligned8(grads[q]);
     const int64_t grid = stream_grid(shard);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_reduce(a, grid, aligned, s);
@@ -397,7 +398,7 @@ extern "C" fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, c
     a.param_bf16 = param_bf16;
     a.found_inf = found_inf;
     a.shard = shard;
-    const bool aligned = param_bf16 == nullptr || is_aligned16(param_bf16);
+    const bool aligned = param_bf16 == nullptr || is_aligned8(param_bf16);
     hipError_t e = launch_adamw(a, stream_grid(shard), aligned, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "adamw launch");
     return FP_OK;
@@ -426,16 +427,17 @@ extern "C" fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* co
     bool aligned = true;
     for (int32_t q = 0; q < world; ++q)
         if (shards[q] != nullptr) aligned = aligned && copy_source_aligned(shards[q], full, shard, q);
-    hipError_t e = launch_unshard(a, copy_tiles_per_shard(shard), aligned, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_unshard(a, copy_tiles_per_shard(shard, kCopyWordsStream), aligned, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "unshard launch");
     return FP_OK;
 }
 
 // ---------------------------------------------------------------------- step
 
-extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
-    if (args == nullptr) return fail(FP_ERR_INVALID, "args is NULL");
-    const fp_step_args& x = *args;
+namespace {
+
+// Every check of fp_shard_step's arguments; the AdamW coefficients on success.
+fp_status check_step(const fp_step_args& x, AdamCoef* c) {
     fp_status st;
     const int64_t S = x.shard;
     if (S < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
@@ -443,9 +445,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     if (x.rank < 0 || x.rank >= x.world) return fail(FP_ERR_RANGE, "rank %d outside [0, %d)", x.rank, x.world);
     if (x.flags & ~(FP_STEP_NO_SKIP | FP_STEP_KEEP_GRAD | FP_STEP_NO_COOP))
         return fail(FP_ERR_INVALID, "unknown flags");
-    StepArgs a;
-    std::memset(&a, 0, sizeof a);
-    if ((st = check_hparams(&x.hp, &a.c)) != FP_OK) return st;
+    if ((st = check_hparams(&x.hp, c)) != FP_OK) return st;
     if ((st = check_ptr_table(x.grads, x.world, S, false, "grads")) != FP_OK) return st;
     if ((st = check_ptr_table(x.shards, x.world, S, true, "shards")) != FP_OK) return st;
     for (int32_t q = 0; q < x.world; ++q)
@@ -477,8 +477,50 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
         if (q != x.rank && overlap(x.shards[q], b2, x.full, bf))
             return fail(FP_ERR_INVALID, "shards[%d] overlaps full", q);
     }
+    return FP_OK;
+}
 
-    const bool no_skip = (x.flags & FP_STEP_NO_SKIP) != 0;
+// The kernels a validated step launches: FP_PATH_*, and for the one-pass
+// path its variant and grid.
+fp_status step_path(const fp_step_args& x, int32_t* path, int* variant, int* grid) {
+    *variant = -1;
+    *grid = 0;
+    if (x.flags & FP_STEP_NO_SKIP) {
+        *path = FP_PATH_NO_SKIP;
+        return FP_OK;
+    }
+    if (x.workspace != nullptr && !(x.flags & FP_STEP_NO_COOP)) {
+        const hipError_t e = plan_step_coop(x.shard, variant, grid);
+        if (e != hipSuccess) return device_fail(e, "occupancy query");
+    }
+    *path = *variant >= 0 ? FP_PATH_ONE_PASS : FP_PATH_TWO_PHASE;
+    return FP_OK;
+}
+
+}  // namespace
+
+extern "C" fp_status fp_step_path(const fp_step_args* args, int32_t* path) {
+    if (args == nullptr || path == nullptr) return fail(FP_ERR_INVALID, "args or path is NULL");
+    AdamCoef c;
+    fp_status st = check_step(*args, &c);
+    if (st != FP_OK) return st;
+    int variant, grid;
+    return step_path(*args, path, &variant, &grid);
+}
+
+extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
+    if (args == nullptr) return fail(FP_ERR_INVALID, "args is NULL");
+    const fp_step_args& x = *args;
+    const int64_t S = x.shard;
+    StepArgs a;
+    std::memset(&a, 0, sizeof a);
+    fp_status st = check_step(x, &a.c);
+    if (st != FP_OK) return st;
+    int32_t path = 0;
+    int variant = -1, grid = 0;
+    if ((st = step_path(x, &path, &variant, &grid)) != FP_OK) return st;
+
+    const bool no_skip = path == FP_PATH_NO_SKIP;
     for (int32_t q = 0; q < x.world; ++q) {
         a.grads[q] = x.grads[q];
         a.shards[q] = q == x.rank ? nullptr : x.shards[q];
@@ -500,9 +542,9 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     a.sync = x.workspace != nullptr ? static_cast<GridSync*>(x.workspace) : nullptr;
 
     uint16_t* own = x.full + (int64_t)x.rank * S;
-    bool aligned = is_aligned16(own);
+    bool aligned = is_aligned8(own);
     for (int32_t q = 0; q < x.world; ++q) {
-        aligned = aligned && is_aligned16(x.grads[q]);
+        aligned = aligned && is_aligned8(x.grads[q]);
         if (q != x.rank) aligned = aligned && copy_source_aligned(x.shards[q], x.full, S, q);
     }
 
@@ -512,19 +554,15 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
         for (int i = 0; i < FP_STEP_EVENTS; ++i) ev[i] = static_cast<hipEvent_t>(x.profile_events[i]);
     hipError_t e;
 
-    if (!no_skip && a.sync != nullptr && !(x.flags & FP_STEP_NO_COOP)) {  // one pass, if it fits
-        int variant = -1, grid = 0;
-        if ((e = plan_step_coop(S, &variant, &grid)) != hipSuccess) return device_fail(e, "occupancy query");
-        if (variant >= 0) {
-            if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-            if ((e = launch_step_coop(a, variant, grid, aligned, s)) != hipSuccess)
-                return device_fail(e, "one-pass step launch");
-            if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-            if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, x.sq_norm, s)) != hipSuccess)
-                return device_fail(e, "norm launch");
-            if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-            return FP_OK;
-        }
+    if (path == FP_PATH_ONE_PASS) {
+        if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+        if ((e = launch_step_coop(a, variant, grid, aligned, s)) != hipSuccess)
+            return device_fail(e, "one-pass step launch");
+        if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+        if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, x.sq_norm, s)) != hipSuccess)
+            return device_fail(e, "norm launch");
+        if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+        return FP_OK;
     }
     if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
 
@@ -532,9 +570,9 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     // ranks' shards as (shard, tile) pairs, in one launch.
     const int64_t reduce_groups = stream_grid(S);
     a.reduce_groups = (int32_t)reduce_groups;
-    a.copy_tiles = (int32_t)copy_tiles_per_shard(S);
-    const int64_t grid = reduce_groups + (int64_t)(x.world - 1) * a.copy_tiles;
-    if (grid > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "shard too large for one launch");
+    a.copy_tiles = (int32_t)copy_tiles_per_shard(S, kCopyWordsStream);
+    const int64_t n_groups = reduce_groups + (int64_t)(x.world - 1) * a.copy_tiles;
+    if (n_groups > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "shard too large for one launch");
     AdamArgs d;
     std::memset(&d, 0, sizeof d);
     d.grad = x.acc;
@@ -548,14 +586,14 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     d.partials = a.partials;
     d.sq_norm = x.sq_norm;
     d.n_partials = (int32_t)reduce_groups;
-    if ((e = launch_step_phase1(a, grid, no_skip, aligned, s)) != hipSuccess) return device_fail(e, "step launch");
+    if ((e = launch_step_phase1(a, n_groups, no_skip, aligned, s)) != hipSuccess) return device_fail(e, "step launch");
     if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     if (no_skip) {
         if (x.sq_norm != nullptr &&
             (e = launch_norm_finalize(a.partials, (int)reduce_groups, x.sq_norm, s)) != hipSuccess)
             return device_fail(e, "norm launch");
     } else {
-        if ((e = launch_adamw(d, stream_grid(S), is_aligned16(own), s)) != hipSuccess)
+        if ((e = launch_adamw(d, stream_grid(S), is_aligned8(own), s)) != hipSuccess)
             return device_fail(e, "adamw launch");
     }
     if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");

@@ -35,7 +35,18 @@ __device__ __forceinline__ uint4 f32x8_to_bf16(const float f[8]) {
                       bf16x2(f[4], f[5]), bf16x2(f[6], f[7]));
 }
 
+// Four bf16 values (8 bytes) <-> fp32.
+__device__ __forceinline__ void bf16x4_to_f32(const uint2 w, float f[4]) {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+    f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+}
+
+__device__ __forceinline__ uint2 f32x4_to_bf16(const float f[4]) {
+    return make_uint2(bf16x2(f[0], f[1]), bf16x2(f[2], f[3]));
+}
+
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // Aligned 16-byte load / store with the non-temporal hint: every stream of
 // the step is touched once per step, so it should not displace other data
@@ -47,6 +58,62 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, const uint4 v) {
     const u32x4_t w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
+// 8-byte forms of the above, for bf16 quads.
+__device__ __forceinline__ uint2 ld8(const void* p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st8(void* p, const uint2 v) {
+    const u32x2_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+}
+
+// A bf16 stream read as 8-byte quads from a base on any 2-byte boundary:
+// the same branch-free scheme as Src16 below on an 8-byte grid (two aligned
+// 8-byte loads, the second repeating the first when the base is aligned,
+// then a byte funnel shift).
+struct Src8 {
+    const uint2* abase;  // aligned quad holding the base's first byte
+    uint32_t ds;         // dwords to skip in the 16-byte window (0 or 1)
+    uint32_t bs;         // then bytes to skip (0 or 2)
+    uint32_t step;       // 1 if misaligned, else 0
+};
+
+__device__ __forceinline__ Src8 src8(const void* base) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(base);
+    const uint32_t mis = static_cast<uint32_t>(a & 7u);
+    Src8 r;
+    r.abase = reinterpret_cast<const uint2*>(a - mis);
+    r.ds = mis >> 2;
+    r.bs = mis & 3u;
+    r.step = mis != 0 ? 1u : 0u;
+    return r;
+}
+
+// The 8 wanted bytes from the aligned quads lo (holding the first wanted
+// byte) and hi (the next quad, or lo again when the base is aligned).
+__device__ __forceinline__ uint2 realign8(const Src8& s, const uint2 lo, const uint2 hi) {
+    const uint32_t w0 = s.ds ? lo.y : lo.x;
+    const uint32_t w1 = s.ds ? hi.x : lo.y;
+    const uint32_t w2 = s.ds ? hi.y : hi.x;
+    return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, s.bs), __builtin_amdgcn_alignbyte(w2, w1, s.bs));
+}
+
+// 8 bytes to any 2-byte-aligned address, inside the 8 target bytes.
+__device__ __forceinline__ void store8_any(void* p, const uint2 v) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if ((a & 7u) == 0) {
+        *reinterpret_cast<uint2*>(p) = v;
+    } else if ((a & 3u) == 0) {
+        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+        q[0] = v.x; q[1] = v.y;
+    } else {
+        uint16_t* q = reinterpret_cast<uint16_t*>(p);
+        q[0] = (uint16_t)v.x; q[1] = (uint16_t)(v.x >> 16);
+        q[2] = (uint16_t)v.y; q[3] = (uint16_t)(v.y >> 16);
+    }
 }
 
 // A bf16 stream read as 16-byte words from a base that may sit anywhere on a

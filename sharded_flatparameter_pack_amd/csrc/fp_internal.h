@@ -12,16 +12,24 @@ namespace fpk {
 
 constexpr int kThreads = 256;          // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kElemsPerChunk = 8;      // one 16-byte bf16 word, two 16-byte fp32 words
-// A workgroup of a streaming kernel owns one tile of kTileChunks consecutive
-// chunks, one per lane, and tiles are numbered in dispatch order, so the
-// workgroups in flight cover one contiguous window of every stream -- on
-// MI355X this keeps HBM pages open far better than grid-stride loops, whose
-// concurrent accesses spread over the whole buffer.
-constexpr int kTileChunks = kThreads;
+// Element streams move in quads of 4 elements (16 bytes of fp32, 8 of bf16).
+// A workgroup of a streaming kernel owns one tile of kTileQuads consecutive
+// quads, kQuadsPerLane per lane, and tiles are numbered in dispatch order,
+// so the workgroups in flight cover one contiguous window of every stream --
+// on MI355X this keeps HBM pages open far better than grid-stride loops,
+// whose concurrent accesses spread over the whole buffer.
+constexpr int kQuadsPerLane = 2;
+constexpr int64_t kTileQuads = (int64_t)kThreads * kQuadsPerLane;
+// 16-byte words per lane of a copy workgroup.  Stand-alone copies and the
+// two-pass step use one (consecutive waves then sweep consecutive addresses,
+// the fastest pattern measured for long copies); the one-pass step uses four,
+// all loads issued before the stores, so that its fewer copy workgroups fit
+// beside the resident barrier workgroups from the start.
+constexpr int kCopyWordsStream = 1;
+constexpr int kCopyWordsCoop = 4;
 constexpr int kPackBlockElems = 8192;  // flat elements per pack workgroup
 constexpr int kPackLdsTensors = 1024;  // tensor descriptors a pack workgroup stages in LDS
-constexpr int kMaxCoopChunks = 2;      // chunks a lane keeps in registers in the one-pass step
+constexpr int kMaxCoopQuads = 4;       // quads a lane keeps in registers in the one-pass step
 constexpr int kSyncGroups = 32;        // first level of the grid barrier
 constexpr int kLineWords = 32;         // 128-byte cache line in 32-bit words
 
@@ -47,9 +55,8 @@ struct AdamCoef {
     double one_m_beta1;  // 1 - beta1
     double beta2;
     double one_m_beta2;  // 1 - beta2
-    double bias1;        // 1 - beta1^t
-    double bias2;        // 1 - beta2^t
-    double lr;
+    double step_size;       // lr / (1 - beta1^t)
+    double inv_sqrt_bias2;  // 1 / sqrt(1 - beta2^t)
     double eps;
 };
 
@@ -65,9 +72,9 @@ struct ReduceArgs {
 };
 
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t tiles_of(int64_t chunks) { return ceil_div64(chunks, kTileChunks); }
+inline int64_t tiles_of(int64_t quads) { return ceil_div64(quads, kTileQuads); }
 // Copy tiles per shard: the whole 16-byte words of a shard number at most S/8 + 1.
-inline int64_t copy_tiles_per_shard(int64_t S) { return ceil_div64(S / 8 + 1, kTileChunks); }
+inline int64_t copy_tiles_per_shard(int64_t S, int words) { return ceil_div64(S / 8 + 1, (int64_t)kThreads * words); }
 
 // Shard q occupies full[qS, (q+1)S).  [lo, a) and [b, hi) are its edge
 // elements that share a 16-byte word of `full` with a neighbouring shard;
@@ -97,7 +104,7 @@ inline bool copy_source_aligned(const uint16_t* src, const uint16_t* full, int64
 }
 // Norm partial slots the workspace provides for a shard of S elements (one
 // per workgroup of any launch geometry used for that shard).
-inline int64_t partial_slots(int64_t S) { return ceil_div64(S / 8, kThreads) + 1; }
+inline int64_t partial_slots(int64_t S) { return ceil_div64(S / 4, kTileQuads) + 1; }
 
 struct AdamArgs {
     const float* grad;
@@ -158,8 +165,9 @@ struct PackArgs {
 };
 
 // Launchers (return the HIP error of the launch).
-// `aligned`: every bf16 stream of the launch is 16-byte aligned at the words
-// the kernel reads or writes (then no realignment code runs).
+// `aligned`: every bf16 quad stream of the launch (gradients, own shard) is
+// 8-byte aligned and every copy source is 16-byte aligned at the words the
+// kernel reads (then no realignment code runs).
 hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s);
@@ -167,8 +175,8 @@ hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hi
 hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool aligned,
                               hipStream_t s);
 // One-pass exact-skip step: plan_step_coop picks the variant (lanes keep
-// 1, 2 or 4 chunks in registers) and a grid that fits the device's
-// co-resident capacity, or sets *variant = -1 when the shard is too large.
+// 2 or 4 quads in registers) and a grid that fits the device's co-resident
+// capacity, or sets *variant = -1 when the shard is too large.
 hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
 hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);

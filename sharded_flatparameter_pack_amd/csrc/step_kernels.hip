@@ -1,15 +1,23 @@
 // step_kernels.hip -- gfx950 kernels of the per-step path: reduce, AdamW with
 // the bf16 cast, unshard, and the shard step (one-pass or two-phase).
 //
-// Each lane moves one 8-element chunk: one 16-byte word per bf16 stream and
-// two per fp32 stream, so every HBM access is a 128-bit (dwordx4) load or
-// store, carries the non-temporal hint (each stream is touched once per
-// step), and a wave touches 1 KiB (bf16) or 2 KiB (fp32) of contiguous
-// memory per access.  Workgroups own dispatch-ordered tiles of 256 chunks.
-// Elements past the last whole chunk are handled one by one by workgroup 0.
-// Every kernel comes in an aligned form (all bf16 streams 16-byte aligned at
-// the words it touches: plain loads, which the compiler keeps in flight
-// together) and a general form (branch-free realignment from a base whose
+// Element streams are processed in quads of 4 elements: one 16-byte access
+// of an fp32 stream, one 8-byte access of a bf16 stream.  Lane t of a
+// workgroup holds quads base + u * 256 + t (u < kU), so every load or store
+// instruction of a wave covers one contiguous span (1 KiB of fp32, 512 bytes
+// of bf16) and writes every byte of each cache line it touches.  That is
+// what makes the stores fast: with each lane owning a 32-byte fp32 chunk
+// written in two 16-byte halves, every instruction left its 128-byte lines
+// half written, and with the non-temporal hint the halves reached HBM
+// separately (measured on MI355X: 2.1 TB/s for pure fp32 stores, against
+// 5.7 TB/s in the quad layout).  Every access carries the non-temporal hint
+// (each stream is touched once per step).  Workgroups own dispatch-ordered
+// tiles of 256 * kU quads.  Lanes past the last quad load the last quad
+// again and store nothing, so the loads of every lane are unconditional and
+// all in flight together; the at most 3 elements past the last quad are
+// handled one by one by workgroup 0.  Every kernel comes in an aligned form
+// (bf16 quad streams 8-byte aligned, copy sources 16-byte aligned: plain
+// loads) and a general form (branch-free realignment from a base whose
 // shift is uniform across the wave).  Nothing here is a contraction, so
 // there is no MFMA; the kernels are bound by HBM.
 //
@@ -39,60 +47,113 @@ __device__ unsigned long long fp_phase_trace[1 << 16][6];
 
 // ---------------------------------------------------------------- streams
 
-__device__ __forceinline__ void load_f32x8(const float* p, float f[8]) {
-    const uint4 u = ld16(p);
-    const uint4 v = ld16(p + 4);
-    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
-    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
-    f[4] = __uint_as_float(v.x); f[5] = __uint_as_float(v.y);
-    f[6] = __uint_as_float(v.z); f[7] = __uint_as_float(v.w);
+// The lane's kU quads in tile `tile` of a stream of nq > 0 quads: quads
+// start + off[u], off[u] = u * 256 + t.  ok[u] tells whether quad u exists;
+// a missing one is replaced by the last quad, which the caller loads but
+// does not store.  Addresses are formed as a workgroup-uniform tile base
+// plus a 32-bit lane offset, so each access needs one offset register per
+// quad, shared by all streams, instead of a 64-bit address per stream.
+template <int kU>
+struct Quads {
+    int64_t start;
+    uint32_t off[kU];
+    bool ok[kU];
+};
+
+template <int kU>
+__device__ __forceinline__ Quads<kU> lane_quads(int64_t tile, int64_t nq) {
+    Quads<kU> Q;
+    Q.start = tile * (kThreads * kU);
+    const int64_t last = nq - 1 - Q.start;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const uint32_t x = (uint32_t)(u * kThreads) + threadIdx.x;
+        Q.ok[u] = (int64_t)x <= last;
+        Q.off[u] = Q.ok[u] ? x : (uint32_t)last;
+    }
+    return Q;
 }
 
-__device__ __forceinline__ void store_f32x8(float* p, const float f[8]) {
-    st16(p, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                       __float_as_uint(f[3])));
-    st16(p + 4, make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
-                           __float_as_uint(f[7])));
+// Byte offsets are formed in 32 bits (a tile spans far less than 4 GiB), so
+// that the compiler can use the scalar-base + 32-bit-offset address form.
+__device__ __forceinline__ const char* at(const void* tile_base, uint32_t byte_off) {
+    return static_cast<const char*>(tile_base) + byte_off;
+}
+__device__ __forceinline__ char* at(void* tile_base, uint32_t byte_off) {
+    return static_cast<char*>(tile_base) + byte_off;
 }
 
-// Word `word` of a bf16 stream starting at `base`.
+template <int kU>
+__device__ __forceinline__ void ld_f32q(const float* p, const Quads<kU>& Q, int u, float f[4]) {
+    const float* tb = p + (Q.start << 2);
+    const uint4 v = ld16(at(tb, Q.off[u] * 16u));
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+
+template <int kU>
+__device__ __forceinline__ void st_f32q(float* p, const Quads<kU>& Q, int u, const float f[4]) {
+    float* tb = p + (Q.start << 2);
+    st16(at(tb, Q.off[u] * 16u), make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                        __float_as_uint(f[2]), __float_as_uint(f[3])));
+}
+
+// Quad u of a bf16 stream starting at `base`.
+template <bool kAligned, int kU>
+__device__ __forceinline__ uint2 ld_bf16q(const uint16_t* base, const Quads<kU>& Q, int u) {
+    const uint16_t* tb = base + (Q.start << 2);
+    if (kAligned) return ld8(at(tb, Q.off[u] * 8u));
+    const Src8 s = src8(tb);
+    const uint2 a = ld8(at(s.abase, Q.off[u] * 8u));
+    const uint2 b = ld8(at(s.abase + s.step, Q.off[u] * 8u));
+    return realign8(s, a, b);
+}
+
+template <bool kAligned, int kU>
+__device__ __forceinline__ void st_bf16q(uint16_t* base, const Quads<kU>& Q, int u, const uint2 v) {
+    uint16_t* tb = base + (Q.start << 2);
+    if (kAligned) st8(at(tb, Q.off[u] * 8u), v);
+    else store8_any(at(tb, Q.off[u] * 8u), v);
+}
+
+// 16-byte word `word` of a bf16 stream (the copies move whole words).
 template <bool kAligned>
 __device__ __forceinline__ uint4 ld_bf16_word(const uint16_t* base, int64_t word) {
     if (kAligned) return ld16(base + (word << 3));
     return ld16_realign(src16(base), word);
 }
 
-template <bool kAligned>
-__device__ __forceinline__ void st_bf16_word(uint16_t* base, int64_t word, const uint4 v) {
-    if (kAligned) st16(base + (word << 3), v);
-    else store16_any(base + (word << 3), v);
-}
-
 // ---------------------------------------------------------------- reduce
-// Ascending-rank fp32 sum of the ranks' bf16 gradients at chunk c.  The
-// loads of up to 8 ranks are issued before any add, so each lane has up to
-// 128 bytes in flight.  "Infra: Data Parallel", ZeRO-1/ZeRO-2 paragraphs
-// (reduce-scatter with averaging); "4.1 数据并行详解" section 2 (average of
-// the local gradients).
-template <bool kAligned, class A>
-__device__ __forceinline__ void sum_ranks8(const A& a, int64_t c, float s[8]) {
+// Ascending-rank fp32 sum of the ranks' bf16 gradients at the lane's kU
+// quads.  The loads of up to 8 ranks are issued before any add.  "Infra:
+// Data Parallel", ZeRO-1/ZeRO-2 paragraphs (reduce-scatter with averaging);
+// "4.1 数据并行详解" section 2 (average of the local gradients).
+template <bool kAligned, int kU, class A>
+__device__ __forceinline__ void sum_ranks(const A& a, const Quads<kU>& Q, float s[kU][4]) {
     const int world = a.world;
     for (int q0 = 0; q0 < world; q0 += 8) {
-        uint4 w[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (q0 + k < world) w[k] = ld_bf16_word<kAligned>(a.grads[q0 + k], c);
+        uint2 w[8][kU];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             if (q0 + k < world) {
-                float f[8];
-                bf16x8_to_f32(w[k], f);
-                if (q0 + k == 0) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) s[e] = f[e];
-                } else {
+                for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(a.grads[q0 + k], Q, u);
+            }
+        }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) s[e] = s[e] + f[e];
+        for (int k = 0; k < 8; ++k) {
+            if (q0 + k < world) {
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    float f[4];
+                    bf16x4_to_f32(w[k][u], f);
+                    if (q0 + k == 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) s[u][e] = f[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) s[u][e] = s[u][e] + f[e];
+                    }
                 }
             }
         }
@@ -106,17 +167,31 @@ __device__ __forceinline__ float sum_ranks1(const A& a, int64_t j) {
     return s;
 }
 
-// y = scale * (sum over ranks), then y = acc + y when accumulating.
-template <bool kAligned, class A>
-__device__ __forceinline__ void reduce_chunk(const A& a, int64_t c, bool accumulate, float y[8]) {
-    sum_ranks8<kAligned>(a, c, y);
+// y = scale * (sum over ranks), then y = acc + y when accumulating.  With
+// kAccFirst the accumulator is loaded before the gradients, so that its
+// load is in flight with theirs (at the cost of holding it across the sum);
+// without it, after the sum.
+template <bool kAligned, bool kAccFirst, int kU, class A>
+__device__ __forceinline__ void reduce_quads(const A& a, const Quads<kU>& Q, bool accumulate,
+                                             float y[kU][4]) {
+    float p[kU][4];
+    if (kAccFirst && accumulate) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = y[e] * a.scale;
+        for (int u = 0; u < kU; ++u) ld_f32q(a.acc, Q, u, p[u]);
+    }
+    sum_ranks<kAligned, kU>(a, Q, y);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[u][e] = y[u][e] * a.scale;
+    }
     if (accumulate) {
-        float p[8];
-        load_f32x8(a.acc + (c << 3), p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = p[e] + y[e];
+        for (int u = 0; u < kU; ++u) {
+            if (!kAccFirst) ld_f32q(a.acc, Q, u, p[u]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[u][e] = p[u][e] + y[u][e];
+        }
     }
 }
 
@@ -127,20 +202,24 @@ __device__ __forceinline__ float reduce_elem(const A& a, int64_t j, bool accumul
     return y;
 }
 
-__device__ __forceinline__ void check_chunk(const float y[8], bool& bad, double& sq, bool want_sq) {
+__device__ __forceinline__ void check_quad(const float y[4], bool& bad, double& sq, bool want_sq) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
         bad |= !finite_f32(y[e]);
         if (want_sq) sq += (double)y[e] * (double)y[e];
     }
 }
 
 // ---------------------------------------------------------------- AdamW
-// One element of decoupled-weight-decay AdamW with bias correction,
-// evaluated in fp64 in the order of its definition; master, exp_avg and
-// exp_avg_sq are each rounded once to fp32.  "Infra: Data Parallel", ZeRO-1
-// paragraph (elementwise update of the rank's slice) and ZeRO figure legend
-// (fp32 master and moments, k = 12).
+// One element of decoupled-weight-decay AdamW with bias correction, in fp64
+// from the fp32 state; master, exp_avg and exp_avg_sq are each rounded once
+// to fp32.  The bias corrections are folded into two host-side coefficients,
+//   theta - lr * (m / b1) / (sqrt(v / b2) + eps)
+//     = theta - (lr / b1) * m / (sqrt(v) * (1 / sqrt(b2)) + eps),
+// which leaves one fp64 division per element; in fp64 the two forms differ
+// by a few units of 2^-53, far below the fp32 rounding that follows.
+// "Infra: Data Parallel", ZeRO-1 paragraph (elementwise update of the
+// rank's slice) and ZeRO figure legend (fp32 master and moments, k = 12).
 __device__ __forceinline__ void adamw_elem(const AdamCoef& c, float g, float& th, float& m,
                                            float& v) {
     const double gd = (double)g;
@@ -150,32 +229,55 @@ __device__ __forceinline__ void adamw_elem(const AdamCoef& c, float g, float& th
     theta = theta * c.decay;
     md = c.beta1 * md + c.one_m_beta1 * gd;
     vd = c.beta2 * vd + c.one_m_beta2 * gd * gd;
-    const double m_hat = md / c.bias1;
-    const double v_hat = vd / c.bias2;
-    theta = theta - c.lr * m_hat / (sqrt(v_hat) + c.eps);
+    const double denom = sqrt(vd) * c.inv_sqrt_bias2 + c.eps;
+    theta = theta - c.step_size * md / denom;
     th = (float)theta;
     m = (float)md;
     v = (float)vd;
 }
 
-// AdamW on chunk c with gradient y, then the bf16 cast to word c of out.
-template <bool kAligned, class A>
-__device__ __forceinline__ void update_chunk(const A& a, int64_t c, const float y[8], bool skip,
-                                             uint16_t* out) {
-    const int64_t j0 = c << 3;
-    float th[8];
-    load_f32x8(a.master + j0, th);
-    if (!skip) {
-        float m[8], v[8];
-        load_f32x8(a.exp_avg + j0, m);
-        load_f32x8(a.exp_avg_sq + j0, v);
+// The fp32 master and moments of a lane's kU quads.  Callers issue these
+// loads before anything they wait on (gradient quads, the overflow flag), so
+// that a wave pays one memory round trip, not two.
+template <int kU>
+struct State {
+    float th[kU][4], m[kU][4], v[kU][4];
+};
+
+template <int kU, class A>
+__device__ __forceinline__ void load_state(const A& a, const Quads<kU>& Q, State<kU>& st) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) adamw_elem(a.c, y[e], th[e], m[e], v[e]);
-        store_f32x8(a.master + j0, th);
-        store_f32x8(a.exp_avg + j0, m);
-        store_f32x8(a.exp_avg_sq + j0, v);
+    for (int u = 0; u < kU; ++u) {
+        ld_f32q(a.master, Q, u, st.th[u]);
+        ld_f32q(a.exp_avg, Q, u, st.m[u]);
+        ld_f32q(a.exp_avg_sq, Q, u, st.v[u]);
     }
-    if (out != nullptr) st_bf16_word<kAligned>(out, c, f32x8_to_bf16(th));
+}
+
+template <int kU>
+__device__ __forceinline__ void adamw_quads(const AdamCoef& c, const float y[kU][4], State<kU>& st) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) adamw_elem(c, y[u][e], st.th[u][e], st.m[u][e], st.v[u][e]);
+    }
+}
+
+// Stores of the lane's existing quads: the state (unless skip) and the bf16
+// cast of the master to `out` (if not null).
+template <bool kAligned, int kU, class A>
+__device__ __forceinline__ void store_quads(const A& a, const Quads<kU>& Q, bool skip,
+                                            const State<kU>& st, uint16_t* out) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        if (!Q.ok[u]) continue;
+        if (!skip) {
+            st_f32q(a.master, Q, u, st.th[u]);
+            st_f32q(a.exp_avg, Q, u, st.m[u]);
+            st_f32q(a.exp_avg_sq, Q, u, st.v[u]);
+        }
+        if (out != nullptr) st_bf16q<kAligned>(out, Q, u, f32x4_to_bf16(st.th[u]));
+    }
 }
 
 template <class A>
@@ -195,11 +297,31 @@ __device__ __forceinline__ void update_elem(const A& a, int64_t j, float y, bool
 // Shard q's whole words of `full` are copied with one aligned store each
 // (the source realigned when needed); its at most 14 edge elements, which
 // share a word with a neighbouring shard, are copied one by one.
-template <bool kAligned>
-__device__ __forceinline__ void copy_word(const uint16_t* src, uint16_t* full, const ShardSpan& sp,
-                                          int64_t w) {
-    if (w < ((sp.b - sp.a) >> 3))
-        st16(full + sp.a + (w << 3), ld_bf16_word<kAligned>(src + (sp.a - sp.lo), w));
+// Copy tile `tile` of shard q's whole words: lane t moves words
+// tile * 256 * kWords + u * 256 + t, u < kWords.  A full tile (the common
+// case, decided per workgroup) loads without bounds checks so that all its
+// loads are in flight together.
+template <bool kAligned, int kWords>
+__device__ __forceinline__ void copy_tile(const uint16_t* src, uint16_t* full, const ShardSpan& sp,
+                                          int64_t tile) {
+    constexpr int64_t kTile = (int64_t)kThreads * kWords;
+    const int64_t n_words = (sp.b - sp.a) >> 3;
+    const uint16_t* from = src + (sp.a - sp.lo);
+    uint16_t* to = full + sp.a;
+    const int64_t w0 = tile * kTile + threadIdx.x;
+    if ((tile + 1) * kTile <= n_words) {
+        uint4 v[kWords];
+#pragma unroll
+        for (int u = 0; u < kWords; ++u) v[u] = ld_bf16_word<kAligned>(from, w0 + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < kWords; ++u) st16(to + ((w0 + u * kThreads) << 3), v[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kWords; ++u) {
+            const int64_t w = w0 + u * kThreads;
+            if (w < n_words) st16(to + (w << 3), ld_bf16_word<kAligned>(from, w));
+        }
+    }
 }
 
 __device__ __forceinline__ void unshard_edges(const uint16_t* src, uint16_t* full, int64_t S, int q,
@@ -296,23 +418,24 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* p
 
 // ---------------------------------------------------------------- kernels
 
-__device__ __forceinline__ int64_t lane_chunk() {
-    return (int64_t)blockIdx.x * kTileChunks + threadIdx.x;
-}
-
 template <bool kAligned, bool kAccumulate, bool kNorm>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceArgs a) {
-    const int64_t n_chunks = a.shard >> 3;
+    constexpr int kU = kQuadsPerLane;
+    const int64_t nq = a.shard >> 2;
     bool bad = false;
     double sq = 0.0;
-    const int64_t c = lane_chunk();
-    if (c < n_chunks) {
-        float y[8];
-        reduce_chunk<kAligned>(a, c, kAccumulate, y);
-        store_f32x8(a.acc + (c << 3), y);
-        check_chunk(y, bad, sq, kNorm);
+    if (nq > 0) {
+        const Quads<kU> Q = lane_quads<kU>(blockIdx.x, nq);
+        float y[kU][4];
+        reduce_quads<kAligned, true, kU>(a, Q, kAccumulate, y);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (!Q.ok[u]) continue;
+            st_f32q(a.acc, Q, u, y[u]);
+            check_quad(y[u], bad, sq, kNorm);
+        }
     }
-    const int64_t tail0 = n_chunks << 3;
+    const int64_t tail0 = nq << 2;
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
         const int64_t j = tail0 + threadIdx.x;
         const float y = reduce_elem(a, j, kAccumulate);
@@ -327,20 +450,29 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceArgs a) {
     }
 }
 
+// The gradient and state loads do not wait for the overflow flag: they are
+// issued first and the flag is read beside them (a skipped step, which is
+// rare, loads 12 bytes per element it does not need).
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
+    constexpr int kU = kQuadsPerLane;
     if (a.sq_norm != nullptr && blockIdx.x == 0) finalize_norm(a.partials, a.n_partials, a.sq_norm);
-    const bool skip = a.found_inf != nullptr && *a.found_inf != 0;
-    const int64_t n_chunks = a.shard >> 3;
-    const int64_t c = lane_chunk();
-    if (c < n_chunks) {
-        float g[8];
-        if (!skip) load_f32x8(a.grad + (c << 3), g);
-        update_chunk<kAligned>(a, c, g, skip, a.param_bf16);
+    const int64_t nq = a.shard >> 2;
+    if (nq > 0) {
+        const Quads<kU> Q = lane_quads<kU>(blockIdx.x, nq);
+        float g[kU][4];
+        State<kU> st;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) ld_f32q(a.grad, Q, u, g[u]);
+        load_state<kU>(a, Q, st);
+        const bool skip = a.found_inf != nullptr && *a.found_inf != 0;
+        if (!skip) adamw_quads<kU>(a.c, g, st);
+        store_quads<kAligned, kU>(a, Q, skip, st, a.param_bf16);
     }
-    const int64_t tail0 = n_chunks << 3;
+    const int64_t tail0 = nq << 2;
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
         const int64_t j = tail0 + threadIdx.x;
+        const bool skip = a.found_inf != nullptr && *a.found_inf != 0;
         update_elem(a, j, skip ? 0.0f : a.grad[j], skip, a.param_bf16);
     }
 }
@@ -351,20 +483,20 @@ __global__ __launch_bounds__(kThreads) void unshard_kernel(const UnshardArgs a) 
     const uint16_t* src = a.shards[q];
     if (src == nullptr) return;
     const ShardSpan sp = shard_span(a.full, a.shard, q);
-    copy_word<kAligned>(src, a.full, sp, lane_chunk());
+    copy_tile<kAligned, kCopyWordsStream>(src, a.full, sp, blockIdx.x);
     if (blockIdx.x == 0) unshard_edges(src, a.full, a.shard, q, threadIdx.x, kThreads);
 }
 
 // Copy role of the step kernels: workgroup idx takes tile idx % copy_tiles
 // of the idx / copy_tiles-th shard other than the own one.
-template <bool kAligned>
+template <bool kAligned, int kWords>
 __device__ __forceinline__ void copy_role(const StepArgs& a, unsigned idx) {
     const unsigned qi = idx / (unsigned)a.copy_tiles;
     const unsigned tile = idx - qi * (unsigned)a.copy_tiles;
     const int q = (int)qi < a.rank ? (int)qi : (int)qi + 1;
     const uint16_t* src = a.shards[q];
     const ShardSpan sp = shard_span(a.full, a.shard, q);
-    copy_word<kAligned>(src, a.full, sp, (int64_t)tile * kTileChunks + threadIdx.x);
+    copy_tile<kAligned, kWords>(src, a.full, sp, tile);
     if (tile == 0) unshard_edges(src, a.full, a.shard, q, threadIdx.x, kThreads);
 }
 
@@ -376,24 +508,34 @@ __device__ __forceinline__ void copy_role(const StepArgs& a, unsigned idx) {
 template <bool kAligned, bool kFused>
 __global__ __launch_bounds__(kThreads) void step_phase1_kernel(const StepArgs a) {
     if (blockIdx.x >= (unsigned)a.reduce_groups) {
-        copy_role<kAligned>(a, blockIdx.x - (unsigned)a.reduce_groups);
+        copy_role<kAligned, kCopyWordsStream>(a, blockIdx.x - (unsigned)a.reduce_groups);
         return;
     }
-    const int64_t n_chunks = a.shard >> 3;
+    constexpr int kU = kQuadsPerLane;
+    const int64_t nq = a.shard >> 2;
     uint16_t* own = a.full + (int64_t)a.rank * a.shard;
     const bool want_sq = a.partials != nullptr;
     const bool acc_in = a.accumulate != 0;
     bool bad = false;
     double sq = 0.0;
-    const int64_t c = lane_chunk();
-    if (c < n_chunks) {
-        float y[8];
-        reduce_chunk<kAligned>(a, c, acc_in, y);
-        check_chunk(y, bad, sq, want_sq);
-        if (!kFused || a.keep_grad) store_f32x8(a.acc + (c << 3), y);
-        if (kFused) update_chunk<kAligned>(a, c, y, false, own);
+    if (nq > 0) {
+        const Quads<kU> Q = lane_quads<kU>(blockIdx.x, nq);
+        State<kU> st;
+        if (kFused) load_state<kU>(a, Q, st);
+        float y[kU][4];
+        reduce_quads<kAligned, true, kU>(a, Q, acc_in, y);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (!Q.ok[u]) continue;
+            check_quad(y[u], bad, sq, want_sq);
+            if (!kFused || a.keep_grad) st_f32q(a.acc, Q, u, y[u]);
+        }
+        if (kFused) {
+            adamw_quads<kU>(a.c, y, st);
+            store_quads<kAligned, kU>(a, Q, false, st, own);
+        }
     }
-    const int64_t tail0 = n_chunks << 3;
+    const int64_t tail0 = nq << 2;
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
         const int64_t j = tail0 + threadIdx.x;
         const float y = reduce_elem(a, j, acc_in);
@@ -411,30 +553,29 @@ __global__ __launch_bounds__(kThreads) void step_phase1_kernel(const StepArgs a)
 
 // One-pass exact-skip step.  Workgroups [0, reduce_groups) take part in a
 // grid barrier and must be resident together (the grid is sized for it);
-// each of their lanes loads, for its kC chunks, the ranks' gradient words
-// and the fp32 master / moments (none of which depends on the overflow
-// flag), reduces, and computes the AdamW update into registers.  The
-// workgroup ORs its overflow bit (and the flag left by earlier
-// micro-batches) into the barrier and waits; the barrier returns the grid's
-// flag, after which the lanes only store: the new state and its bf16 cast,
-// or on overflow just the cast of the old master.  Workgroups past
-// reduce_groups copy the other ranks' shards meanwhile and take no part in
-// the barrier.  The reduced gradient never leaves the registers, so the
-// step moves exactly the algorithmic bytes.
-template <bool kAligned, int kC>
+// each of their lanes loads, for its kQ quads, the fp32 master / moments and
+// the ranks' gradient quads (none of which depends on the overflow flag),
+// reduces, and computes the AdamW update into registers.  The workgroup ORs
+// its overflow bit (and the flag left by earlier micro-batches) into the
+// barrier and waits; the barrier returns the grid's flag, after which the
+// lanes only store: the new state and its bf16 cast, or on overflow just the
+// cast of the old master.  Workgroups past reduce_groups copy the other
+// ranks' shards meanwhile and take no part in the barrier.  The reduced
+// gradient never leaves the registers, so the step moves exactly the
+// algorithmic bytes.
+template <bool kAligned, int kQ>
 __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     FP_PHASE_MARK(0);
     if (blockIdx.x >= (unsigned)a.reduce_groups) {
-        copy_role<kAligned>(a, blockIdx.x - (unsigned)a.reduce_groups);
+        copy_role<kAligned, kCopyWordsCoop>(a, blockIdx.x - (unsigned)a.reduce_groups);
         FP_PHASE_MARK(5);
         return;
     }
     __shared__ unsigned s_skip;
-    const int64_t n_chunks = a.shard >> 3;
+    const int64_t nq = a.shard >> 2;
     const bool want_sq = a.partials != nullptr;
     const bool acc_in = a.accumulate != 0;
     uint16_t* own = a.full + (int64_t)a.rank * a.shard;
-    const int64_t base = (int64_t)blockIdx.x * kThreads * kC + threadIdx.x;
     BarrierTicket ticket = {0u, 0u};
     unsigned prior = 0u;
     if (threadIdx.x == 0) {
@@ -443,28 +584,25 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     }
 
     // reduce and speculative update, all in registers
-    float th[kC][8], m[kC][8], v[kC][8];
-    uint4 old_bf16[kC];
+    const Quads<kQ> Q = lane_quads<kQ>(blockIdx.x, nq > 0 ? nq : 1);
+    State<kQ> st;
+    uint2 old_bf16[kQ];
     bool bad = false;
     double sq = 0.0;
+    if (nq > 0) {
+        load_state<kQ>(a, Q, st);
+        float y[kQ][4];
+        reduce_quads<kAligned, false, kQ>(a, Q, acc_in, y);
 #pragma unroll
-    for (int u = 0; u < kC; ++u) {
-        const int64_t c = base + (int64_t)u * kThreads;
-        if (c < n_chunks) {
-            const int64_t j0 = c << 3;
-            load_f32x8(a.master + j0, th[u]);
-            load_f32x8(a.exp_avg + j0, m[u]);
-            load_f32x8(a.exp_avg_sq + j0, v[u]);
-            float y[8];
-            reduce_chunk<kAligned>(a, c, acc_in, y);
-            check_chunk(y, bad, sq, want_sq);
-            if (a.keep_grad) store_f32x8(a.acc + j0, y);
-            old_bf16[u] = f32x8_to_bf16(th[u]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) adamw_elem(a.c, y[e], th[u][e], m[u][e], v[u][e]);
+        for (int u = 0; u < kQ; ++u) {
+            old_bf16[u] = f32x4_to_bf16(st.th[u]);
+            if (!Q.ok[u]) continue;
+            check_quad(y[u], bad, sq, want_sq);
+            if (a.keep_grad) st_f32q(a.acc, Q, u, y[u]);
         }
+        adamw_quads<kQ>(a.c, y, st);
     }
-    const int64_t tail0 = n_chunks << 3;
+    const int64_t tail0 = nq << 2;
     const bool has_tail = blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0;
     float tt = 0.0f, tm = 0.0f, tv = 0.0f, told = 0.0f;
     if (has_tail) {
@@ -496,18 +634,17 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.found_inf = skip ? 1 : 0;
 
     // commit: stores only
+    if (nq > 0) {
 #pragma unroll
-    for (int u = 0; u < kC; ++u) {
-        const int64_t c = base + (int64_t)u * kThreads;
-        if (c < n_chunks) {
-            const int64_t j0 = c << 3;
+        for (int u = 0; u < kQ; ++u) {
+            if (!Q.ok[u]) continue;
             if (skip) {
-                st_bf16_word<kAligned>(own, c, old_bf16[u]);
+                st_bf16q<kAligned>(own, Q, u, old_bf16[u]);
             } else {
-                store_f32x8(a.master + j0, th[u]);
-                store_f32x8(a.exp_avg + j0, m[u]);
-                store_f32x8(a.exp_avg_sq + j0, v[u]);
-                st_bf16_word<kAligned>(own, c, f32x8_to_bf16(th[u]));
+                st_f32q(a.master, Q, u, st.th[u]);
+                st_f32q(a.exp_avg, Q, u, st.m[u]);
+                st_f32q(a.exp_avg_sq, Q, u, st.v[u]);
+                st_bf16q<kAligned>(own, Q, u, f32x4_to_bf16(st.th[u]));
             }
         }
     }
@@ -579,7 +716,7 @@ namespace {
 // first use and kept for the life of the process.  The smaller of the
 // aligned and general forms' figures bounds both.
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2;  // lanes keep 1 or kMaxCoopChunks chunks
+constexpr int kVariants = 2;  // lanes keep 2 or kMaxCoopQuads quads
 struct CoopLimits {
     std::atomic<int> state{0};  // 0 unknown, 1 computing, 2 ready
     int cus = 0;
@@ -589,10 +726,10 @@ CoopLimits g_limits[kMaxDevices];
 
 const void* coop_fn(int variant, bool aligned) {
     if (aligned)
-        return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<true, 1>)
-                            : reinterpret_cast<const void*>(&step_coop_kernel<true, kMaxCoopChunks>);
-    return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<false, 1>)
-                        : reinterpret_cast<const void*>(&step_coop_kernel<false, kMaxCoopChunks>);
+        return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<true, 2>)
+                            : reinterpret_cast<const void*>(&step_coop_kernel<true, kMaxCoopQuads>);
+    return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<false, 2>)
+                        : reinterpret_cast<const void*>(&step_coop_kernel<false, kMaxCoopQuads>);
 }
 
 hipError_t coop_limits(int dev, const CoopLimits** out) {
@@ -627,10 +764,10 @@ hipError_t plan_step_coop(int64_t shard, int* variant, int* grid) {
     const CoopLimits* L = nullptr;
     if ((e = coop_limits(dev, &L)) != hipSuccess) return e;
     *variant = -1;
-    const int64_t n_chunks = shard >> 3;
-    const int chunks[kVariants] = {1, kMaxCoopChunks};
+    const int64_t nq = shard >> 2;
+    const int quads[kVariants] = {2, kMaxCoopQuads};
     for (int i = 0; i < kVariants; ++i) {
-        const int64_t g = n_chunks > 0 ? ceil_div64(n_chunks, (int64_t)kThreads * chunks[i]) : 1;
+        const int64_t g = nq > 0 ? ceil_div64(nq, (int64_t)kThreads * quads[i]) : 1;
         if (g <= (int64_t)L->per_cu[i] * L->cus) {
             *variant = i;
             *grid = (int)g;
@@ -648,14 +785,14 @@ hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool align
     // together, and otherwise they become so as the copy workgroups finish.
     StepArgs b = a;
     b.reduce_groups = grid;
-    b.copy_tiles = (int32_t)copy_tiles_per_shard(a.shard);
+    b.copy_tiles = (int32_t)copy_tiles_per_shard(a.shard, kCopyWordsCoop);
     const dim3 g((unsigned)((int64_t)grid + (int64_t)(a.world - 1) * b.copy_tiles));
     if (aligned) {
-        if (variant == 0) step_coop_kernel<true, 1><<<g, kThreads, 0, s>>>(b);
-        else step_coop_kernel<true, kMaxCoopChunks><<<g, kThreads, 0, s>>>(b);
+        if (variant == 0) step_coop_kernel<true, 2><<<g, kThreads, 0, s>>>(b);
+        else step_coop_kernel<true, kMaxCoopQuads><<<g, kThreads, 0, s>>>(b);
     } else {
-        if (variant == 0) step_coop_kernel<false, 1><<<g, kThreads, 0, s>>>(b);
-        else step_coop_kernel<false, kMaxCoopChunks><<<g, kThreads, 0, s>>>(b);
+        if (variant == 0) step_coop_kernel<false, 2><<<g, kThreads, 0, s>>>(b);
+        else step_coop_kernel<false, kMaxCoopQuads><<<g, kThreads, 0, s>>>(b);
     }
     return hipGetLastError();
 }

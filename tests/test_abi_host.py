@@ -185,3 +185,32 @@ def test_device_entry_points_reject_bad_arguments(fp):
     assert L.fp_workspace_bytes(1 << 30) == 16384 + 8 * ((1 << 30) // 8 // 256 + 1)
     assert _status(L.fp_shard_step, None, None) == -1
     assert L.fp_status_string(-3) == b"misaligned pointer"
+
+
+def test_step_path_without_a_device(fp):
+    """fp_step_path validates like fp_shard_step and launches nothing; the
+    paths that need no occupancy query are decided on the host (fake,
+    never-dereferenced addresses)."""
+    from sharded_flatparameter_pack_amd import _lib
+    L = fp.lib()
+    grads = (C.c_void_p * 2)(0x1000000, 0x2000000)
+    shards = (C.c_void_p * 2)(None, 0x3000000)
+    a = _lib.fp_step_args()
+    a.shard, a.world, a.rank, a.scale = 16, 2, 0, 0.5
+    a.grads, a.shards = C.cast(grads, C.c_void_p), C.cast(shards, C.c_void_p)
+    a.acc, a.master, a.exp_avg, a.exp_avg_sq = 0x4000000, 0x5000000, 0x6000000, 0x7000000
+    a.hp = _lib.fp_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    a.full, a.found_inf = 0x8000000, 0x9000000
+    path = C.c_int32(-1)
+    a.flags = _lib.FP_STEP_NO_SKIP
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
+    assert path.value == _lib.FP_PATH_NO_SKIP
+    a.flags = _lib.FP_STEP_EXACT_SKIP          # no workspace: no grid barrier
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
+    assert path.value == _lib.FP_PATH_TWO_PHASE
+    a.workspace, a.flags = 0xA000000, _lib.FP_STEP_NO_COOP
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
+    assert path.value == _lib.FP_PATH_TWO_PHASE
+    a.master = 0x4000010                       # overlaps acc
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -1
+    assert _status(L.fp_step_path, C.byref(a), None) == -1

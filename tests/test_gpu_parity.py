@@ -286,9 +286,17 @@ def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_o
     full = torch.zeros(world * S, dtype=torch.int16, device=dev())
     shards = [to_dev(o) for o in others]
     shards[rank] = None
-    fp.shard_step(_grads_with_offset(micro[-1], grad_off), acc, d_th, d_m, d_v, shards, full, rank,
-                  scale=float(scale), accumulate=n_micro > 1, step=step, found_inf=flag, sq_norm=sq,
-                  workspace=ws, flags=flags, **hp_kwargs(hp))
+    call = fp.ShardStep(_grads_with_offset(micro[-1], grad_off), acc, d_th, d_m, d_v, shards, full,
+                        rank, scale=float(scale), accumulate=n_micro > 1, found_inf=flag, sq_norm=sq,
+                        workspace=ws, flags=flags, **hp_kwargs(hp))
+    path = call.path()
+    if flags & fp.FP_STEP_NO_SKIP:
+        assert path == fp.FP_PATH_NO_SKIP
+    elif not workspace or flags & fp.FP_STEP_NO_COOP:
+        assert path == fp.FP_PATH_TWO_PHASE
+    elif S <= 2_000_000:                  # far inside MI355X's co-resident capacity
+        assert path == fp.FP_PATH_ONE_PASS
+    call(step)
     torch.cuda.synchronize()
     assert int(flag.item()) == flag_o
     gh = [to_host(x) for x in (d_th, d_m, d_v)]
@@ -383,6 +391,15 @@ def test_adamw_shardwise_equals_whole_buffer(fp):
     torch.cuda.synchronize()
     for a, b in zip(whole, parts):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("S", [2_000_003, 2_900_001, 3_500_002])
+def test_step_near_the_one_pass_capacity(fp, S):
+    """Shards around the one-pass kernel's co-resident capacity: lanes that
+    keep 2 quads, lanes that keep 4, and the two-kernel fallback."""
+    say(f"step near one-pass capacity S={S}")
+    _step_case(fp, world=2, S=S, rank=1, n_micro=1, step=2, seed=11, flags=0)
+    _step_case(fp, world=2, S=S, rank=0, n_micro=2, step=1, seed=12, flags=0, inf=True)
 
 
 def test_step_is_bitwise_reproducible(fp):
