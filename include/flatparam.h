@@ -298,6 +298,75 @@ fp_status fp_shard_step(const fp_step_args* args, void* stream);
 #define FP_PATH_NO_SKIP 2
 fp_status fp_step_path(const fp_step_args* args, int32_t* path);
 
+/* ------------------------------------------------------------------ units */
+
+/* Many units (for example the ~25 MB DDP buckets of a model, or a model's
+ * FSDP units) stepped together, one launch per stage for all of them.  A
+ * rank's optimizer state is one fp32 partition holding every unit's shard:
+ * [DP] ZeRO-1 / ZeRO-2 (each rank keeps one slice of the whole state);
+ * [GUIDE] section 4.2 (gradients are reduced bucket by bucket).
+ *
+ * fp_units_create: n_units >= 1 units of one rank `rank` in a group of
+ * `world`.  shard: host array of n_units shard sizes S_u >= 0.
+ * grads: host array of n_units * world device pointers; entry u * world + q
+ *   is rank q's bf16 gradient over this rank's shard of unit u (bf16[S_u]).
+ * shards, full: both NULL (a plan that only reduces) or: shards a host array
+ *   of n_units * world device pointers, entry u * world + q rank q's bf16
+ *   shard of unit u (entry rank ignored); full a host array of n_units
+ *   device pointers, unit u's gathered bf16[world * S_u].
+ * The pointers are fixed for the plan's life (create one plan per set of
+ * gradient buffers).  Unit u's fp32 shard sits in the partition at element
+ * offset_u = sum over v < u of S_v rounded up to a multiple of 4
+ * (fp_units_offsets); the partition has fp_units_info's `partition`
+ * elements.  Creation allocates and fills a small device table on the
+ * current device with a synchronous copy (a set-up call: not for graph
+ * capture); calls must be made with that device current.
+ * Errors: FP_ERR_RANGE (n_units, world, rank, sizes), FP_ERR_INVALID (NULL
+ * pointers, a source overlapping its unit's full buffer), FP_ERR_ALIGN (bf16
+ * pointers need 2-byte alignment), FP_ERR_DEVICE (allocation / copy). */
+typedef struct fp_units fp_units;
+fp_status fp_units_create(int32_t n_units, int32_t world, int32_t rank, const int64_t* shard,
+                          const uint16_t* const* grads, const uint16_t* const* shards,
+                          uint16_t* const* full, fp_units** out);
+void fp_units_destroy(fp_units* units);
+/* partition: elements of the rank's fp32 partition; workspace_bytes: the
+ * workspace fp_units_reduce / fp_units_step need for the norm.  Either
+ * output may be NULL. */
+fp_status fp_units_info(const fp_units* units, int64_t* partition, int64_t* workspace_bytes);
+/* offsets: host array of n_units elements, receives offset_u. */
+fp_status fp_units_offsets(const fp_units* units, int64_t* offsets);
+
+/* One micro-batch's reduce over all units in one launch: fp_reduce_shard's
+ * arithmetic on every unit, into acc (device fp32[partition], 16-byte
+ * aligned; unit u at offset_u).  found_inf, sq_norm, workspace as there
+ * (workspace of fp_units_info's size). */
+fp_status fp_units_reduce(const fp_units* units, float scale, int32_t accumulate, float* acc,
+                          int32_t* found_inf, double* sq_norm, void* workspace, void* stream);
+
+/* The last micro-batch's step over all units: fp_shard_step's arithmetic on
+ * every unit, with one overflow flag for the whole step (a non-finite value
+ * in any unit skips the update of every unit).  FP_STEP_EXACT_SKIP runs two
+ * launches (reduce + copies of every unit's other shards, then AdamW and
+ * the casts into each unit's full + rank * S_u); FP_STEP_NO_SKIP one fused
+ * launch; FP_STEP_KEEP_GRAD may be or-ed in.  acc, master, exp_avg,
+ * exp_avg_sq: device fp32[partition], 16-byte aligned.  profile_events as
+ * in fp_step_args.  Requires a plan made with shards and full. */
+typedef struct fp_units_step_args {
+    float scale;
+    int32_t accumulate;
+    float* acc;
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    fp_adamw_hparams hp;
+    int32_t* found_inf;            /* device int32, required */
+    double* sq_norm;               /* device double, may be NULL */
+    void* workspace;               /* device, needed with sq_norm */
+    int32_t flags;
+    void* const* profile_events;
+} fp_units_step_args;
+fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream);
+
 /* ------------------------------------------------------------------ helpers */
 
 /* Model-state bytes per GPU.  [DP] ZeRO figure (one formula per row) and

@@ -24,7 +24,7 @@ from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_ONE_PASS,  # noqa: F40
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
-__all__ = ["Plan", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
+__all__ = ["Plan", "Units", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
            "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "library_path"]
@@ -300,6 +300,115 @@ class ShardStep:
         with torch.cuda.device(self._device):
             check(lib().fp_step_path(C.byref(self._args), C.byref(out)))
         return out.value
+
+
+# ------------------------------------------------------------------ units
+class Units:
+    """Many units (DDP buckets, FSDP units) of one rank stepped together:
+    one launch per stage for all of them (fp_units_*).
+
+    grads: per unit, the world ranks' bf16 gradients over this rank's shard
+    of that unit (a list of 1-D tensors or a [world, S_u] tensor).
+    shards / full: per unit, the ranks' bf16 shards (entry `rank` None) and
+    the gathered bf16 [world * S_u] buffer; both None for a reduce-only plan.
+    The rank's fp32 state is one partition of `partition` elements holding
+    unit u at `offsets[u]`.  The tensors must stay alive and in place for
+    the plan's life; the plan is bound to the device current at creation.
+    """
+
+    def __init__(self, grads, rank: int, shards=None, full=None):
+        torch = _torch()
+        n = len(grads)
+        if n < 1:
+            raise ValueError("need at least one unit")
+        if (shards is None) != (full is None):
+            raise ValueError("shards and full go together")
+        sizes, gtab, stab, ftab = [], [], [], []
+        world = None
+        for u in range(n):
+            g = grads[u]
+            S = g.shape[1] if hasattr(g, "dim") and g.dim() == 2 else g[0].numel()
+            p = _rank_ptrs(g, S, f"grads[{u}]")
+            world = len(p) if world is None else world
+            if len(p) != world:
+                raise ValueError(f"grads[{u}] has {len(p)} ranks, expected {world}")
+            sizes.append(S)
+            gtab += p
+            if shards is not None:
+                sp = _rank_ptrs(shards[u], S, f"shards[{u}]", allow_none=True)
+                if len(sp) != world:
+                    raise ValueError(f"shards[{u}] has {len(sp)} ranks, expected {world}")
+                stab += sp
+                ftab.append(_bf16(full[u], S * world, f"full[{u}]"))
+        self.world, self.rank, self.n_units, self.sizes = world, int(rank), n, sizes
+        self._keep = (grads, shards, full)
+        self._device = (grads[0] if hasattr(grads[0], "device") else grads[0][0]).device
+        out = C.c_void_p()
+        with torch.cuda.device(self._device):
+            check(lib().fp_units_create(
+                n, world, int(rank), (C.c_int64 * n)(*sizes), _ptr_table(gtab),
+                _ptr_table(stab) if shards is not None else None,
+                _ptr_table(ftab) if shards is not None else None, C.byref(out)))
+        self._h = out
+        part, ws = C.c_int64(), C.c_int64()
+        check(lib().fp_units_info(self._h, C.byref(part), C.byref(ws)))
+        self.partition, self.workspace_bytes = part.value, ws.value
+        offs = (C.c_int64 * n)()
+        check(lib().fp_units_offsets(self._h, offs))
+        self.offsets = list(offs)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().fp_units_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def new_workspace(self):
+        torch = _torch()
+        return torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=self._device)
+
+    def unit_slice(self, buf, u: int):
+        """Unit u's shard inside a partition-sized tensor."""
+        return buf.narrow(0, self.offsets[u], self.sizes[u])
+
+    def _opt(self, t, dtype, n, name):
+        return _dev_ptr(t, (dtype,), n, name) if t is not None else None
+
+    def reduce(self, acc, *, scale: float, accumulate: bool = False, found_inf=None, sq_norm=None,
+               workspace=None):
+        torch = _torch()
+        check(lib().fp_units_reduce(
+            self._h, float(scale), int(bool(accumulate)), C.c_void_p(_f32(acc, self.partition, "acc")),
+            self._opt(found_inf, torch.int32, 1, "found_inf"), self._opt(sq_norm, torch.float64, 1, "sq_norm"),
+            self._opt(workspace, torch.uint8, self.workspace_bytes, "workspace"), _stream(acc)))
+        return acc
+
+    def step(self, acc, master, exp_avg, exp_avg_sq, *, scale: float, lr, beta1, beta2, eps,
+             weight_decay, step: int, found_inf, accumulate: bool = False, sq_norm=None,
+             workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None):
+        torch = _torch()
+        P = self.partition
+        a = _lib.fp_units_step_args()
+        a.scale, a.accumulate = float(scale), int(bool(accumulate))
+        a.acc, a.master = _f32(acc, P, "acc"), _f32(master, P, "master")
+        a.exp_avg, a.exp_avg_sq = _f32(exp_avg, P, "exp_avg"), _f32(exp_avg_sq, P, "exp_avg_sq")
+        a.hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
+        a.found_inf = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf")
+        a.sq_norm = self._opt(sq_norm, torch.float64, 1, "sq_norm")
+        a.workspace = self._opt(workspace, torch.uint8, self.workspace_bytes, "workspace")
+        a.flags = int(flags)
+        ev = None
+        if profile_events is not None:
+            if len(profile_events) != _lib.FP_STEP_EVENTS:
+                raise ValueError(f"profile_events needs {_lib.FP_STEP_EVENTS} hipEvent_t handles")
+            ev = (C.c_void_p * _lib.FP_STEP_EVENTS)(*profile_events)
+            a.profile_events = C.cast(ev, C.c_void_p)
+        check(lib().fp_units_step(self._h, C.byref(a), _stream(master)))
 
 
 # ------------------------------------------------------------------ helpers

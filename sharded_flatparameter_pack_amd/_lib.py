@@ -50,6 +50,13 @@ class fp_step_args(C.Structure):
                 ("workspace", _vp), ("flags", _i32), ("profile_events", _vp)]
 
 
+class fp_units_step_args(C.Structure):
+    _fields_ = [("scale", _f32), ("accumulate", _i32), ("acc", _vp), ("master", _vp),
+                ("exp_avg", _vp), ("exp_avg_sq", _vp), ("hp", fp_adamw_hparams),
+                ("found_inf", _vp), ("sq_norm", _vp), ("workspace", _vp), ("flags", _i32),
+                ("profile_events", _vp)]
+
+
 # name -> (restype, argtypes); the export test compares this table with the header
 SIGNATURES = {
     "fp_plan_create": (_i32, [_i32, _vp, _vp, _i32, C.POINTER(_vp)]),
@@ -63,6 +70,12 @@ SIGNATURES = {
     "fp_unshard": (_i32, [_i64, _i32, _vp, _vp, _vp]),
     "fp_shard_step": (_i32, [C.POINTER(fp_step_args), _vp]),
     "fp_step_path": (_i32, [C.POINTER(fp_step_args), C.POINTER(C.c_int32)]),
+    "fp_units_create": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, C.POINTER(_vp)]),
+    "fp_units_destroy": (None, [_vp]),
+    "fp_units_info": (_i32, [_vp, _vp, _vp]),
+    "fp_units_offsets": (_i32, [_vp, _vp]),
+    "fp_units_reduce": (_i32, [_vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "fp_units_step": (_i32, [_vp, C.POINTER(fp_units_step_args), _vp]),
     "fp_state_bytes": (_i32, [_f64, _i32, _f64, _i32, C.POINTER(_f64)]),
     "fp_status_string": (C.c_char_p, [_i32]),
     "fp_last_error": (C.c_char_p, []),

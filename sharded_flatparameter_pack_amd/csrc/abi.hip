@@ -600,6 +600,291 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     return FP_OK;
 }
 
+// ---------------------------------------------------------------------- units
+
+struct fp_units {
+    int32_t n = 0, world = 1, rank = 0;
+    int device = -1;
+    bool has_unshard = false;
+    bool aligned = true;
+    int64_t partition = 0;
+    int64_t reduce_groups = 0, copy_groups = 0;
+    std::vector<int64_t> shard, offset;
+    std::vector<const uint16_t*> grads, shards;  // host copies, for validation
+    std::vector<uint16_t*> full;
+    void* dev = nullptr;  // UnitDesc[n] | tile_start[n+1] | copy_start[n+1] | grads[n*w] | shards[n*w]
+};
+
+namespace {
+void free_units(fp_units* u) {
+    if (u->dev != nullptr) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(u->device);
+        (void)hipFree(u->dev);
+        if (cur >= 0) (void)hipSetDevice(cur);
+    }
+    delete u;
+}
+
+const UnitDesc* units_desc(const fp_units* u) { return static_cast<const UnitDesc*>(u->dev); }
+const int64_t* units_tile_start(const fp_units* u) {
+    return reinterpret_cast<const int64_t*>(units_desc(u) + u->n);
+}
+const int64_t* units_copy_start(const fp_units* u) { return units_tile_start(u) + u->n + 1; }
+
+int64_t units_workspace_bytes(const fp_units* u) { return kWorkspaceHeader + 8 * (u->reduce_groups + 1); }
+
+fp_status check_units_state(const fp_units* u, const float* const* f32, const char* const* names, int n) {
+    const int64_t b4 = u->partition * 4;
+    for (int i = 0; i < n; ++i) {
+        fp_status st = check_f32(f32[i], u->partition, names[i]);
+        if (st != FP_OK) return st;
+        for (int j = 0; j < i; ++j)
+            if (overlap(f32[i], b4, f32[j], b4)) return fail(FP_ERR_INVALID, "%s overlaps %s", names[i], names[j]);
+        for (int32_t k = 0; k < u->n; ++k) {
+            const int64_t S = u->shard[k];
+            for (int32_t q = 0; q < u->world; ++q)
+                if (overlap(u->grads[(size_t)k * u->world + q], 2 * S, f32[i], b4))
+                    return fail(FP_ERR_INVALID, "unit %d: grads[%d] overlaps %s", k, q, names[i]);
+            if (u->has_unshard && overlap(u->full[k], 2 * S * u->world, f32[i], b4))
+                return fail(FP_ERR_INVALID, "unit %d: full overlaps %s", k, names[i]);
+        }
+    }
+    return FP_OK;
+}
+
+fp_status check_units_device(const fp_units* u) {
+    int device = -1;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+    if (device != u->device)
+        return fail(FP_ERR_INVALID, "units plan was created on device %d, current is %d", u->device, device);
+    return FP_OK;
+}
+
+void fill_units_args(const fp_units* u, UnitsArgs* a) {
+    std::memset(a, 0, sizeof *a);
+    a->units = units_desc(u);
+    a->tile_start = units_tile_start(u);
+    a->copy_start = units_copy_start(u);
+    a->reduce_groups = u->reduce_groups;
+    a->n_units = u->n;
+    a->world = u->world;
+    a->rank = u->rank;
+}
+}  // namespace
+
+extern "C" fp_status fp_units_create(int32_t n_units, int32_t world, int32_t rank, const int64_t* shard,
+                                     const uint16_t* const* grads, const uint16_t* const* shards,
+                                     uint16_t* const* full, fp_units** out) {
+    if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    fp_status st;
+    if (n_units < 1) return fail(FP_ERR_RANGE, "n_units must be >= 1");
+    if ((st = check_world(world)) != FP_OK) return st;
+    if (rank < 0 || rank >= world) return fail(FP_ERR_RANGE, "rank %d outside [0, %d)", rank, world);
+    if (shard == nullptr || grads == nullptr) return fail(FP_ERR_INVALID, "shard or grads table is NULL");
+    if ((shards == nullptr) != (full == nullptr))
+        return fail(FP_ERR_INVALID, "shards and full must both be given or both be NULL");
+    const bool unshard = shards != nullptr;
+    int64_t partition = 0, tiles = 0, copies = 0;
+    for (int32_t k = 0; k < n_units; ++k) {
+        const int64_t S = shard[k];
+        if (S < 0 || S > ((int64_t)1 << 40)) return fail(FP_ERR_RANGE, "unit %d: shard %lld out of range", k, (long long)S);
+        if ((st = check_ptr_table(grads + (size_t)k * world, world, S, false, "grads")) != FP_OK) return st;
+        if (unshard) {
+            if ((st = check_ptr_table(shards + (size_t)k * world, world, S, true, "shards")) != FP_OK) return st;
+            if (full[k] == nullptr && S > 0) return fail(FP_ERR_INVALID, "unit %d: full is NULL", k);
+            if (!aligned(full[k], 2)) return fail(FP_ERR_ALIGN, "unit %d: full misaligned", k);
+            for (int32_t q = 0; q < world; ++q) {
+                const uint16_t* src = shards[(size_t)k * world + q];
+                if (q != rank && src == nullptr && S > 0) return fail(FP_ERR_INVALID, "unit %d: shards[%d] is NULL", k, q);
+                if (q != rank && overlap(src, 2 * S, full[k], 2 * S * world))
+                    return fail(FP_ERR_INVALID, "unit %d: shards[%d] overlaps full", k, q);
+                if (overlap(grads[(size_t)k * world + q], 2 * S, full[k], 2 * S * world))
+                    return fail(FP_ERR_INVALID, "unit %d: grads[%d] overlaps full", k, q);
+            }
+        }
+        partition += (S + 3) & ~(int64_t)3;
+        tiles += unit_tiles(S);
+        if (unshard) copies += (int64_t)(world - 1) * copy_tiles_per_shard(S, kCopyWordsStream);
+    }
+    if (tiles + copies > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "units too large for one launch");
+
+    fp_units* u = new (std::nothrow) fp_units();
+    if (u == nullptr) return fail(FP_ERR_DEVICE, "out of host memory");
+    u->n = n_units;
+    u->world = world;
+    u->rank = rank;
+    u->has_unshard = unshard;
+    u->shard.assign(shard, shard + n_units);
+    u->grads.assign(grads, grads + (size_t)n_units * world);
+    if (unshard) {
+        u->shards.assign(shards, shards + (size_t)n_units * world);
+        u->full.assign(full, full + n_units);
+    }
+    u->reduce_groups = tiles;
+    u->copy_groups = copies;
+    u->partition = partition;
+
+    // host image of the device tables
+    const size_t n = (size_t)n_units, w = (size_t)world;
+    const size_t desc_b = n * sizeof(UnitDesc), start_b = (n + 1) * sizeof(int64_t);
+    const size_t ptr_b = n * w * sizeof(void*);
+    const size_t total_b = desc_b + 2 * start_b + 2 * ptr_b;
+    std::vector<unsigned char> img(total_b, 0);
+    hipError_t e = hipGetDevice(&u->device);
+    if (e == hipSuccess) e = hipMalloc(&u->dev, total_b);
+    if (e != hipSuccess) {
+        u->dev = nullptr;
+        free_units(u);
+        return device_fail(e, "allocating the units tables");
+    }
+    char* base = static_cast<char*>(u->dev);
+    UnitDesc* desc = reinterpret_cast<UnitDesc*>(img.data());
+    int64_t* tile_start = reinterpret_cast<int64_t*>(img.data() + desc_b);
+    int64_t* copy_start = tile_start + n + 1;
+    const uint16_t** gtab = reinterpret_cast<const uint16_t**>(img.data() + desc_b + 2 * start_b);
+    const uint16_t** stab = gtab + n * w;
+    int64_t off = 0, t0 = 0, c0 = 0;
+    bool al = true;
+    for (size_t k = 0; k < n; ++k) {
+        const int64_t S = shard[k];
+        UnitDesc& d = desc[k];
+        d.grads = reinterpret_cast<const uint16_t* const*>(base + desc_b + 2 * start_b + k * w * sizeof(void*));
+        d.shards = unshard ? reinterpret_cast<const uint16_t* const*>(base + desc_b + 2 * start_b + ptr_b +
+                                                                      k * w * sizeof(void*))
+                           : nullptr;
+        d.full = unshard ? full[k] : nullptr;
+        d.shard = S;
+        d.offset = off;
+        d.copy_tiles = unshard ? (int32_t)copy_tiles_per_shard(S, kCopyWordsStream) : 0;
+        u->offset.push_back(off);
+        tile_start[k] = t0;
+        copy_start[k] = c0;
+        off += (S + 3) & ~(int64_t)3;
+        t0 += unit_tiles(S);
+        if (unshard) c0 += (int64_t)(world - 1) * d.copy_tiles;
+        for (size_t q = 0; q < w; ++q) {
+            gtab[k * w + q] = grads[k * w + q];
+            al = al && is_aligned8(grads[k * w + q]);
+            if (unshard) {
+                stab[k * w + q] = (int32_t)q == rank ? nullptr : shards[k * w + q];
+                if ((int32_t)q != rank) al = al && copy_source_aligned(shards[k * w + q], full[k], S, (int)q);
+            }
+        }
+        if (unshard) al = al && is_aligned8(full[k] + (int64_t)rank * S);
+    }
+    tile_start[n] = t0;
+    copy_start[n] = c0;
+    u->aligned = al;
+    if ((e = hipMemcpy(u->dev, img.data(), total_b, hipMemcpyHostToDevice)) != hipSuccess) {
+        free_units(u);
+        return device_fail(e, "uploading the units tables");
+    }
+    *out = u;
+    return FP_OK;
+}
+
+extern "C" void fp_units_destroy(fp_units* units) {
+    if (units != nullptr) free_units(units);
+}
+
+extern "C" fp_status fp_units_info(const fp_units* units, int64_t* partition, int64_t* workspace_bytes) {
+    if (units == nullptr) return fail(FP_ERR_INVALID, "units is NULL");
+    if (partition) *partition = units->partition;
+    if (workspace_bytes) *workspace_bytes = units_workspace_bytes(units);
+    return FP_OK;
+}
+
+extern "C" fp_status fp_units_offsets(const fp_units* units, int64_t* offsets) {
+    if (units == nullptr || offsets == nullptr) return fail(FP_ERR_INVALID, "units or offsets is NULL");
+    for (int32_t k = 0; k < units->n; ++k) offsets[k] = units->offset[k];
+    return FP_OK;
+}
+
+extern "C" fp_status fp_units_reduce(const fp_units* units, float scale, int32_t accumulate, float* acc,
+                                     int32_t* found_inf, double* sq_norm, void* workspace, void* stream) {
+    if (units == nullptr) return fail(FP_ERR_INVALID, "units is NULL");
+    fp_status st;
+    const float* f32[1] = {acc};
+    const char* names[1] = {"acc"};
+    if ((st = check_units_state(units, f32, names, 1)) != FP_OK) return st;
+    if (found_inf != nullptr && !aligned(found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
+    if (sq_norm != nullptr) {
+        if (!aligned(sq_norm, 8)) return fail(FP_ERR_ALIGN, "sq_norm misaligned");
+        if (workspace == nullptr) return fail(FP_ERR_INVALID, "sq_norm needs a workspace");
+        if (!aligned(workspace, 16)) return fail(FP_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    if ((st = check_units_device(units)) != FP_OK) return st;
+    UnitsArgs a;
+    fill_units_args(units, &a);
+    a.acc = acc;
+    a.found_inf = found_inf;
+    a.partials = sq_norm != nullptr ? partials_of(workspace) : nullptr;
+    a.scale = scale;
+    a.accumulate = accumulate ? 1 : 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_units_reduce(a, units->aligned, s);
+    if (e != hipSuccess) return device_fail(e, "units reduce launch");
+    if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)units->reduce_groups, sq_norm, s)) != hipSuccess)
+        return device_fail(e, "norm launch");
+    return FP_OK;
+}
+
+extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream) {
+    if (units == nullptr || args == nullptr) return fail(FP_ERR_INVALID, "units or args is NULL");
+    const fp_units_step_args& x = *args;
+    if (!units->has_unshard) return fail(FP_ERR_INVALID, "units plan has no shards / full buffers");
+    if (x.flags & ~(FP_STEP_NO_SKIP | FP_STEP_KEEP_GRAD)) return fail(FP_ERR_INVALID, "unknown flags");
+    UnitsArgs a;
+    fill_units_args(units, &a);
+    fp_status st;
+    if ((st = check_hparams(&x.hp, &a.c)) != FP_OK) return st;
+    const float* f32[4] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq};
+    const char* names[4] = {"acc", "master", "exp_avg", "exp_avg_sq"};
+    if ((st = check_units_state(units, f32, names, 4)) != FP_OK) return st;
+    if (x.found_inf == nullptr) return fail(FP_ERR_INVALID, "found_inf is NULL");
+    if (!aligned(x.found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
+    if (x.sq_norm != nullptr) {
+        if (!aligned(x.sq_norm, 8)) return fail(FP_ERR_ALIGN, "sq_norm misaligned");
+        if (x.workspace == nullptr) return fail(FP_ERR_INVALID, "sq_norm needs a workspace");
+        if (!aligned(x.workspace, 16)) return fail(FP_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    if ((st = check_units_device(units)) != FP_OK) return st;
+    const bool no_skip = (x.flags & FP_STEP_NO_SKIP) != 0;
+    a.acc = x.acc;
+    a.master = x.master;
+    a.exp_avg = x.exp_avg;
+    a.exp_avg_sq = x.exp_avg_sq;
+    a.found_inf = x.found_inf;
+    a.partials = x.sq_norm != nullptr ? partials_of(x.workspace) : nullptr;
+    a.scale = x.scale;
+    a.accumulate = x.accumulate ? 1 : 0;
+    a.keep_grad = (x.flags & FP_STEP_KEEP_GRAD) ? 1 : 0;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[FP_STEP_EVENTS] = {nullptr, nullptr, nullptr};
+    if (x.profile_events != nullptr)
+        for (int i = 0; i < FP_STEP_EVENTS; ++i) ev[i] = static_cast<hipEvent_t>(x.profile_events[i]);
+    hipError_t e;
+    if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    if ((e = launch_units_phase1(a, units->copy_groups, no_skip, units->aligned, s)) != hipSuccess)
+        return device_fail(e, "units step launch");
+    if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (no_skip) {
+        if (x.sq_norm != nullptr &&
+            (e = launch_norm_finalize(a.partials, (int)units->reduce_groups, x.sq_norm, s)) != hipSuccess)
+            return device_fail(e, "norm launch");
+    } else {
+        a.sq_norm = x.sq_norm;
+        if ((e = launch_units_adamw(a, units->aligned, s)) != hipSuccess) return device_fail(e, "units adamw launch");
+    }
+    if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    return FP_OK;
+}
+
 // ---------------------------------------------------------------------- helpers
 
 extern "C" fp_status fp_state_bytes(double psi, int32_t world, double k, int32_t stage, double* out) {

@@ -154,6 +154,51 @@ struct StepArgs {
     GridSync* sync;          // one-pass: barrier state in the workspace
 };
 
+// One unit of a multi-unit launch (device table entry).  The rank's fp32
+// partition (acc, master, moments) holds unit u at element `offset`, a
+// multiple of 4, so every unit's fp32 shard is 16-byte aligned.
+struct UnitDesc {
+    const uint16_t* const* grads;   // world device pointers: rank q's bf16 gradient
+    const uint16_t* const* shards;  // world device pointers (entry rank null), or null
+    uint16_t* full;                 // bf16[world * shard], or null
+    int64_t shard;
+    int64_t offset;
+    int32_t copy_tiles;             // copy workgroups per other shard
+    int32_t pad;
+};
+
+// A launch over all units of a plan.  Workgroup i < reduce_groups takes a
+// reduce / AdamW tile of unit u with tile_start[u] <= i < tile_start[u+1];
+// copy workgroup j (numbered from reduce_groups) takes copy tile
+// j - copy_start[u] of unit u with copy_start[u] <= j < copy_start[u+1].
+struct UnitsArgs {
+    const UnitDesc* units;
+    const int64_t* tile_start;   // [n_units + 1]
+    const int64_t* copy_start;   // [n_units + 1]
+    float* acc;
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    int32_t* found_inf;
+    double* partials;
+    double* sq_norm;             // AdamW launch: finalised by workgroup 0
+    AdamCoef c;
+    int64_t reduce_groups;       // tile_start[n_units]
+    float scale;
+    int32_t n_units;
+    int32_t world;
+    int32_t rank;
+    int32_t accumulate;
+    int32_t keep_grad;
+};
+
+// Reduce / AdamW workgroups of one unit: at least one, so that its tail
+// elements and flag have an owner.
+inline int64_t unit_tiles(int64_t S) {
+    const int64_t t = tiles_of(S >> 2);
+    return t > 0 ? t : 1;
+}
+
 struct PackArgs {
     const int64_t* offsets;     // [n_tensors + 1] prefix sums, offsets[n] = T
     const int32_t* group_first; // [n_groups + 1] first tensor overlapping each group
@@ -180,5 +225,13 @@ hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update
 hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
 hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
+// Multi-unit launches: one micro-batch's reduce over all units; the last
+// micro-batch's reduce (+ AdamW when fused) with the copies of all units'
+// other shards (copy_groups workgroups after the reduce tiles); AdamW over
+// all units.
+hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s);
+hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update,
+                               bool aligned, hipStream_t s);
+hipError_t launch_units_adamw(const UnitsArgs& a, bool aligned, hipStream_t s);
 
 }  // namespace fpk

@@ -214,3 +214,33 @@ def test_step_path_without_a_device(fp):
     a.master = 0x4000010                       # overlaps acc
     assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -1
     assert _status(L.fp_step_path, C.byref(a), None) == -1
+
+
+def test_units_validation_without_a_device(fp):
+    """fp_units_create rejects bad arguments before any device call."""
+    L = fp.lib()
+    out = C.c_void_p()
+    sizes = (C.c_int64 * 2)(16, 8)
+    g = (C.c_void_p * 4)(0x1000000, 0x2000000, 0x3000000, 0x4000000)
+    assert _status(L.fp_units_create, 0, 2, 0, sizes, g, None, None, C.byref(out)) == -2   # no units
+    assert _status(L.fp_units_create, 2, 0, 0, sizes, g, None, None, C.byref(out)) == -2   # world 0
+    assert _status(L.fp_units_create, 2, 2, 2, sizes, g, None, None, C.byref(out)) == -2   # rank
+    assert _status(L.fp_units_create, 2, 2, 0, None, g, None, None, C.byref(out)) == -1
+    assert _status(L.fp_units_create, 2, 2, 0, sizes, None, None, None, C.byref(out)) == -1
+    full = (C.c_void_p * 2)(0x5000000, 0x6000000)
+    assert _status(L.fp_units_create, 2, 2, 0, sizes, g, None, full, C.byref(out)) == -1  # shards missing
+    g_odd = (C.c_void_p * 4)(0x1000000, 0x2000001, 0x3000000, 0x4000000)
+    assert _status(L.fp_units_create, 2, 2, 0, sizes, g_odd, None, None, C.byref(out)) == -3
+    g_null = (C.c_void_p * 4)(0x1000000, None, 0x3000000, 0x4000000)
+    assert _status(L.fp_units_create, 2, 2, 0, sizes, g_null, None, None, C.byref(out)) == -1
+    neg = (C.c_int64 * 2)(16, -1)
+    assert _status(L.fp_units_create, 2, 2, 0, neg, g, None, None, C.byref(out)) == -2
+    # a gradient row inside its unit's full buffer
+    sh = (C.c_void_p * 4)(None, 0x7000000, None, 0x8000000)
+    g_in = (C.c_void_p * 4)(0x5000000, 0x2000000, 0x3000000, 0x4000000)
+    assert _status(L.fp_units_create, 2, 2, 0, sizes, g_in, sh, full, C.byref(out)) == -1
+    assert out.value is None
+    assert _status(L.fp_units_info, None, None, None) == -1
+    assert _status(L.fp_units_reduce, None, 1.0, 0, None, None, None, None, None) == -1
+    assert _status(L.fp_units_step, None, None, None) == -1
+    L.fp_units_destroy(None)
