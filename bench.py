@@ -1,13 +1,16 @@
 """Throughput of one rank's shard step (reduce + AdamW + bf16 cast + unshard).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode exact|noskip]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--mode exact|twophase|noskip] [--eager]
 
-A step is the whole per-step hot path for rank r's shard of one unit: the
-fixed-order reduce of the N_d ranks' bf16 gradients (last micro-batch),
-the AdamW update of the fp32 master / moments with the overflow gate, the
-bf16 cast of the own shard into the full buffer and the copy of the other
-N_d - 1 shards into it (fp_shard_step).  Pack and views are one-time set-up
-per unit and are not part of a step.
+A step is the whole per-step hot path for rank r's shard: the fixed-order
+reduce of the N_d ranks' bf16 gradients for every micro-batch, the AdamW
+update of the fp32 master / moments with the overflow gate, the bf16 cast
+of the own shard into the full buffer and the copy of the other N_d - 1
+shards into it.  Single-unit workloads run fp_shard_step; the bucketed
+workload runs the multi-unit entry points, one launch per micro-batch over
+all buckets.  Pack and views are one-time set-up per unit and are not part
+of a step; pack throughput is reported on its own.
 
 All inputs are synthetic and resident in HBM before timing starts.  The
 step rotates over enough buffer sets (>= 1.5 GB) that no step finds its
@@ -17,7 +20,7 @@ Output: one JSON line.  `value` is algorithmic GB/s of the whole step,
 B = 2*N*n + 8*(n-1) + 24 + 2 + 4*(N-1) bytes per shard element; `roofline`
 times the dominant kernel with HIP events recorded around it on the
 library's stream inside the timed region; `cpu_baseline` times the serial
-CPU oracle on the same workload on one host core.
+CPU oracle on a bounded sample of the same workload on one host core.
 """
 
 from __future__ import annotations
@@ -40,8 +43,11 @@ METRIC = "shard-step GB/s and params/s (reduce+AdamW+unshard), % of MI355X HBM p
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 ROTATE_BYTES = 1.5e9           # buffer-set rotation span, > 256 MB Infinity Cache
 KERNEL_SOURCES = ["sharded_flatparameter_pack_amd/csrc/step_kernels.hip",
+                  "sharded_flatparameter_pack_amd/csrc/unit_kernels.hip",
+                  "sharded_flatparameter_pack_amd/csrc/step_ops.h",
                   "sharded_flatparameter_pack_amd/csrc/fp_device.h",
                   "sharded_flatparameter_pack_amd/csrc/fp_internal.h"]
+MODE_FLAGS = {"exact": "FP_STEP_EXACT_SKIP", "twophase": "FP_STEP_NO_COOP", "noskip": "FP_STEP_NO_SKIP"}
 
 
 def step_bytes_per_elem(world: int, n_micro: int) -> int:
@@ -63,6 +69,7 @@ class HipEvents:
     def __init__(self):
         self.L = C.CDLL("libamdhip64.so.7")
         self.L.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.L.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.L.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.L.hipEventSynchronize.argtypes = [C.c_void_p]
         self.L.hipEventDestroy.argtypes = [C.c_void_p]
@@ -72,6 +79,10 @@ class HipEvents:
         if self.L.hipEventCreate(C.byref(e)) != 0:
             raise RuntimeError("hipEventCreate failed")
         return e.value
+
+    def record(self, e, stream):
+        if self.L.hipEventRecord(C.c_void_p(e), C.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b) -> float:
         ms = C.c_float()
@@ -84,63 +95,279 @@ class HipEvents:
         self.L.hipEventDestroy(C.c_void_p(e))
 
 
-def make_sets(cfg, rank, n_sets, dev):
-    """n_sets independent buffer sets of one rank's shard step, all on the GPU."""
+# ------------------------------------------------------------------ workloads
+class SingleUnit:
+    """Buffer sets of one rank's step on one unit (fp_shard_step)."""
+
+    def __init__(self, cfg, rank, dev, flags):
+        import torch
+        import sharded_flatparameter_pack_amd as fp
+        from workloads import gen
+        self.cfg, self.rank, self.world, self.n_micro = cfg, rank, cfg.world, cfg.n_micro
+        self.S = S = -(-cfg.units()[0] // cfg.world)
+        world = self.world
+        per_set = S * (2 * world + 16 + 2 * (world - 1) + 2 * world)
+        self.n_sets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        self.sets = []
+        for k in range(self.n_sets):
+            key = lambda stream, q=0: (stream, k, 0, q)  # noqa: E731
+            grads = gen.torch_bf16_normal(world * S, cfg.grad_sigma, cfg.seed, key(gen.STREAM_GRAD), dev)
+            others = gen.torch_bf16_normal(world * S, cfg.master_sigma, cfg.seed, key(gen.STREAM_SHARD), dev)
+            s = dict(grads=grads.view(world, S),
+                     shards=[None if q == rank else others[q * S:(q + 1) * S] for q in range(world)],
+                     master=gen.torch_normal_f32(S, cfg.master_sigma, cfg.seed, key(gen.STREAM_MASTER), dev),
+                     exp_avg=torch.zeros(S, dtype=torch.float32, device=dev),
+                     exp_avg_sq=torch.zeros(S, dtype=torch.float32, device=dev),
+                     acc=torch.zeros(S, dtype=torch.float32, device=dev),
+                     full=torch.zeros(world * S, dtype=torch.int16, device=dev),
+                     found_inf=torch.zeros(1, dtype=torch.int32, device=dev),
+                     workspace=fp.new_workspace(dev, S))
+            self.sets.append(s)
+        self.set_flags(flags)
+
+    def set_flags(self, flags):
+        import sharded_flatparameter_pack_amd as fp
+        hp, world = self.cfg.hp, self.world
+        self.calls = [fp.ShardStep(s["grads"], s["acc"], s["master"], s["exp_avg"], s["exp_avg_sq"],
+                                   s["shards"], s["full"], self.rank, scale=1.0 / world, lr=hp.lr,
+                                   beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
+                                   weight_decay=hp.weight_decay, found_inf=s["found_inf"],
+                                   workspace=s["workspace"], flags=flags)
+                      for s in self.sets]
+        self.path = self.calls[0].path()
+
+    def n_events(self):
+        return 3
+
+    def step(self, i, events=None):
+        self.calls[i % self.n_sets](i // self.n_sets + 1, events)
+
+    def kernels(self, step_ms, ev_ms):
+        """(name, rocprof id, ms per launch, algorithmic bytes per launch, launches per step)."""
+        import sharded_flatparameter_pack_amd as fp
+        S, N = self.S, self.world
+        B = step_bytes_per_elem(N, 1)
+        if self.path == fp.FP_PATH_NO_SKIP:
+            return [("step_phase1_kernel<true>", "step_phase1_fused", step_ms, S * B, 1)]
+        if self.path == fp.FP_PATH_ONE_PASS:
+            return [("step_coop_kernel", "step_coop", step_ms, S * B, 1)]
+        k1, k2 = ev_ms[1] - ev_ms[0], ev_ms[2] - ev_ms[1]
+        f1 = k1 / (k1 + k2)
+        return [("step_phase1_kernel<false>", "step_phase1", step_ms * f1, S * (2 * N + 4 * (N - 1)), 1),
+                ("adamw_kernel", "adamw", step_ms * (1 - f1), S * 26, 1)]
+
+    def flagged(self):
+        import sharded_flatparameter_pack_amd as fp
+        if any(int(s["found_inf"].item()) for s in self.sets):
+            return "unexpected overflow flag in a finite workload"
+        if any(fp.workspace_timeouts(s["workspace"]) for s in self.sets):
+            return "grid barrier wait gave up"
+        return None
+
+
+class Bucketed:
+    """Buffer sets of one rank's step on all buckets of a bucketed model: one
+    multi-unit reduce launch per earlier micro-batch, then fp_units_step."""
+
+    def __init__(self, cfg, rank, dev, flags):
+        import torch
+        import sharded_flatparameter_pack_amd as fp
+        from workloads import gen
+        self.cfg, self.rank, self.world, self.n_micro = cfg, rank, cfg.world, cfg.n_micro
+        N, n = cfg.world, cfg.n_micro
+        sizes = [-(-T // N) for T in cfg.units()]
+        self.sizes = sizes
+        self.S = sum(sizes)
+        per_set = self.S * (2 * N * n + 16 + 4 * N)
+        self.n_sets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        offs = [0]
+        for S in sizes[:-1]:
+            offs.append(offs[-1] + S)
+        self.sets = []
+        for k in range(self.n_sets):
+            # rank q's gradient (and shard) rows of bucket b are slices of one buffer per set and micro-batch
+            grads = [gen.torch_bf16_normal(N * self.S, cfg.grad_sigma, cfg.seed, (gen.STREAM_GRAD, k, m), dev)
+                     .view(N, self.S) for m in range(n)]
+            others = gen.torch_bf16_normal(N * self.S, cfg.master_sigma, cfg.seed, (gen.STREAM_SHARD, k),
+                                           dev).view(N, self.S)
+            full = [torch.zeros(N * S, dtype=torch.int16, device=dev) for S in sizes]
+            g_rows = [[[grads[m][q, o:o + S] for q in range(N)] for o, S in zip(offs, sizes)]
+                      for m in range(n)]
+            sh_rows = [[None if q == rank else others[q, o:o + S] for q in range(N)]
+                       for o, S in zip(offs, sizes)]
+            plans = [fp.Units(g_rows[m], rank, shards=sh_rows, full=full) for m in range(n)]
+            P = plans[0].partition
+            self.sets.append(dict(plans=plans, grads=grads, others=others, full=full,
+                                  master=gen.torch_normal_f32(P, cfg.master_sigma, cfg.seed,
+                                                              (gen.STREAM_MASTER, k), dev),
+                                  exp_avg=torch.zeros(P, dtype=torch.float32, device=dev),
+                                  exp_avg_sq=torch.zeros(P, dtype=torch.float32, device=dev),
+                                  acc=torch.zeros(P, dtype=torch.float32, device=dev),
+                                  found_inf=torch.zeros(1, dtype=torch.int32, device=dev)))
+        self.ev = HipEvents()
+        self.set_flags(flags)
+
+    def set_flags(self, flags):
+        import sharded_flatparameter_pack_amd as fp
+        self.flags = flags & fp.FP_STEP_NO_SKIP       # the multi-unit step has no one-pass form
+        self.path = fp.FP_PATH_NO_SKIP if self.flags else fp.FP_PATH_TWO_PHASE
+
+    def n_events(self):
+        return self.n_micro + 2
+
+    def step(self, i, events=None):
+        import torch
+        s = self.sets[i % self.n_sets]
+        hp, n = self.cfg.hp, self.n_micro
+        scale = 1.0 / (self.world * n)
+        stream = torch.cuda.current_stream().cuda_stream
+        for m in range(n - 1):
+            if events is not None:
+                self.ev.record(events[m], stream)
+            s["plans"][m].reduce(s["acc"], scale=scale, accumulate=m > 0, found_inf=s["found_inf"])
+        s["plans"][n - 1].step(s["acc"], s["master"], s["exp_avg"], s["exp_avg_sq"], scale=scale,
+                               accumulate=n > 1, lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
+                               weight_decay=hp.weight_decay, step=i // self.n_sets + 1,
+                               found_inf=s["found_inf"], flags=self.flags,
+                               profile_events=None if events is None else events[n - 1:n + 2])
+
+    def kernels(self, step_ms, ev_ms):
+        S, N, n = self.S, self.world, self.n_micro
+        d = [ev_ms[i + 1] - ev_ms[i] for i in range(n + 1)]
+        tot = sum(d)
+        out = []
+        acc_in = 4 if n > 1 else 0
+        if n > 1:
+            t_red = sum(d[:n - 1]) / tot * step_ms
+            alg_red = S * (2 * N * (n - 1) + 4 + 8 * (n - 2))   # the first writes acc, later ones read + write
+            out.append(("units_reduce_kernel", "units_reduce", t_red / (n - 1), alg_red / (n - 1), n - 1))
+        if self.flags:
+            out.append(("units_phase1_kernel<true>", "units_phase1_fused", (d[n - 1] + d[n]) / tot * step_ms,
+                        S * (2 * N + acc_in + 26 + 4 * (N - 1)), 1))
+        else:
+            out.append(("units_phase1_kernel<false>", "units_phase1", d[n - 1] / tot * step_ms,
+                        S * (2 * N + acc_in + 4 * (N - 1)), 1))
+            out.append(("units_adamw_kernel", "units_adamw", d[n] / tot * step_ms, S * 26, 1))
+        return out
+
+    def flagged(self):
+        if any(int(s["found_inf"].item()) for s in self.sets):
+            return "unexpected overflow flag in a finite workload"
+        return None
+
+
+def make_workload(cfg, rank, dev, flags):
+    if cfg.shapes is None:
+        return Bucketed(cfg, rank, dev, flags)
+    if cfg.n_micro == 1:
+        return SingleUnit(cfg, rank, dev, flags)
+    raise ValueError("single-unit workloads with several micro-batches are not benchmarked")
+
+
+# ------------------------------------------------------------------ timing
+def time_steps(w, K, W, eager, ev):
+    """(step ms, mean event offsets of an eager pass in ms, steps timed, how)."""
+    import torch
+    for i in range(W):
+        w.step(i)
+    torch.cuda.synchronize()
+
+    def eager_pass(first, count):
+        evs = [[ev.create() for _ in range(w.n_events())] for _ in range(count)]
+        torch.cuda.synchronize()
+        for k in range(count):
+            w.step(first + k, evs[k])
+        torch.cuda.synchronize()
+        mean = [0.0] * w.n_events()
+        for e in evs:
+            for j in range(1, len(e)):
+                mean[j] += ev.elapsed_ms(e[0], e[j]) / count
+            for x in e:
+                ev.destroy(x)
+        return mean
+
+    if eager:
+        ev_ms = eager_pass(W, K)
+        return ev_ms[-1], ev_ms, K, "eager launches from Python; step and kernel times from hipEvents " \
+                                    "recorded around the library's kernels"
+    n = w.n_sets
+    reps = max(1, -(-K // n))
+    K = reps * n
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            w.step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            w.step(i)
+    for _ in range(max(1, W // n)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / K
+    del graph
+    ev_ms = eager_pass(W + K, min(K, 200))
+    return step_ms, ev_ms, K, "HIP graph of one step per buffer set, replayed; span timed by hipEvents " \
+                              "on the replay stream; per-kernel split from hipEvents in an eager pass"
+
+
+def pack_bench(cfg, dev, reps: int):
+    """fp_pack of the workload's FlatParameter (fp32 tensors): elements/s and GB/s."""
     import torch
     import sharded_flatparameter_pack_amd as fp
-    from workloads import gen
-    world = cfg.world
-    T = cfg.units()[0]
-    S = -(-T // world)
-    sets = []
-    for k in range(n_sets):
-        key = lambda stream, q=0: (stream, k, 0, q)  # noqa: E731
-        grads = gen.torch_bf16_normal(world * S, cfg.grad_sigma, cfg.seed, key(gen.STREAM_GRAD), dev)
-        others = gen.torch_bf16_normal(world * S, cfg.master_sigma, cfg.seed, key(gen.STREAM_SHARD), dev)
-        sets.append(dict(
-            grads=grads.view(world, S),
-            shards=[None if q == rank else others[q * S:(q + 1) * S] for q in range(world)],
-            master=gen.torch_normal_f32(S, cfg.master_sigma, cfg.seed, key(gen.STREAM_MASTER), dev),
-            exp_avg=torch.zeros(S, dtype=torch.float32, device=dev),
-            exp_avg_sq=torch.zeros(S, dtype=torch.float32, device=dev),
-            acc=torch.zeros(S, dtype=torch.float32, device=dev),
-            full=torch.zeros(world * S, dtype=torch.int16, device=dev),
-            found_inf=torch.zeros(1, dtype=torch.int32, device=dev),
-            workspace=fp.new_workspace(dev, S)))
-    return S, sets
+    plan = fp.Plan(cfg.shapes, cfg.world)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    tensors = [torch.randn(s, generator=g, device=dev, dtype=torch.float32) for s in cfg.shapes]
+    flat = torch.empty(plan.padded, dtype=torch.float32, device=dev)
+    plan.pack(tensors, flat)
+    torch.cuda.synchronize()
+    ms = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        plan.pack(tensors, flat)
+        e1.record()
+        torch.cuda.synchronize()
+        ms += e0.elapsed_time(e1)
+    ms /= reps
+    alg = 4 * plan.numel + 4 * plan.padded
+    gbs = alg / (ms * 1e-3) / 1e9
+    out = {"workload": cfg.name, "tensors": len(cfg.shapes), "elements": plan.numel, "padded": plan.padded,
+           "dtype": "fp32", "us_per_pack": round(ms * 1e3, 2), "elements_per_s": round(plan.numel / (ms * 1e-3), 1),
+           "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "timing": f"hipEvents around each fp_pack call (pointer-table upload + kernel), mean of {reps} calls"}
+    plan.close()
+    return out
 
 
-def cpu_baseline(cfg, rank, budget_s: float):
-    """The serial CPU oracle on the same workload, on one host core."""
-    import numpy as np
-    import oracle
-    from workloads import gen
-    world = cfg.world
-    S = -(-cfg.units()[0] // world)
-    grads = [gen.bf16_normal(S, cfg.grad_sigma, cfg.seed, gen.STREAM_GRAD, 0, 0, q) for q in range(world)]
-    others = [gen.bf16_normal(S, cfg.master_sigma, cfg.seed, gen.STREAM_SHARD, 0, 0, q) for q in range(world)]
-    master = gen.normal_f32(S, cfg.master_sigma, cfg.seed, gen.STREAM_MASTER)
-    m, v, acc = np.zeros(S, np.float32), np.zeros(S, np.float32), np.zeros(S, np.float32)
-    old = os.sched_getaffinity(0)
-    core = min(old)
-    os.sched_setaffinity(0, {core})
-    try:
-        oracle.lib()
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.shard_step([grads], acc, master, m, v, others, rank, hp=cfg.hp, step=reps + 1)
-            reps += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        dt = time.perf_counter() - t0
-    finally:
-        os.sched_setaffinity(0, old)
-    B = step_bytes_per_elem(world, 1)
-    return {"value": round(S * reps * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "params_per_s": round(S * reps / dt, 1), "seconds": round(dt, 2),
-            "host_cores_available": len(old), "cpu": platform.processor() or platform.machine(),
-            "sample": f"{reps} whole shard steps of the {cfg.name} workload (rank {rank}, S={S}, "
-                      f"N_d={world}) by the serial oracle: reduce, AdamW, bf16 cast, unshard"}
+def copy_reference(fp, dev, reps: int = 20):
+    """Measured plain-copy bandwidth (fp_unshard of 16 x 8M bf16 shards, 256 MiB each way)."""
+    import torch
+    world, S = 16, 8 * 1024 * 1024
+    src = torch.ones(world * S, dtype=torch.int16, device=dev)
+    full = torch.zeros(world * S, dtype=torch.int16, device=dev)
+    shards = [src[q * S:(q + 1) * S] for q in range(world)]
+    fp.unshard(shards, full)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fp.unshard(shards, full)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return round(4 * world * S / (ms * 1e-3) / 1e9, 1)
 
 
 def copy_calibration(fp, dev, launches: int) -> int:
@@ -159,6 +386,45 @@ def copy_calibration(fp, dev, launches: int) -> int:
     return 0
 
 
+def cpu_baseline(cfg, rank, budget_s: float):
+    """The serial CPU oracle on a bounded sample of the workload, on one host core:
+    whole shard steps (all micro-batches) of a shard of at most 2M elements with
+    the workload's N_d and micro-batch count."""
+    import numpy as np
+    import oracle
+    from workloads import gen
+    world, n = cfg.world, cfg.n_micro
+    S_full = -(-cfg.units()[0] // world)
+    S = min(S_full, 2_000_000)
+    micro = [[gen.bf16_normal(S, cfg.grad_sigma, cfg.seed, gen.STREAM_GRAD, 0, m, q) for q in range(world)]
+             for m in range(n)]
+    others = [gen.bf16_normal(S, cfg.master_sigma, cfg.seed, gen.STREAM_SHARD, 0, 0, q) for q in range(world)]
+    master = gen.normal_f32(S, cfg.master_sigma, cfg.seed, gen.STREAM_MASTER)
+    m_, v_, acc = np.zeros(S, np.float32), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    old = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(old)})
+    try:
+        oracle.lib()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.shard_step(micro, acc, master, m_, v_, others, rank, hp=cfg.hp, step=reps + 1)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, old)
+    B = step_bytes_per_elem(world, n)
+    what = "the whole shard" if S == S_full else f"the first {S} elements of a {S_full}-element shard"
+    if len(cfg.units()) > 1:
+        what += f" of unit 0 (of {len(cfg.units())})"
+    return {"value": round(S * reps * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "params_per_s": round(S * reps / dt, 1), "seconds": round(dt, 2),
+            "host_cores_available": len(old), "cpu": platform.processor() or platform.machine(),
+            "sample": f"{reps} shard steps of {what} of the {cfg.name} workload (rank {rank}, N_d={world}, "
+                      f"{n} micro-batch(es)) by the serial oracle: reduce, AdamW, bf16 cast, unshard"}
+
+
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources."""
@@ -172,18 +438,21 @@ def load_traffic(workload: str, kernel: str):
     return d.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ main
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c2_layer_d1024_nd8")
-    ap.add_argument("--mode", choices=["exact", "twophase", "noskip"], default="exact",
-                    help="exact: exact overflow skip (one-pass cooperative kernel when the shard "
-                         "fits); twophase: exact skip with two kernels; noskip: one pass, no gate")
+    ap.add_argument("--mode", choices=list(MODE_FLAGS), default="exact",
+                    help="exact: exact overflow skip (one-pass kernel when the shard fits); "
+                         "twophase: exact skip with two kernels; noskip: one pass, no gate")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python with per-kernel events (launch-bound for "
                          "small shards) instead of replaying a captured HIP graph")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other modes, the pack and the copy reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run fp_unshard (a plain copy of known size) for counter calibration")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -208,128 +477,60 @@ def main(argv=None) -> int:
     if args.copy_calibration:
         return copy_calibration(fp, dev, args.steps)
     cfg = CONFIGS[args.workload]
-    if cfg.shapes is None or cfg.n_micro != 1:
-        print("bench.py times single-unit, single-micro-batch workloads", file=sys.stderr)
-        return 2
     rank = cfg.ranks[0]
-    world = cfg.world
-    B = step_bytes_per_elem(world, 1)
-    T = cfg.units()[0]
-    S = -(-T // world)
-    n_sets = max(2, math.ceil(ROTATE_BYTES / (S * (2 * world + 16 + 2 * (world - 1) + 2 * world))))
-    S, sets = make_sets(cfg, rank, n_sets, dev)
-    flags = {"exact": fp.FP_STEP_EXACT_SKIP, "twophase": fp.FP_STEP_NO_COOP,
-             "noskip": fp.FP_STEP_NO_SKIP}[args.mode]
-    hp = cfg.hp
+    world, n = cfg.world, cfg.n_micro
+    B = step_bytes_per_elem(world, n)
     ev = HipEvents()
-    K, W = args.steps, args.warmup
+    path_names = {fp.FP_PATH_ONE_PASS: "one-pass", fp.FP_PATH_TWO_PHASE: "two-phase",
+                  fp.FP_PATH_NO_SKIP: "fused-no-skip"}
 
-    calls = [fp.ShardStep(s["grads"], s["acc"], s["master"], s["exp_avg"], s["exp_avg_sq"],
-                          s["shards"], s["full"], rank, scale=1.0 / world, lr=hp.lr, beta1=hp.beta1,
-                          beta2=hp.beta2, eps=hp.eps, weight_decay=hp.weight_decay,
-                          found_inf=s["found_inf"], workspace=s["workspace"], flags=flags)
-             for s in sets]
-
-    def step(i, profile=None):
-        calls[i % n_sets](i // n_sets + 1, profile)
-
-    def eager_pass(first, count):
-        evs = [[ev.create() for _ in range(3)] for _ in range(count)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(count):
-            step(first + k, evs[k])
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        k1 = [ev.elapsed_ms(e[0], e[1]) for e in evs]
-        k2 = [ev.elapsed_ms(e[1], e[2]) for e in evs]
-        for e in evs:
-            for x in e:
-                ev.destroy(x)
-        return dt, sum(k1) / count, sum(k2) / count
-
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    if args.eager:
-        elapsed, k1_ms, k2_ms = eager_pass(W, K)
-        timing = "eager launches from Python; kernel times from hipEvents recorded by the library " \
-                 "around its kernels"
-    else:
-        # One step per buffer set captured into a graph; replays run the steps
-        # back to back on torch's current stream, timed by events on it.
-        reps = max(1, -(-K // n_sets))
-        K = reps * n_sets
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(n_sets):
-                step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(n_sets):
-                step(i)
-        for _ in range(max(1, W // n_sets)):
-            graph.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for _ in range(reps):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        span_ms = e0.elapsed_time(e1)
-        # per-kernel split of the step from a short eager pass with events
-        _, k1_ms, k2_ms = eager_pass(W + K, min(K, 200))
-        timing = "HIP graph of one step per buffer set, replayed; span timed by hipEvents on the " \
-                 "replay stream; per-kernel split from library-recorded hipEvents in an eager pass"
-    if any(int(s["found_inf"].item()) for s in sets):
-        print("unexpected overflow flag in a finite workload", file=sys.stderr)
+    w = make_workload(cfg, rank, dev, getattr(fp, MODE_FLAGS[args.mode]))
+    S = w.S
+    step_ms, ev_ms, K, timing = time_steps(w, args.steps, args.warmup, args.eager, ev)
+    bad = w.flagged()
+    if bad:
+        print(bad, file=sys.stderr)
         return 1
-    if any(fp.workspace_timeouts(s["workspace"]) for s in sets):
-        print("grid barrier wait gave up", file=sys.stderr)
-        return 1
-    path = calls[0].path()
-    step_ms = (span_ms / K) if not args.eager else (k1_ms + k2_ms)
-    ms_step = elapsed * 1e3 / K
-    gbs = S * B * K / elapsed / 1e9
-    if path in (fp.FP_PATH_NO_SKIP, fp.FP_PATH_ONE_PASS):
-        # one kernel per step: its average duration is the step's (graph span / steps)
-        nm = "step_phase1_kernel<true>" if path == fp.FP_PATH_NO_SKIP else "step_coop_kernel"
-        kid = "step_phase1_fused" if path == fp.FP_PATH_NO_SKIP else "step_coop"
-        kernels = [(nm, kid, step_ms, S * B)]
-    else:
-        frac1 = k1_ms / (k1_ms + k2_ms)
-        kernels = [("step_phase1_kernel<false>", "step_phase1", step_ms * frac1,
-                    S * (2 * world + 4 * (world - 1))),
-                   ("adamw_kernel", "adamw", step_ms * (1 - frac1), S * 26)]
-    name, kernel_id, dur_ms, alg = max(kernels, key=lambda x: x[2])
+    kernels = w.kernels(step_ms, ev_ms)
+    name, kernel_id, dur_ms, alg, _ = max(kernels, key=lambda x: x[2] * x[4])
     achieved = alg / (dur_ms * 1e-3) / 1e9
+    gbs = S * B / (step_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": W, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32/f64", "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32/f64", "data": "synthetic",
         "config": {"workload": cfg.name, "N_d": world, "rank": rank, "shard_elems": S,
-                   "unit_elems": T, "n_micro": 1, "mode": args.mode,
-                   "alg_bytes_per_elem": B, "buffer_sets": n_sets,
-                   "path": {fp.FP_PATH_ONE_PASS: "one-pass", fp.FP_PATH_TWO_PHASE: "two-phase",
-                            fp.FP_PATH_NO_SKIP: "fused-no-skip"}[path]},
-        "params_per_s": round(S * K / elapsed, 1),
+                   "units": len(cfg.units()), "n_micro": n, "mode": args.mode,
+                   "path": path_names[w.path], "alg_bytes_per_elem": B, "buffer_sets": w.n_sets},
+        "params_per_s": round(S / (step_ms * 1e-3), 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "kernels": [{"name": n, "avg_us": round(d * 1e3, 3), "alg_bytes": a,
-                     "alg_GBps": round(a / (d * 1e-3) / 1e9, 1)} for n, _, d, a in kernels],
+        "kernels": [{"name": nm, "avg_us": round(d * 1e3, 3), "launches_per_step": c, "alg_bytes": a,
+                     "alg_GBps": round(a / (d * 1e-3) / 1e9, 1)} for nm, _, d, a, c in kernels],
         "roofline": {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(cfg.name, kernel_id)},
         "timing": timing,
-        "eager_kernel_us": [round(k1_ms * 1e3, 3), round(k2_ms * 1e3, 3)],
         "source_hash": kernel_source_hash(),
     }
+    if not args.no_extras:
+        modes = {}
+        for mode in MODE_FLAGS:
+            if mode == args.mode:
+                continue
+            w.set_flags(getattr(fp, MODE_FLAGS[mode]))
+            ms = time_steps(w, min(args.steps, 400), min(args.warmup, 20), args.eager, ev)[0]
+            modes[mode] = {"path": path_names[w.path], "ms_per_step": round(ms, 5),
+                           "GBps": round(S * B / (ms * 1e-3) / 1e9, 2),
+                           "frac_of_hbm_peak": round(S * B / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        result["modes"] = modes
+        del w
+        torch.cuda.empty_cache()
+        copy_gbs = copy_reference(fp, dev)
+        result["copy_reference"] = {"GBps": copy_gbs, "what": "fp_unshard of 16 x 8M bf16 shards "
+                                    "(256 MiB read + 256 MiB written): the plain-copy rate on this GPU",
+                                    "value_over_copy": round(gbs / copy_gbs, 4)}
+        if cfg.shapes is not None:
+            result["pack"] = pack_bench(cfg, dev, 20)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, rank, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -542,10 +542,10 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     a.sync = x.workspace != nullptr ? static_cast<GridSync*>(x.workspace) : nullptr;
 
     uint16_t* own = x.full + (int64_t)x.rank * S;
-    bool aligned = is_aligned8(own);
+    bool aligned = is_aligned8(own), copy_aligned = true;
     for (int32_t q = 0; q < x.world; ++q) {
         aligned = aligned && is_aligned8(x.grads[q]);
-        if (q != x.rank) aligned = aligned && copy_source_aligned(x.shards[q], x.full, S, q);
+        if (q != x.rank) copy_aligned = copy_aligned && copy_source_aligned(x.shards[q], x.full, S, q);
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -556,7 +556,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
 
     if (path == FP_PATH_ONE_PASS) {
         if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-        if ((e = launch_step_coop(a, variant, grid, aligned, s)) != hipSuccess)
+        if ((e = launch_step_coop(a, variant, grid, aligned, copy_aligned, s)) != hipSuccess)
             return device_fail(e, "one-pass step launch");
         if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
         if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, x.sq_norm, s)) != hipSuccess)
@@ -586,7 +586,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     d.partials = a.partials;
     d.sq_norm = x.sq_norm;
     d.n_partials = (int32_t)reduce_groups;
-    if ((e = launch_step_phase1(a, n_groups, no_skip, aligned, s)) != hipSuccess) return device_fail(e, "step launch");
+    if ((e = launch_step_phase1(a, n_groups, no_skip, aligned, copy_aligned, s)) != hipSuccess) return device_fail(e, "step launch");
     if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     if (no_skip) {
         if (x.sq_norm != nullptr &&
@@ -606,13 +606,16 @@ struct fp_units {
     int32_t n = 0, world = 1, rank = 0;
     int device = -1;
     bool has_unshard = false;
-    bool aligned = true;
+    bool aligned = true;        // gradient rows and own slices 8-byte aligned
+    bool copy_aligned = true;   // copy sources 16-byte aligned
     int64_t partition = 0;
     int64_t reduce_groups = 0, copy_groups = 0;
     std::vector<int64_t> shard, offset;
     std::vector<const uint16_t*> grads, shards;  // host copies, for validation
     std::vector<uint16_t*> full;
-    void* dev = nullptr;  // UnitDesc[n] | tile_start[n+1] | copy_start[n+1] | grads[n*w] | shards[n*w]
+    void* dev = nullptr;  // unit records [n], then the per-workgroup unit index [groups]
+    int64_t record_bytes = 0;
+    int32_t tile_run = 0, copy_run = 0;  // equal tile counts of all units but the last, or 0
 };
 
 namespace {
@@ -626,12 +629,6 @@ void free_units(fp_units* u) {
     }
     delete u;
 }
-
-const UnitDesc* units_desc(const fp_units* u) { return static_cast<const UnitDesc*>(u->dev); }
-const int64_t* units_tile_start(const fp_units* u) {
-    return reinterpret_cast<const int64_t*>(units_desc(u) + u->n);
-}
-const int64_t* units_copy_start(const fp_units* u) { return units_tile_start(u) + u->n + 1; }
 
 int64_t units_workspace_bytes(const fp_units* u) { return kWorkspaceHeader + 8 * (u->reduce_groups + 1); }
 
@@ -665,9 +662,12 @@ fp_status check_units_device(const fp_units* u) {
 
 void fill_units_args(const fp_units* u, UnitsArgs* a) {
     std::memset(a, 0, sizeof *a);
-    a->units = units_desc(u);
-    a->tile_start = units_tile_start(u);
-    a->copy_start = units_copy_start(u);
+    a->records = static_cast<const char*>(u->dev);
+    a->unit_of = reinterpret_cast<const int32_t*>(static_cast<const char*>(u->dev) +
+                                                  u->record_bytes * u->n);
+    a->record_bytes = u->record_bytes;
+    a->tile_run = u->tile_run;
+    a->copy_run = u->copy_run;
     a->reduce_groups = u->reduce_groups;
     a->n_units = u->n;
     a->world = u->world;
@@ -728,12 +728,13 @@ extern "C" fp_status fp_units_create(int32_t n_units, int32_t world, int32_t ran
     u->copy_groups = copies;
     u->partition = partition;
 
-    // host image of the device tables
+    // host image of the device tables: unit records, then the unit index of every workgroup
     const size_t n = (size_t)n_units, w = (size_t)world;
-    const size_t desc_b = n * sizeof(UnitDesc), start_b = (n + 1) * sizeof(int64_t);
-    const size_t ptr_b = n * w * sizeof(void*);
-    const size_t total_b = desc_b + 2 * start_b + 2 * ptr_b;
+    u->record_bytes = unit_record_bytes(world);
+    const size_t rec_b = n * (size_t)u->record_bytes;
+    const size_t total_b = rec_b + (size_t)(tiles + copies) * sizeof(int32_t);
     std::vector<unsigned char> img(total_b, 0);
+    int32_t* unit_of = reinterpret_cast<int32_t*>(img.data() + rec_b);
     hipError_t e = hipGetDevice(&u->device);
     if (e == hipSuccess) e = hipMalloc(&u->dev, total_b);
     if (e != hipSuccess) {
@@ -741,44 +742,53 @@ extern "C" fp_status fp_units_create(int32_t n_units, int32_t world, int32_t ran
         free_units(u);
         return device_fail(e, "allocating the units tables");
     }
-    char* base = static_cast<char*>(u->dev);
-    UnitDesc* desc = reinterpret_cast<UnitDesc*>(img.data());
-    int64_t* tile_start = reinterpret_cast<int64_t*>(img.data() + desc_b);
-    int64_t* copy_start = tile_start + n + 1;
-    const uint16_t** gtab = reinterpret_cast<const uint16_t**>(img.data() + desc_b + 2 * start_b);
-    const uint16_t** stab = gtab + n * w;
     int64_t off = 0, t0 = 0, c0 = 0;
-    bool al = true;
+    bool al = true, cal = true;
     for (size_t k = 0; k < n; ++k) {
         const int64_t S = shard[k];
-        UnitDesc& d = desc[k];
-        d.grads = reinterpret_cast<const uint16_t* const*>(base + desc_b + 2 * start_b + k * w * sizeof(void*));
-        d.shards = unshard ? reinterpret_cast<const uint16_t* const*>(base + desc_b + 2 * start_b + ptr_b +
-                                                                      k * w * sizeof(void*))
-                           : nullptr;
-        d.full = unshard ? full[k] : nullptr;
+        unsigned char* rec = img.data() + k * (size_t)u->record_bytes;
+        UnitDesc d;
+        std::memset(&d, 0, sizeof d);
         d.shard = S;
         d.offset = off;
+        d.tile0 = t0;
+        d.copy0 = c0;
+        d.full = unshard ? full[k] : nullptr;
         d.copy_tiles = unshard ? (int32_t)copy_tiles_per_shard(S, kCopyWordsStream) : 0;
+        std::memcpy(rec, &d, sizeof d);
+        const uint16_t** gtab = reinterpret_cast<const uint16_t**>(rec + kUnitHeader);
+        const uint16_t** stab = gtab + w;
         u->offset.push_back(off);
-        tile_start[k] = t0;
-        copy_start[k] = c0;
+        const int64_t nt = unit_tiles(S), nc = unshard ? (int64_t)(world - 1) * d.copy_tiles : 0;
+        for (int64_t i = 0; i < nt; ++i) unit_of[t0 + i] = (int32_t)k;
+        for (int64_t i = 0; i < nc; ++i) unit_of[tiles + c0 + i] = (int32_t)k;
         off += (S + 3) & ~(int64_t)3;
-        t0 += unit_tiles(S);
-        if (unshard) c0 += (int64_t)(world - 1) * d.copy_tiles;
+        t0 += nt;
+        c0 += nc;
         for (size_t q = 0; q < w; ++q) {
-            gtab[k * w + q] = grads[k * w + q];
+            gtab[q] = grads[k * w + q];
             al = al && is_aligned8(grads[k * w + q]);
             if (unshard) {
-                stab[k * w + q] = (int32_t)q == rank ? nullptr : shards[k * w + q];
-                if ((int32_t)q != rank) al = al && copy_source_aligned(shards[k * w + q], full[k], S, (int)q);
+                stab[q] = (int32_t)q == rank ? nullptr : shards[k * w + q];
+                if ((int32_t)q != rank) cal = cal && copy_source_aligned(shards[k * w + q], full[k], S, (int)q);
             }
         }
         if (unshard) al = al && is_aligned8(full[k] + (int64_t)rank * S);
     }
-    tile_start[n] = t0;
-    copy_start[n] = c0;
     u->aligned = al;
+    u->copy_aligned = cal;
+    // equal units (all but the last): the unit of a workgroup is a division
+    {
+        const int64_t t = unit_tiles(shard[0]);
+        const int64_t c = unshard ? (int64_t)(world - 1) * copy_tiles_per_shard(shard[0], kCopyWordsStream) : 0;
+        bool eq_t = true, eq_c = true;
+        for (size_t k = 1; k + 1 < n; ++k) {
+            eq_t = eq_t && unit_tiles(shard[k]) == t;
+            eq_c = eq_c && (unshard ? (int64_t)(world - 1) * copy_tiles_per_shard(shard[k], kCopyWordsStream) : 0) == c;
+        }
+        u->tile_run = eq_t && t <= 0x7FFFFFFF ? (int32_t)t : 0;
+        u->copy_run = eq_c && c > 0 && c <= 0x7FFFFFFF ? (int32_t)c : 0;
+    }
     if ((e = hipMemcpy(u->dev, img.data(), total_b, hipMemcpyHostToDevice)) != hipSuccess) {
         free_units(u);
         return device_fail(e, "uploading the units tables");
@@ -870,7 +880,7 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
         for (int i = 0; i < FP_STEP_EVENTS; ++i) ev[i] = static_cast<hipEvent_t>(x.profile_events[i]);
     hipError_t e;
     if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-    if ((e = launch_units_phase1(a, units->copy_groups, no_skip, units->aligned, s)) != hipSuccess)
+    if ((e = launch_units_phase1(a, units->copy_groups, no_skip, units->aligned, units->copy_aligned, s)) != hipSuccess)
         return device_fail(e, "units step launch");
     if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     if (no_skip) {

@@ -48,26 +48,33 @@ __device__ __forceinline__ uint2 f32x4_to_bf16(const float f[4]) {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
+// Every stream lives in global memory.  Saying so (address space 1) matters
+// for pointers the kernels read from memory (the multi-unit records): the
+// compiler would otherwise emit flat accesses, which also count against the
+// scalar-load counter, so each wait for a pointer would wait for every
+// stream load in flight as well.
+#define FP_GLOBAL __attribute__((address_space(1)))
+
 // Aligned 16-byte load / store with the non-temporal hint: every stream of
 // the step is touched once per step, so it should not displace other data
 // in the caches (measured ~8% faster than plain accesses on cold HBM).
 __device__ __forceinline__ uint4 ld16(const void* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    const u32x4_t v = __builtin_nontemporal_load((const FP_GLOBAL u32x4_t*)(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ void st16(void* p, const uint4 v) {
     const u32x4_t w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    __builtin_nontemporal_store(w, (FP_GLOBAL u32x4_t*)(p));
 }
 
 // 8-byte forms of the above, for bf16 quads.
 __device__ __forceinline__ uint2 ld8(const void* p) {
-    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    const u32x2_t v = __builtin_nontemporal_load((const FP_GLOBAL u32x2_t*)(p));
     return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ void st8(void* p, const uint2 v) {
     const u32x2_t w = {v.x, v.y};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+    __builtin_nontemporal_store(w, (FP_GLOBAL u32x2_t*)(p));
 }
 
 // A bf16 stream read as 8-byte quads from a base on any 2-byte boundary:
@@ -105,12 +112,13 @@ __device__ __forceinline__ uint2 realign8(const Src8& s, const uint2 lo, const u
 __device__ __forceinline__ void store8_any(void* p, const uint2 v) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
     if ((a & 7u) == 0) {
-        *reinterpret_cast<uint2*>(p) = v;
+        const u32x2_t w = {v.x, v.y};
+        *(FP_GLOBAL u32x2_t*)(p) = w;
     } else if ((a & 3u) == 0) {
-        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+        FP_GLOBAL uint32_t* q = (FP_GLOBAL uint32_t*)(p);
         q[0] = v.x; q[1] = v.y;
     } else {
-        uint16_t* q = reinterpret_cast<uint16_t*>(p);
+        FP_GLOBAL uint16_t* q = (FP_GLOBAL uint16_t*)(p);
         q[0] = (uint16_t)v.x; q[1] = (uint16_t)(v.x >> 16);
         q[2] = (uint16_t)v.y; q[3] = (uint16_t)(v.y >> 16);
     }

@@ -154,27 +154,35 @@ struct StepArgs {
     GridSync* sync;          // one-pass: barrier state in the workspace
 };
 
-// One unit of a multi-unit launch (device table entry).  The rank's fp32
-// partition (acc, master, moments) holds unit u at element `offset`, a
-// multiple of 4, so every unit's fp32 shard is 16-byte aligned.
+// One unit of a multi-unit launch: a device record of kUnitHeader bytes
+// (this header) followed by the unit's world gradient row pointers and
+// world shard pointers (entry rank null; all null without unshard), so that
+// a workgroup reaches everything about its unit from one record address.
+// The rank's fp32 partition (acc, master, moments) holds unit u at element
+// `offset`, a multiple of 4, so every unit's fp32 shard is 16-byte aligned.
 struct UnitDesc {
-    const uint16_t* const* grads;   // world device pointers: rank q's bf16 gradient
-    const uint16_t* const* shards;  // world device pointers (entry rank null), or null
-    uint16_t* full;                 // bf16[world * shard], or null
     int64_t shard;
     int64_t offset;
-    int32_t copy_tiles;             // copy workgroups per other shard
-    int32_t pad;
+    int64_t tile0;       // first reduce / AdamW workgroup of the unit
+    int64_t copy0;       // first copy workgroup of the unit, counted from reduce_groups
+    uint16_t* full;      // bf16[world * shard], or null
+    int32_t copy_tiles;  // copy workgroups per other shard
+    int32_t pad[3];
 };
+constexpr int64_t kUnitHeader = 64;
+static_assert(sizeof(UnitDesc) <= kUnitHeader, "unit header exceeds its slot");
+inline int64_t unit_record_bytes(int world) { return kUnitHeader + 16 * (int64_t)world; }
 
-// A launch over all units of a plan.  Workgroup i < reduce_groups takes a
-// reduce / AdamW tile of unit u with tile_start[u] <= i < tile_start[u+1];
-// copy workgroup j (numbered from reduce_groups) takes copy tile
-// j - copy_start[u] of unit u with copy_start[u] <= j < copy_start[u+1].
+// A launch over all units of a plan.  Workgroup i (reduce / AdamW tiles
+// first, then copy tiles) belongs to unit u(i), whose record sits at
+// records + u(i) * record_bytes.  When every unit but the last has the same
+// number of reduce tiles (and of copy tiles) -- equal DDP buckets -- u(i)
+// is computed (tile_run / copy_run > 0); otherwise it is read from unit_of.
 struct UnitsArgs {
-    const UnitDesc* units;
-    const int64_t* tile_start;   // [n_units + 1]
-    const int64_t* copy_start;   // [n_units + 1]
+    const char* records;
+    const int32_t* unit_of;      // [reduce_groups + copy_groups]
+    int32_t tile_run;            // reduce tiles of each unit but the last, or 0
+    int32_t copy_run;            // copy tiles of each unit but the last, or 0
     float* acc;
     float* master;
     float* exp_avg;
@@ -183,7 +191,8 @@ struct UnitsArgs {
     double* partials;
     double* sq_norm;             // AdamW launch: finalised by workgroup 0
     AdamCoef c;
-    int64_t reduce_groups;       // tile_start[n_units]
+    int64_t reduce_groups;
+    int64_t record_bytes;
     float scale;
     int32_t n_units;
     int32_t world;
@@ -191,6 +200,10 @@ struct UnitsArgs {
     int32_t accumulate;
     int32_t keep_grad;
 };
+
+// Ranks reduced per group of loads in flight: 16 when more than 8 ranks
+// contribute (one round trip for up to 16 ranks), else 8.
+inline bool wide_group(int world) { return world > 8; }
 
 // Reduce / AdamW workgroups of one unit: at least one, so that its tail
 // elements and flag have an owner.
@@ -211,19 +224,21 @@ struct PackArgs {
 
 // Launchers (return the HIP error of the launch).
 // `aligned`: every bf16 quad stream of the launch (gradients, own shard) is
-// 8-byte aligned and every copy source is 16-byte aligned at the words the
-// kernel reads (then no realignment code runs).
+// 8-byte aligned; `copy_aligned` (and `aligned` for fp_unshard's kernel):
+// every copy source is 16-byte aligned at the words the kernel reads.  Then
+// no realignment code runs for those streams.
 hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hipStream_t s);
 hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool aligned,
-                              hipStream_t s);
+                              bool copy_aligned, hipStream_t s);
 // One-pass exact-skip step: plan_step_coop picks the variant (lanes keep
 // 2 or 4 quads in registers) and a grid that fits the device's co-resident
 // capacity, or sets *variant = -1 when the shard is too large.
 hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
-hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, hipStream_t s);
+hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, bool copy_aligned,
+                            hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
 // Multi-unit launches: one micro-batch's reduce over all units; the last
 // micro-batch's reduce (+ AdamW when fused) with the copies of all units'
@@ -231,7 +246,7 @@ hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipSt
 // all units.
 hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s);
 hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update,
-                               bool aligned, hipStream_t s);
+                               bool aligned, bool copy_aligned, hipStream_t s);
 hipError_t launch_units_adamw(const UnitsArgs& a, bool aligned, hipStream_t s);
 
 }  // namespace fpk

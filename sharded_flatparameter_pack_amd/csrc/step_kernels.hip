@@ -16,10 +16,10 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* p
 
 // ---------------------------------------------------------------- kernels
 
-template <bool kAligned, bool kAccumulate, bool kNorm>
+template <bool kAligned, bool kAccumulate, bool kNorm, int kG>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceArgs a) {
-    reduce_tile<kAligned, kAccumulate, kNorm>(a, blockIdx.x, a.found_inf,
-                                              kNorm ? a.partials + blockIdx.x : nullptr);
+    reduce_tile<kAligned, kAccumulate, kNorm, kG>(a, blockIdx.x, a.found_inf,
+                                                  kNorm ? a.partials + blockIdx.x : nullptr);
 }
 
 template <bool kAligned>
@@ -42,13 +42,13 @@ __global__ __launch_bounds__(kThreads) void unshard_kernel(const UnshardArgs a) 
 // step (kFused = true).  Workgroups [0, reduce_groups) take reduce tiles;
 // the others take (shard, tile) pairs of the copy of the other ranks'
 // shards into `full`.
-template <bool kAligned, bool kFused>
+template <bool kAligned, bool kCopyAligned, bool kFused, int kG>
 __global__ __launch_bounds__(kThreads) void step_phase1_kernel(const StepArgs a) {
     if (blockIdx.x >= (unsigned)a.reduce_groups) {
-        copy_role<kAligned, kCopyWordsStream>(a, blockIdx.x - (unsigned)a.reduce_groups);
+        copy_role<kCopyAligned, kCopyWordsStream>(a, blockIdx.x - (unsigned)a.reduce_groups);
         return;
     }
-    step_reduce_tile<kAligned, kFused>(a, blockIdx.x, a.accumulate != 0, a.keep_grad != 0,
+    step_reduce_tile<kAligned, kFused, kG>(a, blockIdx.x, a.accumulate != 0, a.keep_grad != 0,
                                        a.full + (int64_t)a.rank * a.shard, a.found_inf,
                                        a.partials != nullptr ? a.partials + blockIdx.x : nullptr);
 }
@@ -65,11 +65,11 @@ __global__ __launch_bounds__(kThreads) void step_phase1_kernel(const StepArgs a)
 // ranks' shards meanwhile and take no part in the barrier.  The reduced
 // gradient never leaves the registers, so the step moves exactly the
 // algorithmic bytes.
-template <bool kAligned, int kQ>
+template <bool kAligned, bool kCopyAligned, int kQ>
 __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     FP_PHASE_MARK(0);
     if (blockIdx.x >= (unsigned)a.reduce_groups) {
-        copy_role<kAligned, kCopyWordsCoop>(a, blockIdx.x - (unsigned)a.reduce_groups);
+        copy_role<kCopyAligned, kCopyWordsCoop>(a, blockIdx.x - (unsigned)a.reduce_groups);
         FP_PHASE_MARK(5);
         return;
     }
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     if (nq > 0) {
         load_state<kQ>(a, Q, st);
         float y[kQ][4];
-        reduce_quads<kAligned, false, kQ>(a, Q, acc_in, y);
+        reduce_quads<kAligned, false, 8, kQ>(a, Q, acc_in, y);
 #pragma unroll
         for (int u = 0; u < kQ; ++u) {
             old_bf16[u] = f32x4_to_bf16(st.th[u]);
@@ -166,10 +166,16 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
 
 // ---------------------------------------------------------------- launchers
 
+template <bool kAligned, bool kAcc, bool kNorm>
+void reduce_launch(const ReduceArgs& a, dim3 g, bool wide, hipStream_t s) {
+    if (wide) reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, 0, s>>>(a);
+    else reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, 0, s>>>(a);
+}
+
 hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStream_t s) {
-    const bool norm = a.partials != nullptr, acc = a.accumulate != 0;
+    const bool norm = a.partials != nullptr, acc = a.accumulate != 0, wide = wide_group(a.world);
     const dim3 g((unsigned)grid);
-#define FP_REDUCE(AL, AC, NO) reduce_kernel<AL, AC, NO><<<g, kThreads, 0, s>>>(a)
+#define FP_REDUCE(AL, AC, NO) reduce_launch<AL, AC, NO>(a, g, wide, s)
     if (aligned) {
         if (acc) { if (norm) FP_REDUCE(true, true, true); else FP_REDUCE(true, true, false); }
         else { if (norm) FP_REDUCE(true, false, true); else FP_REDUCE(true, false, false); }
@@ -199,15 +205,29 @@ hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hi
     return hipGetLastError();
 }
 
+namespace {
+template <bool kAligned, bool kCopyAligned, bool kFused>
+void phase1_launch(const StepArgs& a, dim3 g, hipStream_t s) {
+    if (wide_group(a.world)) step_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, 0, s>>>(a);
+    else step_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, 0, s>>>(a);
+}
+
+template <bool kAligned, bool kCopyAligned>
+void phase1_launch(const StepArgs& a, dim3 g, bool fused, hipStream_t s) {
+    if (fused) phase1_launch<kAligned, kCopyAligned, true>(a, g, s);
+    else phase1_launch<kAligned, kCopyAligned, false>(a, g, s);
+}
+}  // namespace
+
 hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool aligned,
-                              hipStream_t s) {
+                              bool copy_aligned, hipStream_t s) {
     const dim3 g((unsigned)grid);
     if (aligned) {
-        if (fused_update) step_phase1_kernel<true, true><<<g, kThreads, 0, s>>>(a);
-        else step_phase1_kernel<true, false><<<g, kThreads, 0, s>>>(a);
+        if (copy_aligned) phase1_launch<true, true>(a, g, fused_update, s);
+        else phase1_launch<true, false>(a, g, fused_update, s);
     } else {
-        if (fused_update) step_phase1_kernel<false, true><<<g, kThreads, 0, s>>>(a);
-        else step_phase1_kernel<false, false><<<g, kThreads, 0, s>>>(a);
+        if (copy_aligned) phase1_launch<false, true>(a, g, fused_update, s);
+        else phase1_launch<false, false>(a, g, fused_update, s);
     }
     return hipGetLastError();
 }
@@ -226,12 +246,19 @@ struct CoopLimits {
 };
 CoopLimits g_limits[kMaxDevices];
 
-const void* coop_fn(int variant, bool aligned) {
-    if (aligned)
-        return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<true, 2>)
-                            : reinterpret_cast<const void*>(&step_coop_kernel<true, kMaxCoopQuads>);
-    return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<false, 2>)
-                        : reinterpret_cast<const void*>(&step_coop_kernel<false, kMaxCoopQuads>);
+template <bool kAligned, bool kCopyAligned>
+const void* coop_fn(int variant) {
+    return variant == 0 ? reinterpret_cast<const void*>(&step_coop_kernel<kAligned, kCopyAligned, 2>)
+                        : reinterpret_cast<const void*>(&step_coop_kernel<kAligned, kCopyAligned, kMaxCoopQuads>);
+}
+
+const void* coop_fn(int variant, int form) {
+    switch (form) {
+        case 0: return coop_fn<true, true>(variant);
+        case 1: return coop_fn<true, false>(variant);
+        case 2: return coop_fn<false, true>(variant);
+        default: return coop_fn<false, false>(variant);
+    }
 }
 
 hipError_t coop_limits(int dev, const CoopLimits** out) {
@@ -244,11 +271,13 @@ hipError_t coop_limits(int dev, const CoopLimits** out) {
         if (state == 0 && L.state.compare_exchange_strong(expect, 1)) {
             hipError_t e = hipDeviceGetAttribute(&L.cus, hipDeviceAttributeMultiprocessorCount, dev);
             for (int i = 0; i < kVariants && e == hipSuccess; ++i) {
-                int a = 0, b = 0;
-                e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, coop_fn(i, true), kThreads, 0);
-                if (e == hipSuccess)
-                    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, coop_fn(i, false), kThreads, 0);
-                L.per_cu[i] = a < b ? a : b;
+                int lo = 1 << 30;
+                for (int form = 0; form < 4 && e == hipSuccess; ++form) {
+                    int b = 0;
+                    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, coop_fn(i, form), kThreads, 0);
+                    lo = b < lo ? b : lo;
+                }
+                L.per_cu[i] = lo;
             }
             L.state.store(e == hipSuccess ? 2 : 0, std::memory_order_release);
             if (e != hipSuccess) return e;
@@ -279,7 +308,8 @@ hipError_t plan_step_coop(int64_t shard, int* variant, int* grid) {
     return hipSuccess;
 }
 
-hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, hipStream_t s) {
+hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, bool copy_aligned,
+                            hipStream_t s) {
     // A plain launch (a cooperative launch costs ~17 us more per launch on
     // MI355X).  The barrier workgroups [0, reduce_groups) fit the device's
     // resident capacity and are dispatched before the copy workgroups, which
@@ -289,13 +319,19 @@ hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool align
     b.reduce_groups = grid;
     b.copy_tiles = (int32_t)copy_tiles_per_shard(a.shard, kCopyWordsCoop);
     const dim3 g((unsigned)((int64_t)grid + (int64_t)(a.world - 1) * b.copy_tiles));
+#define FP_COOP(AL, CA)                                                          \
+    do {                                                                         \
+        if (variant == 0) step_coop_kernel<AL, CA, 2><<<g, kThreads, 0, s>>>(b);    \
+        else step_coop_kernel<AL, CA, kMaxCoopQuads><<<g, kThreads, 0, s>>>(b);     \
+    } while (0)
     if (aligned) {
-        if (variant == 0) step_coop_kernel<true, 2><<<g, kThreads, 0, s>>>(b);
-        else step_coop_kernel<true, kMaxCoopQuads><<<g, kThreads, 0, s>>>(b);
+        if (copy_aligned) FP_COOP(true, true);
+        else FP_COOP(true, false);
     } else {
-        if (variant == 0) step_coop_kernel<false, 2><<<g, kThreads, 0, s>>>(b);
-        else step_coop_kernel<false, kMaxCoopQuads><<<g, kThreads, 0, s>>>(b);
+        if (copy_aligned) FP_COOP(false, true);
+        else FP_COOP(false, false);
     }
+#undef FP_COOP
     return hipGetLastError();
 }
 

@@ -126,23 +126,30 @@ __device__ __forceinline__ uint4 ld_bf16_word(const uint16_t* base, int64_t word
 
 // ---------------------------------------------------------------- reduce
 // Ascending-rank fp32 sum of the ranks' bf16 gradients at the lane's kU
-// quads.  The loads of up to 8 ranks are issued before any add.  "Infra:
+// quads, in groups of kG ranks: the loads of a group are all issued before
+// its adds, so a group costs one memory round trip (kG = 16 for large
+// groups of ranks, at the price of the registers that hold them).  "Infra:
 // Data Parallel", ZeRO-1/ZeRO-2 paragraphs (reduce-scatter with averaging);
 // "4.1 数据并行详解" section 2 (average of the local gradients).
-template <bool kAligned, int kU, class A>
+template <bool kAligned, int kG, int kU, class A>
 __device__ __forceinline__ void sum_ranks(const A& a, const Quads<kU>& Q, float s[kU][4]) {
     const int world = a.world;
-    for (int q0 = 0; q0 < world; q0 += 8) {
-        uint2 w[8][kU];
+    for (int q0 = 0; q0 < world; q0 += kG) {
+        // Every slot of the group loads (slots past the last rank repeat the
+        // last rank's row, a cache hit, and are not added), so that the row
+        // pointers' scalar loads and then the stream loads issue back to back
+        // without a branch between them.
+        const uint16_t* row[kG];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (q0 + k < world) {
+        for (int k = 0; k < kG; ++k) row[k] = a.grads[q0 + k < world ? q0 + k : world - 1];
+        uint2 w[kG][kU];
 #pragma unroll
-                for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(a.grads[q0 + k], Q, u);
-            }
+        for (int k = 0; k < kG; ++k) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(row[k], Q, u);
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < kG; ++k) {
             if (q0 + k < world) {
 #pragma unroll
                 for (int u = 0; u < kU; ++u) {
@@ -172,7 +179,7 @@ __device__ __forceinline__ float sum_ranks1(const A& a, int64_t j) {
 // kAccFirst the accumulator is loaded before the gradients, so that its
 // load is in flight with theirs (at the cost of holding it across the sum);
 // without it, after the sum.
-template <bool kAligned, bool kAccFirst, int kU, class A>
+template <bool kAligned, bool kAccFirst, int kG, int kU, class A>
 __device__ __forceinline__ void reduce_quads(const A& a, const Quads<kU>& Q, bool accumulate,
                                              float y[kU][4]) {
     float p[kU][4];
@@ -180,7 +187,7 @@ __device__ __forceinline__ void reduce_quads(const A& a, const Quads<kU>& Q, boo
 #pragma unroll
         for (int u = 0; u < kU; ++u) ld_f32q(a.acc, Q, u, p[u]);
     }
-    sum_ranks<kAligned, kU>(a, Q, y);
+    sum_ranks<kAligned, kG, kU>(a, Q, y);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
 #pragma unroll
@@ -422,7 +429,7 @@ __device__ __forceinline__ void finalize_norm(const double* partials, int n, dou
 // Reduce tile `tile` of one micro-batch into acc, with the overflow check
 // (flag OR-ed into found_inf) and, with kNorm, the tile's sum of squares
 // written to *partial by thread 0.
-template <bool kAligned, bool kAccumulate, bool kNorm, class A>
+template <bool kAligned, bool kAccumulate, bool kNorm, int kG, class A>
 __device__ __forceinline__ void reduce_tile(const A& a, int64_t tile, int32_t* found_inf,
                                             double* partial) {
     constexpr int kU = kQuadsPerLane;
@@ -432,7 +439,7 @@ __device__ __forceinline__ void reduce_tile(const A& a, int64_t tile, int32_t* f
     if (nq > 0) {
         const Quads<kU> Q = lane_quads<kU>(tile, nq);
         float y[kU][4];
-        reduce_quads<kAligned, true, kU>(a, Q, kAccumulate, y);
+        reduce_quads<kAligned, true, kG, kU>(a, Q, kAccumulate, y);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             if (!Q.ok[u]) continue;
@@ -502,7 +509,7 @@ __device__ __forceinline__ void copy_role(const A& a, unsigned idx) {
 // overflow flag of the whole step is known; kFused = true also runs AdamW
 // and the cast to `own` in the same pass (no gate).  keep_grad: with
 // kFused, also leave the reduced gradient in acc.
-template <bool kAligned, bool kFused, class A>
+template <bool kAligned, bool kFused, int kG, class A>
 __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool accumulate,
                                                  bool keep_grad, uint16_t* own, int32_t* found_inf,
                                                  double* partial) {
@@ -516,7 +523,7 @@ __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool 
         State<kU> st;
         if (kFused) load_state<kU>(a, Q, st);
         float y[kU][4];
-        reduce_quads<kAligned, true, kU>(a, Q, accumulate, y);
+        reduce_quads<kAligned, true, kG, kU>(a, Q, accumulate, y);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             if (!Q.ok[u]) continue;

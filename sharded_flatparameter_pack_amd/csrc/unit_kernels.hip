@@ -3,27 +3,15 @@
 // partition ("Infra: Data Parallel", ZeRO-1/ZeRO-2 paragraphs: each rank
 // keeps one slice of the whole optimizer state; "4.1 数据并行详解",
 // section 4.2: gradients are reduced bucket by bucket).  Each workgroup
-// finds its unit by a binary search over the plan's tile prefix table
-// (scalar loads, cached), then runs the same tile bodies as the single-unit
-// kernels on that unit's pointers.
+// finds its unit (by a division for equal units, else from the plan's
+// per-workgroup table), reads the unit's record (header and rank pointers),
+// and runs the same tile bodies as the single-unit kernels on that unit.
 
 #include "step_ops.h"
 
 namespace fpk {
 
 namespace {
-
-// The unit whose workgroup range holds idx: the last u with
-// start[u] <= idx (start ascending, start[0] = 0, idx < start[n]).
-__device__ __forceinline__ int find_unit(const int64_t* start, int n, int64_t idx) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (start[mid] <= idx) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
 
 // One unit as the tile bodies see it.
 struct UnitView {
@@ -35,6 +23,8 @@ struct UnitView {
     float* exp_avg;
     float* exp_avg_sq;
     int64_t shard;
+    int64_t tile0;
+    int64_t copy0;
     AdamCoef c;
     float scale;
     int32_t world;
@@ -42,17 +32,34 @@ struct UnitView {
     int32_t copy_tiles;
 };
 
-__device__ __forceinline__ UnitView unit_view(const UnitsArgs& a, int u) {
-    const UnitDesc& d = a.units[u];
+// The unit of workgroup `group`: arithmetic for equal units, else the
+// per-workgroup table (one more dependent load before the unit's record).
+__device__ __forceinline__ int unit_of_group(const UnitsArgs& a, int64_t group) {
+    const bool copy = group >= a.reduce_groups;
+    const uint32_t run = (uint32_t)(copy ? a.copy_run : a.tile_run);
+    if (run != 0) {
+        const uint32_t i = (uint32_t)(copy ? group - a.reduce_groups : group);
+        const uint32_t u = i / run;
+        return u < (uint32_t)a.n_units ? (int)u : a.n_units - 1;
+    }
+    return a.unit_of[group];
+}
+
+__device__ __forceinline__ UnitView unit_view(const UnitsArgs& a, int64_t group) {
+    const int u = unit_of_group(a, group);
+    const char* rec = a.records + (int64_t)u * a.record_bytes;
+    const UnitDesc& d = *reinterpret_cast<const UnitDesc*>(rec);
     UnitView v;
-    v.grads = d.grads;
-    v.shards = d.shards;
+    v.grads = reinterpret_cast<const uint16_t* const*>(rec + kUnitHeader);
+    v.shards = v.grads + a.world;
     v.full = d.full;
     v.acc = a.acc + d.offset;
     v.master = a.master + d.offset;
     v.exp_avg = a.exp_avg + d.offset;
     v.exp_avg_sq = a.exp_avg_sq + d.offset;
     v.shard = d.shard;
+    v.tile0 = d.tile0;
+    v.copy0 = d.copy0;
     v.c = a.c;
     v.scale = a.scale;
     v.world = a.world;
@@ -67,43 +74,57 @@ __device__ __forceinline__ uint16_t* own_slice(const UnitView& v) {
 
 }  // namespace
 
-template <bool kAligned, bool kAccumulate, bool kNorm>
+template <bool kAligned, bool kAccumulate, bool kNorm, int kG>
 __global__ __launch_bounds__(kThreads) void units_reduce_kernel(const UnitsArgs a) {
-    const int u = find_unit(a.tile_start, a.n_units, blockIdx.x);
-    const UnitView v = unit_view(a, u);
-    reduce_tile<kAligned, kAccumulate, kNorm>(v, (int64_t)blockIdx.x - a.tile_start[u], a.found_inf,
-                                              kNorm ? a.partials + blockIdx.x : nullptr);
+    const UnitView v = unit_view(a, blockIdx.x);
+    reduce_tile<kAligned, kAccumulate, kNorm, kG>(v, (int64_t)blockIdx.x - v.tile0, a.found_inf,
+                                                  kNorm ? a.partials + blockIdx.x : nullptr);
 }
 
-template <bool kAligned, bool kFused>
+template <bool kAligned, bool kCopyAligned, bool kFused, int kG>
 __global__ __launch_bounds__(kThreads) void units_phase1_kernel(const UnitsArgs a) {
+    const UnitView v = unit_view(a, blockIdx.x);
     if ((int64_t)blockIdx.x >= a.reduce_groups) {
-        const int64_t idx = (int64_t)blockIdx.x - a.reduce_groups;
-        const int u = find_unit(a.copy_start, a.n_units, idx);
-        const UnitView v = unit_view(a, u);
-        copy_role<kAligned, kCopyWordsStream>(v, (unsigned)(idx - a.copy_start[u]));
+        copy_role<kCopyAligned, kCopyWordsStream>(v, (unsigned)((int64_t)blockIdx.x - a.reduce_groups - v.copy0));
         return;
     }
-    const int u = find_unit(a.tile_start, a.n_units, blockIdx.x);
-    const UnitView v = unit_view(a, u);
-    step_reduce_tile<kAligned, kFused>(v, (int64_t)blockIdx.x - a.tile_start[u], a.accumulate != 0,
-                                       a.keep_grad != 0, own_slice(v), a.found_inf,
-                                       a.partials != nullptr ? a.partials + blockIdx.x : nullptr);
+    step_reduce_tile<kAligned, kFused, kG>(v, (int64_t)blockIdx.x - v.tile0, a.accumulate != 0,
+                                           a.keep_grad != 0, own_slice(v), a.found_inf,
+                                           a.partials != nullptr ? a.partials + blockIdx.x : nullptr);
 }
 
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void units_adamw_kernel(const UnitsArgs a) {
     if (a.sq_norm != nullptr && blockIdx.x == 0)
         finalize_norm(a.partials, (int)a.reduce_groups, a.sq_norm);
-    const int u = find_unit(a.tile_start, a.n_units, blockIdx.x);
-    const UnitView v = unit_view(a, u);
-    adamw_tile<kAligned>(v, v.acc, (int64_t)blockIdx.x - a.tile_start[u], a.found_inf, own_slice(v));
+    const UnitView v = unit_view(a, blockIdx.x);
+    adamw_tile<kAligned>(v, v.acc, (int64_t)blockIdx.x - v.tile0, a.found_inf, own_slice(v));
 }
+
+namespace {
+template <bool kAligned, bool kAcc, bool kNorm>
+void units_reduce_launch(const UnitsArgs& a, dim3 g, hipStream_t s) {
+    if (wide_group(a.world)) units_reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, 0, s>>>(a);
+    else units_reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, 0, s>>>(a);
+}
+
+template <bool kAligned, bool kCopyAligned, bool kFused>
+void units_phase1_launch(const UnitsArgs& a, dim3 g, hipStream_t s) {
+    if (wide_group(a.world)) units_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, 0, s>>>(a);
+    else units_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, 0, s>>>(a);
+}
+
+template <bool kAligned, bool kCopyAligned>
+void units_phase1_launch(const UnitsArgs& a, dim3 g, bool fused, hipStream_t s) {
+    if (fused) units_phase1_launch<kAligned, kCopyAligned, true>(a, g, s);
+    else units_phase1_launch<kAligned, kCopyAligned, false>(a, g, s);
+}
+}  // namespace
 
 hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s) {
     const bool norm = a.partials != nullptr, acc = a.accumulate != 0;
     const dim3 g((unsigned)a.reduce_groups);
-#define FP_UREDUCE(AL, AC, NO) units_reduce_kernel<AL, AC, NO><<<g, kThreads, 0, s>>>(a)
+#define FP_UREDUCE(AL, AC, NO) units_reduce_launch<AL, AC, NO>(a, g, s)
     if (aligned) {
         if (acc) { if (norm) FP_UREDUCE(true, true, true); else FP_UREDUCE(true, true, false); }
         else { if (norm) FP_UREDUCE(true, false, true); else FP_UREDUCE(true, false, false); }
@@ -116,14 +137,14 @@ hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s) 
 }
 
 hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update,
-                               bool aligned, hipStream_t s) {
+                               bool aligned, bool copy_aligned, hipStream_t s) {
     const dim3 g((unsigned)(a.reduce_groups + copy_groups));
     if (aligned) {
-        if (fused_update) units_phase1_kernel<true, true><<<g, kThreads, 0, s>>>(a);
-        else units_phase1_kernel<true, false><<<g, kThreads, 0, s>>>(a);
+        if (copy_aligned) units_phase1_launch<true, true>(a, g, fused_update, s);
+        else units_phase1_launch<true, false>(a, g, fused_update, s);
     } else {
-        if (fused_update) units_phase1_kernel<false, true><<<g, kThreads, 0, s>>>(a);
-        else units_phase1_kernel<false, false><<<g, kThreads, 0, s>>>(a);
+        if (copy_aligned) units_phase1_launch<false, true>(a, g, fused_update, s);
+        else units_phase1_launch<false, false>(a, g, fused_update, s);
     }
     return hipGetLastError();
 }

@@ -174,3 +174,11 @@ def test_units_equal_single_unit_steps(fp):
         assert torch.equal(plan.unit_slice(v, u).view(torch.int32), v1.view(torch.int32))
         assert torch.equal(full_a[u], full_b[u])
     plan.close()
+
+
+@pytest.mark.parametrize("tail", [7_000, 20_480, 45_001])
+def test_units_equal_buckets_with_a_tail(fp, tail):
+    """Equal buckets plus a last one that is shorter, equal or longer (the
+    workgroup-to-unit mapping by division), at 16 ranks and 4 micro-batches."""
+    say(f"units equal buckets tail={tail}")
+    _units_case(fp, [20_480] * 5 + [tail], world=16, rank=0, n_micro=4, step=2, seed=21, flags=0)
