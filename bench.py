@@ -109,12 +109,15 @@ class SingleUnit:
         per_set = S * (2 * world + 16 + 2 * (world - 1) + 2 * world)
         self.n_sets = max(2, math.ceil(ROTATE_BYTES / per_set))
         self.sets = []
+        # each simulated rank's rows start 16-byte aligned, as separate per-rank
+        # buffers would (row stride rounded up to 8 elements)
+        Sp = -(-S // 8) * 8
         for k in range(self.n_sets):
             key = lambda stream, q=0: (stream, k, 0, q)  # noqa: E731
-            grads = gen.torch_bf16_normal(world * S, cfg.grad_sigma, cfg.seed, key(gen.STREAM_GRAD), dev)
-            others = gen.torch_bf16_normal(world * S, cfg.master_sigma, cfg.seed, key(gen.STREAM_SHARD), dev)
-            s = dict(grads=grads.view(world, S),
-                     shards=[None if q == rank else others[q * S:(q + 1) * S] for q in range(world)],
+            grads = gen.torch_bf16_normal(world * Sp, cfg.grad_sigma, cfg.seed, key(gen.STREAM_GRAD), dev)
+            others = gen.torch_bf16_normal(world * Sp, cfg.master_sigma, cfg.seed, key(gen.STREAM_SHARD), dev)
+            s = dict(grads=grads.view(world, Sp)[:, :S],
+                     shards=[None if q == rank else others[q * Sp:q * Sp + S] for q in range(world)],
                      master=gen.torch_normal_f32(S, cfg.master_sigma, cfg.seed, key(gen.STREAM_MASTER), dev),
                      exp_avg=torch.zeros(S, dtype=torch.float32, device=dev),
                      exp_avg_sq=torch.zeros(S, dtype=torch.float32, device=dev),

@@ -151,10 +151,9 @@ __device__ __forceinline__ uint32_t pick(uint32_t i, uint32_t a0, uint32_t a1, u
     return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
 }
 
-// Word `word` (16 bytes at byte offset 16 * word from the base).
-__device__ __forceinline__ uint4 ld16_realign(const Src16& s, int64_t word) {
-    const uint4 lo = ld16(s.abase + word);
-    const uint4 hi = ld16(s.abase + word + s.step);
+// The 16 wanted bytes from the aligned words lo (holding the first wanted
+// byte) and hi (the next word, or lo again when the base is aligned).
+__device__ __forceinline__ uint4 realign16(const Src16& s, const uint4 lo, const uint4 hi) {
     const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     const uint32_t d = s.ds;
     const uint32_t w0 = pick(d, w[0], w[1], w[2], w[3]);
@@ -164,6 +163,22 @@ __device__ __forceinline__ uint4 ld16_realign(const Src16& s, int64_t word) {
     const uint32_t w4 = pick(d, w[4], w[5], w[6], w[7]);
     return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, s.bs), __builtin_amdgcn_alignbyte(w2, w1, s.bs),
                       __builtin_amdgcn_alignbyte(w3, w2, s.bs), __builtin_amdgcn_alignbyte(w4, w3, s.bs));
+}
+
+// Word `word` (16 bytes at byte offset 16 * word from the base).
+__device__ __forceinline__ uint4 ld16_realign(const Src16& s, int64_t word) {
+    return realign16(s, ld16(s.abase + word), ld16(s.abase + word + s.step));
+}
+
+// The value of the next lane of the wave (lane i receives lane i + 1's;
+// lane 63 receives `fallback`): a wave-shift DPP move, no memory access.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v, uint32_t fallback) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fallback, (int)v, 0x130 /* wave_shl:1 */, 0xF,
+                                                 0xF, false);
+}
+__device__ __forceinline__ uint4 from_next_lane(const uint4 v, const uint4 fallback) {
+    return make_uint4(from_next_lane(v.x, fallback.x), from_next_lane(v.y, fallback.y),
+                      from_next_lane(v.z, fallback.z), from_next_lane(v.w, fallback.w));
 }
 
 // 16 bytes starting at any 2-byte-aligned address.  A misaligned address is

@@ -78,11 +78,13 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     const bool want_sq = a.partials != nullptr;
     const bool acc_in = a.accumulate != 0;
     uint16_t* own = a.full + (int64_t)a.rank * a.shard;
+    // Thread 0 takes the barrier ticket and reads the flag left by earlier
+    // kernels (measured faster than having every lane read them).
     BarrierTicket ticket = {0u, 0u};
-    unsigned prior = 0u;
+    int32_t prior = 0;
     if (threadIdx.x == 0) {
         ticket = grid_ticket(a.sync);
-        prior = *a.found_inf != 0 ? 1u : 0u;   // written by earlier kernels
+        prior = *a.found_inf;
     }
 
     // reduce and speculative update, all in registers
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     }
     FP_PHASE_MARK(2);
     if (threadIdx.x == 0) {
-        grid_arrive(a.sync, ticket, (group_bad || prior) ? 1u : 0u, (unsigned)a.reduce_groups);
+        grid_arrive(a.sync, ticket, (group_bad || prior != 0) ? 1u : 0u, (unsigned)a.reduce_groups);
         FP_PHASE_MARK(3);
         s_skip = grid_wait(a.sync, ticket);
     }

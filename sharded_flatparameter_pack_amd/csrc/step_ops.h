@@ -135,18 +135,13 @@ template <bool kAligned, int kG, int kU, class A>
 __device__ __forceinline__ void sum_ranks(const A& a, const Quads<kU>& Q, float s[kU][4]) {
     const int world = a.world;
     for (int q0 = 0; q0 < world; q0 += kG) {
-        // Every slot of the group loads (slots past the last rank repeat the
-        // last rank's row, a cache hit, and are not added), so that the row
-        // pointers' scalar loads and then the stream loads issue back to back
-        // without a branch between them.
-        const uint16_t* row[kG];
-#pragma unroll
-        for (int k = 0; k < kG; ++k) row[k] = a.grads[q0 + k < world ? q0 + k : world - 1];
         uint2 w[kG][kU];
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
+            if (q0 + k < world) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(row[k], Q, u);
+                for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(a.grads[q0 + k], Q, u);
+            }
         }
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
@@ -319,8 +314,25 @@ __device__ __forceinline__ void copy_tile(const uint16_t* src, uint16_t* full, c
     const int64_t w0 = tile * kTile + threadIdx.x;
     if ((tile + 1) * kTile <= n_words) {
         uint4 v[kWords];
+        if (kAligned) {
 #pragma unroll
-        for (int u = 0; u < kWords; ++u) v[u] = ld_bf16_word<kAligned>(from, w0 + u * kThreads);
+            for (int u = 0; u < kWords; ++u) v[u] = ld16(from + ((w0 + u * kThreads) << 3));
+        } else {
+            // Realignment takes the word after each lane's own from the next
+            // lane (the lanes of a wave hold consecutive words); only the
+            // wave's last lane loads that word itself.  One load per word
+            // instead of two.
+            const Src16 s = src16(from);
+            uint4 hi[kWords] = {};
+#pragma unroll
+            for (int u = 0; u < kWords; ++u) v[u] = ld16(s.abase + w0 + u * kThreads);
+            if ((threadIdx.x & 63) == 63) {
+#pragma unroll
+                for (int u = 0; u < kWords; ++u) hi[u] = ld16(s.abase + w0 + u * kThreads + s.step);
+            }
+#pragma unroll
+            for (int u = 0; u < kWords; ++u) v[u] = realign16(s, v[u], from_next_lane(v[u], hi[u]));
+        }
 #pragma unroll
         for (int u = 0; u < kWords; ++u) st16(to + ((w0 + u * kThreads) << 3), v[u]);
     } else {
