@@ -136,6 +136,13 @@ class Plan:
 
     def pack(self, tensors, flat=None):
         """FlatParameter of `tensors` (one 2- or 4-byte dtype) on the GPU."""
+        return self.packer(tensors, flat)()
+
+    def packer(self, tensors, flat=None):
+        """A callable that packs `tensors` into `flat` (allocated here when
+        None) and returns it, with the tensors checked and their pointers
+        marshalled once -- for repeated packs of the same buffers.  The
+        caller keeps the tensors alive and in place."""
         torch = _torch()
         if len(tensors) != len(self.shapes):
             raise ValueError("tensor count differs from the plan")
@@ -148,9 +155,14 @@ class Plan:
             ptrs.append(_dev_ptr(t, (dtype,), math.prod(s), f"tensors[{i}]") if t.numel() else None)
         if flat is None:
             flat = torch.empty(self.padded, dtype=dtype, device=tensors[0].device)
-        fptr = _dev_ptr(flat, (dtype,), self.padded, "flat")
-        check(lib().fp_pack(self._h, esize, _ptr_table(ptrs), C.c_void_p(fptr), _stream(flat)))
-        return flat
+        fptr = C.c_void_p(_dev_ptr(flat, (dtype,), self.padded, "flat"))
+        table = _ptr_table(ptrs)
+        fn, h = lib().fp_pack, self._h
+
+        def run():
+            check(fn(h, esize, table, fptr, _stream(flat)))
+            return flat
+        return run
 
     def views(self, buf, rank: int = -1):
         """Views of the original tensors on `buf` (aliasing, no copy).
