@@ -48,6 +48,9 @@ def lib():
                                     _vp, _vp, _vp, _vp, _i32]),
                 "or_unshard": (None, [_i64, _i32, _vp, _vp]),
                 "or_state_bytes": (_f64, [_f64, _i32, _f64, _i32]),
+                "or_shard0_geometry": (None, [_i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+                "or_shard0_pack": (None, [_i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+                "or_shard0_unpack": (None, [_i32, _vp, _vp, _i32, _i32, _vp, _vp]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -113,6 +116,50 @@ def views(numels, world: int, rank: int):
     to = np.empty(len(n), dtype=np.int64)
     lib().or_views(len(n), _ptr(n), world, rank, _ptr(bo), _ptr(ln), _ptr(to))
     return bo, ln, to
+
+
+# ---------------------------------------------------------------- per-parameter dim-0 shards
+def _shape_arrays(shapes):
+    nd = np.array([len(s) for s in shapes], dtype=np.int32)
+    dims = np.array([d for s in shapes for d in s] or [0], dtype=np.int64)
+    return nd, dims
+
+
+def shard0_geometry(shapes, world: int):
+    """(rows c_i, row_elems r_i, offset_i, S) of the per-parameter dim-0 layout."""
+    n = len(shapes)
+    nd, dims = _shape_arrays(shapes)
+    c, r, o = (np.empty(max(n, 1), dtype=np.int64) for _ in range(3))
+    S = _i64()
+    lib().or_shard0_geometry(n, _ptr(nd), _ptr(dims), world, _ptr(c), _ptr(r), _ptr(o), C.byref(S))
+    return c[:n], r[:n], o[:n], S.value
+
+
+def shard0_pack(tensors, world: int, rank: int) -> np.ndarray:
+    """Rank `rank`'s buffer of the group (each parameter's dim-0 chunk, zero-padded)."""
+    srcs = [np.ascontiguousarray(t) for t in tensors]
+    dtype = srcs[0].dtype
+    if any(x.dtype != dtype for x in srcs) or dtype.itemsize not in (2, 4):
+        raise TypeError("shard0_pack needs tensors of one 2- or 4-byte dtype")
+    shapes = [x.shape for x in srcs]
+    _, _, _, S = shard0_geometry(shapes, world)
+    nd, dims = _shape_arrays(shapes)
+    out = np.empty(max(S, 1), dtype=dtype)
+    lib().or_shard0_pack(len(srcs), _ptr(nd), _ptr(dims), world, dtype.itemsize, rank,
+                         _ptr_table([x.reshape(-1) if x.size else np.zeros(1, dtype) for x in srcs]),
+                         _ptr(out))
+    return out[:S]
+
+
+def shard0_unpack(full: np.ndarray, shapes, world: int):
+    """The parameters (global shapes) from the ranks' buffers one after the other."""
+    full = np.ascontiguousarray(full)
+    nd, dims = _shape_arrays(shapes)
+    outs = [np.empty(tuple(s), dtype=full.dtype) for s in shapes]
+    lib().or_shard0_unpack(len(shapes), _ptr(nd), _ptr(dims), world, full.dtype.itemsize,
+                           _ptr(full if full.size else np.zeros(1, full.dtype)),
+                           _ptr_table([o.reshape(-1) if o.size else np.zeros(1, full.dtype) for o in outs]))
+    return outs
 
 
 # ---------------------------------------------------------------- bf16

@@ -140,6 +140,100 @@ int32_t or_views(int32_t n_tensors, const int64_t* numel, int32_t world,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Per-parameter dim-0 sharding.  [DP] FSDP2 section and its figure: each   */
+/* parameter is split along dim 0 over the ranks and keeps its global      */
+/* shape; three (4,2) weights over 2 ranks give every rank the first (or    */
+/* last) two rows of each weight, local shape (2,2), 12 elements per rank; */
+/* [DP] "FSDP2: record each parameter's shard": an (8,4) weight over 4     */
+/* ranks gives a local (2,4).  Parameters of one group still travel       */
+/* together: a rank's shards of the group's parameters are concatenated    */
+/* into one buffer for the group's collectives.                             */
+/* Reading for splits the pages do not show: chunks of c = ceil(d0/world)  */
+/* rows, rank q holding rows [q*c, min((q+1)*c, d0)); each rank's chunk is  */
+/* padded with zero rows to c rows so that every rank's buffer has the same */
+/* size S = sum_i c_i * r_i (r_i = elements per row, the product of the     */
+/* other dimensions).  A 0-d parameter is one row of one element.           */
+/* ------------------------------------------------------------------------ */
+
+/* Per parameter: chunk rows c_i, row length r_i and offset in a rank's
+ * buffer; *shard = S. */
+void or_shard0_geometry(int32_t n, const int32_t* ndims, const int64_t* shapes,
+                        int32_t world, int64_t* rows, int64_t* row_elems,
+                        int64_t* offset, int64_t* shard)
+{
+    int64_t d = 0, o = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        int64_t d0 = ndims[i] > 0 ? shapes[d] : 1;
+        int64_t r = 1;
+        for (int32_t k = 1; k < ndims[i]; ++k)
+            r *= shapes[d + k];
+        d += ndims[i];
+        rows[i] = (d0 + world - 1) / world;
+        row_elems[i] = r;
+        offset[i] = o;
+        o += rows[i] * r;
+    }
+    *shard = o;
+}
+
+/* Rows of a chunk of c rows that rank q really holds out of d0. */
+static int64_t or_shard0_real_rows(int64_t d0, int64_t c, int32_t q)
+{
+    int64_t left = d0 - (int64_t)q * c;
+    return left < 0 ? 0 : (left < c ? left : c);
+}
+
+static int64_t or_dim0(const int32_t* ndims, const int64_t* shapes, int32_t i)
+{
+    int64_t d = 0;
+    for (int32_t j = 0; j < i; ++j)
+        d += ndims[j];
+    return ndims[i] > 0 ? shapes[d] : 1;
+}
+
+/* Rank `rank`'s buffer: for each parameter its real rows (row-major, bit for
+ * bit) followed by zero rows up to c_i rows. */
+void or_shard0_pack(int32_t n, const int32_t* ndims, const int64_t* shapes,
+                    int32_t world, int32_t elem_size, int32_t rank,
+                    const void* const* src, void* dst)
+{
+    int64_t c[n > 0 ? n : 1], r[n > 0 ? n : 1], off[n > 0 ? n : 1], S;
+    or_shard0_geometry(n, ndims, shapes, world, c, r, off, &S);
+    unsigned char* out = (unsigned char*)dst;
+    for (int32_t i = 0; i < n; ++i) {
+        int64_t d0 = or_dim0(ndims, shapes, i);
+        int64_t real = or_shard0_real_rows(d0, c[i], rank) * r[i];
+        const unsigned char* in = (const unsigned char*)src[i] + (int64_t)rank * c[i] * r[i] * elem_size;
+        for (int64_t k = 0; k < real * elem_size; ++k)
+            out[off[i] * elem_size + k] = in[k];
+        for (int64_t k = real * elem_size; k < c[i] * r[i] * elem_size; ++k)
+            out[off[i] * elem_size + k] = 0;
+    }
+}
+
+/* The inverse after a gather: full = the world ranks' buffers one after the
+ * other; parameter i's row j comes from rank j / c_i, row j % c_i of that
+ * rank's chunk.  Padding rows are dropped. */
+void or_shard0_unpack(int32_t n, const int32_t* ndims, const int64_t* shapes,
+                      int32_t world, int32_t elem_size, const void* full,
+                      void* const* dst)
+{
+    int64_t c[n > 0 ? n : 1], r[n > 0 ? n : 1], off[n > 0 ? n : 1], S;
+    or_shard0_geometry(n, ndims, shapes, world, c, r, off, &S);
+    const unsigned char* in = (const unsigned char*)full;
+    for (int32_t i = 0; i < n; ++i) {
+        int64_t d0 = or_dim0(ndims, shapes, i);
+        unsigned char* out = (unsigned char*)dst[i];
+        for (int64_t j = 0; j < d0; ++j) {
+            int64_t q = j / c[i], jj = j % c[i];
+            const unsigned char* row = in + (q * S + off[i] + jj * r[i]) * elem_size;
+            for (int64_t k = 0; k < r[i] * elem_size; ++k)
+                out[j * r[i] * elem_size + k] = row[k];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* bf16 <-> fp32.  A bf16 value is the upper half of an fp32 bit pattern.   */
 /* ------------------------------------------------------------------------ */
 

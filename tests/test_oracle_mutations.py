@@ -46,10 +46,16 @@ MUTATIONS = {
     "overflow_check_misses_nan": ("if (!isfinite(acc[i]))", "if (isinf(acc[i]))"),
     "norm_squares_in_fp32": ("s = s + (double)acc[i] * (double)acc[i];", "s = s + (double)(acc[i] * acc[i]);"),
     "locate_offset_by_one": ("offset[j] = pos[j] - start;\n        } else", "offset[j] = pos[j] - start + 1;\n        } else"),
+    "shard0_chunk_rounded_down": ("rows[i] = (d0 + world - 1) / world;", "rows[i] = d0 / world + (d0 % world ? 0 : 0);"),
+    "shard0_padding_first": ("out[off[i] * elem_size + k] = in[k];", "out[off[i] * elem_size + (c[i] * r[i] - real) * elem_size + k] = in[k];"),
+    "shard0_rank_offset_in_rows_not_elements": ("(int64_t)rank * c[i] * r[i] * elem_size;", "(int64_t)rank * c[i] * elem_size;"),
+    "shard0_unpack_row_order": ("int64_t q = j / c[i], jj = j % c[i];", "int64_t q = j % world, jj = j / world;"),
+    "shard0_row_length_wrong": ("for (int32_t k = 1; k < ndims[i]; ++k)", "for (int32_t k = 2; k < ndims[i]; ++k)"),
 }
 
 PIN_FILES = ["tests/test_oracle_pack.py", "tests/test_oracle_reduce.py",
-             "tests/test_oracle_adamw.py", "tests/test_oracle_bf16_memory.py"]
+             "tests/test_oracle_adamw.py", "tests/test_oracle_bf16_memory.py",
+             "tests/test_oracle_shard0.py"]
 
 
 @pytest.mark.slow
