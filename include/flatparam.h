@@ -367,6 +367,68 @@ typedef struct fp_units_step_args {
 } fp_units_step_args;
 fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream);
 
+/* ------------------------------------------------------------------ dim-0 */
+
+/* Per-parameter sharding along dim 0.  [DP] FSDP2 sections and the
+ * FSDP1 / FSDP2 comparison figure: every parameter of a group is cut along
+ * its first dimension over the N_d ranks and keeps its global shape; a
+ * rank's pieces of the group's parameters travel together in one buffer.
+ * Geometry, for parameter i of shape (d0, ...) with r_i = product of the
+ * other dims (1 for a 0-d parameter, which counts as one row of one element):
+ *   c_i = ceil(d0 / N_d) rows per rank; rank q holds rows
+ *   [q c_i, min((q+1) c_i, d0)) of it, the rest of its c_i rows are zero;
+ *   off_i = sum over j < i of c_j r_j;  S = sum of c_i r_i.
+ * Rank q's buffer holds its chunk of parameter i at [off_i, off_i + c_i r_i)
+ * (row-major, padding rows last); the gathered buffer is the N_d ranks'
+ * buffers one after the other, bf16 or fp32 [N_d * S].  Padding rows are
+ * the plainest reading where d0 is not a multiple of N_d (the pages show
+ * only even splits). */
+typedef struct fp_shard0_plan fp_shard0_plan;
+
+/* n_params >= 1 parameters, ndims / shapes as in fp_plan_create; world in
+ * [1, 1 << 20].  Host only.  FP_ERR_RANGE when a dim exceeds 2^40 or S
+ * exceeds 2^40 elements. */
+fp_status fp_shard0_plan_create(int32_t n_params, const int32_t* ndims, const int64_t* shapes,
+                                int32_t world, fp_shard0_plan** out);
+/* Releases the plan and the device tables its calls attached to it (the
+ * caller makes sure none of its calls is still running). */
+void fp_shard0_plan_destroy(fp_shard0_plan* plan);
+/* shard: S; numel: sum of the parameters' numels (either may be NULL). */
+fp_status fp_shard0_plan_info(const fp_shard0_plan* plan, int64_t* shard, int64_t* numel);
+/* Rank `rank`'s local piece of every parameter, one descriptor per
+ * parameter written to out[0..n): buf_offset = off_i into the rank's buffer,
+ * numel = real rows * r_i, tensor_offset = q c_i r_i into the flattened
+ * parameter (0 when empty), shape = (real rows, other dims...) -- the local
+ * shape, 2-D or more kept (a 0-d parameter has ndim 1).  FP_ERR_RANGE if
+ * cap < n (then *n_out = n) or rank outside [0, N_d).  Host only. */
+fp_status fp_shard0_views(const fp_shard0_plan* plan, int32_t rank, fp_view* out, int32_t cap,
+                          int32_t* n_out);
+
+/* Rank `rank`'s buffer of the group from the full parameters:
+ * dst[off_i + k] = param_i[q c_i r_i + k] for the real rows, 0 for the
+ * padding rows.  rank == -1 writes every rank's buffer: dst is then the
+ * gathered layout, [N_d * S].  elem_size 2 or 4, bits copied as they are.
+ * params: host array of n_params device pointers (contiguous, row-major,
+ * aligned to elem_size; NULL only for empty parameters); dst: device
+ * buffer aligned to elem_size, not overlapping any parameter.
+ * The first call of an (operation, elem_size, rank) on a device builds and
+ * uploads that call's segment tables (hipMalloc, synchronous copies; kept
+ * until fp_shard0_plan_destroy); every call uploads its pointer table on
+ * `stream` from pinned staging, waiting on the host only if the previous
+ * upload of the same table has not finished.  Calls on one plan are
+ * serialised by a lock; order them on one stream. */
+fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
+                         const void* const* params, void* dst, void* stream);
+
+/* After the all-gather: every parameter at its global shape from the
+ * gathered buffer: param_i[q c_i r_i + k] = full[q S + off_i + k] for every
+ * rank q and real row (padding rows are dropped).  full: device [N_d * S],
+ * aligned to elem_size; params as in fp_shard0_pack but written, none
+ * overlapping full or each other.  Tables and staging as in
+ * fp_shard0_pack. */
+fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* full,
+                           void* const* params, void* stream);
+
 /* ------------------------------------------------------------------ helpers */
 
 /* Model-state bytes per GPU.  [DP] ZeRO figure (one formula per row) and

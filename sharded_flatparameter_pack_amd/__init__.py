@@ -24,7 +24,7 @@ from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_ONE_PASS,  # noqa: F40
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
-__all__ = ["Plan", "Units", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
+__all__ = ["Plan", "Units", "Shard0Plan", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
            "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "library_path"]
@@ -176,6 +176,103 @@ class Plan:
             v = buf.narrow(0, d["buf_offset"], d["numel"])
             out.append(v.view(d["shape"]) if rank < 0 else v)
         return out
+
+
+class Shard0Plan:
+    """Per-parameter dim-0 layout of a parameter group over N_d ranks: each
+    parameter cut into ceil(d0 / N_d)-row chunks (zero rows past d0), a
+    rank's chunks back to back in one buffer of S elements."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], world: int):
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.world = int(world)
+        ndims = (C.c_int32 * len(self.shapes))(*[len(s) for s in self.shapes])
+        flat_dims = [d for s in self.shapes for d in s]
+        dims = (C.c_int64 * max(1, len(flat_dims)))(*flat_dims)
+        h = C.c_void_p()
+        check(lib().fp_shard0_plan_create(len(self.shapes), ndims, dims, self.world, C.byref(h)))
+        self._h = h
+        s, t = C.c_int64(), C.c_int64()
+        check(lib().fp_shard0_plan_info(self._h, C.byref(s), C.byref(t)))
+        self.shard, self.numel = s.value, t.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().fp_shard0_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def view_descriptors(self, rank: int):
+        """One dict per parameter: buf_offset, numel, tensor_offset, local shape."""
+        n = len(self.shapes)
+        out = (_lib.fp_view * n)()
+        n_out = C.c_int32()
+        check(lib().fp_shard0_views(self._h, int(rank), out, n, C.byref(n_out)))
+        return [{"tensor": v.tensor, "buf_offset": v.buf_offset, "numel": v.numel,
+                 "tensor_offset": v.tensor_offset, "shape": tuple(v.shape[:v.ndim])} for v in out]
+
+    def views(self, buf, rank: int):
+        """Rank `rank`'s local piece of every parameter on its buffer `buf`
+        (aliasing, no copy), each with its local shape."""
+        return [buf.narrow(0, d["buf_offset"], d["numel"]).view(d["shape"])
+                for d in self.view_descriptors(rank)]
+
+    def _params(self, params):
+        if len(params) != len(self.shapes):
+            raise ValueError("parameter count differs from the plan")
+        dtype = params[0].dtype
+        ptrs = []
+        for i, (t, s) in enumerate(zip(params, self.shapes)):
+            if tuple(t.shape) != s or t.dtype != dtype:
+                raise ValueError(f"parameter {i}: shape {tuple(t.shape)} / dtype {t.dtype} differ from the plan")
+            ptrs.append(_dev_ptr(t, (dtype,), math.prod(s), f"params[{i}]") if t.numel() else None)
+        return dtype, params[0].element_size(), ptrs
+
+    def packer(self, params, dst=None, rank: int = -1):
+        """A callable writing rank `rank`'s buffer (rank = -1: every rank's,
+        the gathered layout) of `params` into `dst` (allocated here when
+        None) and returning it; pointers are marshalled once."""
+        torch = _torch()
+        dtype, esize, ptrs = self._params(params)
+        n = self.shard * (self.world if rank < 0 else 1)
+        if dst is None:
+            dst = torch.empty(n, dtype=dtype, device=params[0].device)
+        dptr = C.c_void_p(_dev_ptr(dst, (dtype,), n, "dst"))
+        table = _ptr_table(ptrs)
+        fn, h, r = lib().fp_shard0_pack, self._h, int(rank)
+
+        def run():
+            check(fn(h, esize, r, table, dptr, _stream(dst)))
+            return dst
+        return run
+
+    def pack(self, params, dst=None, rank: int = -1):
+        return self.packer(params, dst, rank)()
+
+    def unpacker(self, full, params=None):
+        """A callable writing every parameter (global shape) from the gathered
+        buffer `full` into `params` (allocated here when None) and returning
+        them."""
+        torch = _torch()
+        if params is None:
+            params = [torch.empty(s, dtype=full.dtype, device=full.device) for s in self.shapes]
+        dtype, esize, ptrs = self._params(params)
+        fptr = C.c_void_p(_dev_ptr(full, (dtype,), self.shard * self.world, "full"))
+        table = _ptr_table(ptrs)
+        fn, h = lib().fp_shard0_unpack, self._h
+
+        def run():
+            check(fn(h, esize, fptr, table, _stream(full)))
+            return params
+        return run
+
+    def unpack(self, full, params=None):
+        return self.unpacker(full, params)()
 
 
 # ------------------------------------------------------------------ reduce

@@ -76,6 +76,12 @@ SIGNATURES = {
     "fp_units_offsets": (_i32, [_vp, _vp]),
     "fp_units_reduce": (_i32, [_vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "fp_units_step": (_i32, [_vp, C.POINTER(fp_units_step_args), _vp]),
+    "fp_shard0_plan_create": (_i32, [_i32, _vp, _vp, _i32, C.POINTER(_vp)]),
+    "fp_shard0_plan_destroy": (None, [_vp]),
+    "fp_shard0_plan_info": (_i32, [_vp, _vp, _vp]),
+    "fp_shard0_views": (_i32, [_vp, _i32, _vp, _i32, _vp]),
+    "fp_shard0_pack": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "fp_shard0_unpack": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "fp_state_bytes": (_i32, [_f64, _i32, _f64, _i32, C.POINTER(_f64)]),
     "fp_status_string": (C.c_char_p, [_i32]),
     "fp_last_error": (C.c_char_p, []),

@@ -895,6 +895,310 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
     return FP_OK;
 }
 
+// ---------------------------------------------------------------------- dim-0 layout
+
+namespace {
+// Device tables of one segment list on one device, and the staging of its
+// per-call pointer table.
+struct SegTable {
+    int op = -1, es = 0, rank = 0;   // what the list is for
+    int device = -1;
+    int64_t groups = 0;
+    int32_t n_ptrs = 0;
+    SegDesc* segs = nullptr;
+    int32_t* seg_of = nullptr;
+    void** tab = nullptr;
+    void** tab_staging = nullptr;
+    hipEvent_t uploaded = nullptr;
+};
+
+void free_seg_table(SegTable& t) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (t.device >= 0) (void)hipSetDevice(t.device);
+    if (t.uploaded) (void)hipEventSynchronize(t.uploaded), (void)hipEventDestroy(t.uploaded);
+    if (t.segs) (void)hipFree(t.segs);
+    if (t.seg_of) (void)hipFree(t.seg_of);
+    if (t.tab) (void)hipFree(t.tab);
+    if (t.tab_staging) (void)hipHostFree(t.tab_staging);
+    if (cur >= 0) (void)hipSetDevice(cur);
+    t = SegTable();
+}
+
+constexpr int kOpPackRank = 0, kOpPackAll = 1, kOpUnpack = 2;
+}  // namespace
+
+struct fp_shard0_plan {
+    int32_t n = 0, world = 1;
+    std::vector<int32_t> ndims;
+    std::vector<int64_t> dims, dim_start, d0, rows, row_elems, off, numel;
+    int64_t shard = 0, total = 0;
+    std::mutex mu;
+    std::vector<SegTable> tables;
+};
+
+namespace {
+int64_t real_rows(const fp_shard0_plan* p, int32_t i, int32_t q) {
+    const int64_t left = p->d0[i] - (int64_t)q * p->rows[i];
+    return left < 0 ? 0 : (left < p->rows[i] ? left : p->rows[i]);
+}
+
+// The segment list of an operation, in 2-byte units.  Pointer table: pack ->
+// [dst, params...]; unpack -> [params..., full].
+std::vector<SegDesc> shard0_segments(const fp_shard0_plan* p, int op, int es, int rank) {
+    const int64_t u = es / 2;
+    std::vector<SegDesc> v;
+    auto add = [&](int32_t dst, int64_t dst_off, int32_t src, int64_t src_off, int64_t len) {
+        if (len <= 0) return;
+        SegDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.dst = dst;
+        d.dst_off = dst_off * u;
+        d.src = src;
+        d.src_off = src_off * u;
+        d.len = len * u;
+        v.push_back(d);
+    };
+    if (op == kOpUnpack) {
+        for (int32_t i = 0; i < p->n; ++i)
+            for (int32_t q = 0; q < p->world; ++q)
+                add(i, (int64_t)q * p->rows[i] * p->row_elems[i], p->n, (int64_t)q * p->shard + p->off[i],
+                    real_rows(p, i, q) * p->row_elems[i]);
+        return v;
+    }
+    const int32_t q0 = op == kOpPackAll ? 0 : rank, q1 = op == kOpPackAll ? p->world : rank + 1;
+    for (int32_t q = q0; q < q1; ++q) {
+        const int64_t base = op == kOpPackAll ? (int64_t)q * p->shard : 0;
+        for (int32_t i = 0; i < p->n; ++i) {
+            const int64_t real = real_rows(p, i, q) * p->row_elems[i];
+            add(0, base + p->off[i], 1 + i, (int64_t)q * p->rows[i] * p->row_elems[i], real);
+            add(0, base + p->off[i] + real, -1, 0, p->rows[i] * p->row_elems[i] - real);
+        }
+    }
+    return v;
+}
+
+// The device tables of (op, es, rank) on the current device, built on first use.
+fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** out) {
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+    for (auto& t : p->tables)
+        if (t.device == device && t.op == op && t.es == es && t.rank == rank) {
+            *out = &t;
+            return FP_OK;
+        }
+    std::vector<SegDesc> segs = shard0_segments(p, op, es, rank);
+    std::vector<int32_t> seg_of;
+    int64_t g = 0;
+    for (size_t s = 0; s < segs.size(); ++s) {
+        segs[s].tile0 = g;
+        const int64_t n = segment_tiles(segs[s].len);
+        if (g + n > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "layout too large for one launch");
+        for (int64_t k = 0; k < n; ++k) seg_of.push_back((int32_t)s);
+        g += n;
+    }
+    SegTable t;
+    t.op = op;
+    t.es = es;
+    t.rank = rank;
+    t.device = device;
+    t.groups = g;
+    t.n_ptrs = p->n + 1;
+    const size_t segs_b = (segs.empty() ? 1 : segs.size()) * sizeof(SegDesc);
+    const size_t of_b = (seg_of.empty() ? 1 : seg_of.size()) * sizeof(int32_t);
+    const size_t tab_b = (size_t)t.n_ptrs * sizeof(void*);
+    if ((e = hipMalloc((void**)&t.segs, segs_b)) != hipSuccess ||
+        (e = hipMalloc((void**)&t.seg_of, of_b)) != hipSuccess ||
+        (e = hipMalloc((void**)&t.tab, tab_b)) != hipSuccess ||
+        (e = hipHostMalloc((void**)&t.tab_staging, tab_b, hipHostMallocDefault)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&t.uploaded, hipEventDisableTiming)) != hipSuccess ||
+        (!segs.empty() && (e = hipMemcpy(t.segs, segs.data(), segs.size() * sizeof(SegDesc),
+                                         hipMemcpyHostToDevice)) != hipSuccess) ||
+        (!seg_of.empty() && (e = hipMemcpy(t.seg_of, seg_of.data(), seg_of.size() * sizeof(int32_t),
+                                           hipMemcpyHostToDevice)) != hipSuccess)) {
+        free_seg_table(t);
+        return device_fail(e, "allocating the layout's device tables");
+    }
+    p->tables.push_back(t);
+    *out = &p->tables.back();
+    return FP_OK;
+}
+
+// Uploads the pointer table and launches the segment copy of a table.
+fp_status shard0_run(SegTable* t, void* const* ptrs, hipStream_t s) {
+    hipError_t e;
+    // the staging buffer may still feed the previous call's upload
+    if ((e = hipEventSynchronize(t->uploaded)) != hipSuccess) return device_fail(e, "hipEventSynchronize");
+    for (int32_t i = 0; i < t->n_ptrs; ++i) t->tab_staging[i] = ptrs[i];
+    if ((e = hipMemcpyAsync(t->tab, t->tab_staging, (size_t)t->n_ptrs * sizeof(void*),
+                            hipMemcpyHostToDevice, s)) != hipSuccess)
+        return device_fail(e, "uploading the pointer table");
+    if ((e = hipEventRecord(t->uploaded, s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (t->groups == 0) return FP_OK;
+    SegArgs a;
+    a.segs = t->segs;
+    a.seg_of = t->seg_of;
+    a.dst_tab = t->tab;
+    a.src_tab = t->tab;
+    if ((e = launch_segments(a, t->groups, s)) != hipSuccess) return device_fail(e, "segment copy launch");
+    return FP_OK;
+}
+}  // namespace
+
+extern "C" fp_status fp_shard0_plan_create(int32_t n_params, const int32_t* ndims, const int64_t* shapes,
+                                           int32_t world, fp_shard0_plan** out) {
+    if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (n_params < 1) return fail(FP_ERR_RANGE, "n_params must be >= 1");
+    if (ndims == nullptr) return fail(FP_ERR_INVALID, "ndims is NULL");
+    fp_status st;
+    if ((st = check_world(world)) != FP_OK) return st;
+    int64_t n_dims = 0;
+    for (int32_t i = 0; i < n_params; ++i) {
+        if (ndims[i] < 0 || ndims[i] > FP_MAX_NDIM)
+            return fail(FP_ERR_RANGE, "parameter %d: ndim %d outside [0, %d]", i, ndims[i], FP_MAX_NDIM);
+        n_dims += ndims[i];
+    }
+    if (n_dims > 0 && shapes == nullptr) return fail(FP_ERR_INVALID, "shapes is NULL");
+    fp_shard0_plan* p = new (std::nothrow) fp_shard0_plan();
+    if (p == nullptr) return fail(FP_ERR_DEVICE, "out of host memory");
+    p->n = n_params;
+    p->world = world;
+    p->ndims.assign(ndims, ndims + n_params);
+    p->dims.assign(shapes, shapes + n_dims);
+    const int64_t limit = (int64_t)1 << 40;
+    int64_t d = 0, off = 0, total = 0;
+    for (int32_t i = 0; i < n_params; ++i) {
+        p->dim_start.push_back(d);
+        int64_t d0 = 1, r = 1;
+        for (int32_t k = 0; k < ndims[i]; ++k, ++d) {
+            const int64_t s = shapes[d];
+            if (s < 0 || s > limit) {
+                delete p;
+                return fail(FP_ERR_RANGE, "parameter %d: dimension %lld out of range", i, (long long)s);
+            }
+            if (k == 0) d0 = s;
+            else r *= s;
+            if (r > limit) {
+                delete p;
+                return fail(FP_ERR_RANGE, "parameter %d: too many elements", i);
+            }
+        }
+        const int64_t c = (d0 + world - 1) / world;
+        if (r > 0 && d0 > limit / r) {          // numel, and so c * r, above 2^40
+            delete p;
+            return fail(FP_ERR_RANGE, "parameter %d: too many elements", i);
+        }
+        p->d0.push_back(d0);
+        p->rows.push_back(c);
+        p->row_elems.push_back(r);
+        p->off.push_back(off);
+        p->numel.push_back(d0 * r);
+        off += c * r;
+        total += d0 * r;
+        if (off > limit) {
+            delete p;
+            return fail(FP_ERR_RANGE, "group buffer exceeds 2^40 elements");
+        }
+    }
+    p->shard = off;
+    p->total = total;
+    *out = p;
+    return FP_OK;
+}
+
+extern "C" void fp_shard0_plan_destroy(fp_shard0_plan* plan) {
+    if (plan == nullptr) return;
+    for (auto& t : plan->tables) free_seg_table(t);
+    delete plan;
+}
+
+extern "C" fp_status fp_shard0_plan_info(const fp_shard0_plan* plan, int64_t* shard, int64_t* numel) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (shard) *shard = plan->shard;
+    if (numel) *numel = plan->total;
+    return FP_OK;
+}
+
+extern "C" fp_status fp_shard0_views(const fp_shard0_plan* plan, int32_t rank, fp_view* out, int32_t cap,
+                                     int32_t* n_out) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (rank < 0 || rank >= plan->world) return fail(FP_ERR_RANGE, "rank %d outside [0, %d)", rank, plan->world);
+    if (n_out) *n_out = plan->n;
+    if (cap < plan->n) return fail(FP_ERR_RANGE, "cap %d < %d parameters", cap, plan->n);
+    if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+    for (int32_t i = 0; i < plan->n; ++i) {
+        fp_view v;
+        std::memset(&v, 0, sizeof v);
+        v.tensor = i;
+        const int64_t real = real_rows(plan, i, rank);
+        v.buf_offset = plan->off[i];
+        v.numel = real * plan->row_elems[i];
+        v.tensor_offset = (int64_t)rank * plan->rows[i] * plan->row_elems[i];
+        if (v.numel == 0) v.tensor_offset = 0;
+        v.ndim = plan->ndims[i] > 0 ? plan->ndims[i] : 1;
+        v.shape[0] = real;
+        for (int32_t k = 1; k < plan->ndims[i]; ++k) v.shape[k] = plan->dims[plan->dim_start[i] + k];
+        out[i] = v;
+    }
+    return FP_OK;
+}
+
+extern "C" fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
+                                    const void* const* params, void* dst, void* stream) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
+    if (rank < -1 || rank >= plan->world) return fail(FP_ERR_RANGE, "rank %d outside [-1, %d)", rank, plan->world);
+    if (params == nullptr) return fail(FP_ERR_INVALID, "params table is NULL");
+    const int64_t dst_elems = rank < 0 ? plan->shard * plan->world : plan->shard;
+    if (dst == nullptr && dst_elems > 0) return fail(FP_ERR_INVALID, "dst is NULL");
+    if (!aligned(dst, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "dst misaligned");
+    for (int32_t i = 0; i < plan->n; ++i) {
+        if (plan->numel[i] == 0) continue;
+        if (params[i] == nullptr) return fail(FP_ERR_INVALID, "params[%d] is NULL", i);
+        if (!aligned(params[i], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "params[%d] misaligned", i);
+        if (overlap(params[i], plan->numel[i] * elem_size, dst, dst_elems * elem_size))
+            return fail(FP_ERR_INVALID, "params[%d] overlaps dst", i);
+    }
+    std::lock_guard<std::mutex> lock(plan->mu);
+    SegTable* t = nullptr;
+    fp_status st = shard0_table(plan, rank < 0 ? kOpPackAll : kOpPackRank, elem_size, rank < 0 ? 0 : rank, &t);
+    if (st != FP_OK) return st;
+    std::vector<void*> ptrs((size_t)plan->n + 1);
+    ptrs[0] = dst;
+    for (int32_t i = 0; i < plan->n; ++i) ptrs[1 + i] = const_cast<void*>(params[i]);
+    return shard0_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+}
+
+extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* full,
+                                      void* const* params, void* stream) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
+    if (params == nullptr) return fail(FP_ERR_INVALID, "params table is NULL");
+    const int64_t full_elems = plan->shard * plan->world;
+    if (full == nullptr && full_elems > 0) return fail(FP_ERR_INVALID, "full is NULL");
+    if (!aligned(full, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "full misaligned");
+    for (int32_t i = 0; i < plan->n; ++i) {
+        if (plan->numel[i] == 0) continue;
+        if (params[i] == nullptr) return fail(FP_ERR_INVALID, "params[%d] is NULL", i);
+        if (!aligned(params[i], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "params[%d] misaligned", i);
+        if (overlap(params[i], plan->numel[i] * elem_size, full, full_elems * elem_size))
+            return fail(FP_ERR_INVALID, "params[%d] overlaps full", i);
+        for (int32_t j = 0; j < i; ++j)
+            if (overlap(params[i], plan->numel[i] * elem_size, params[j], plan->numel[j] * elem_size))
+                return fail(FP_ERR_INVALID, "params[%d] overlaps params[%d]", i, j);
+    }
+    std::lock_guard<std::mutex> lock(plan->mu);
+    SegTable* t = nullptr;
+    fp_status st = shard0_table(plan, kOpUnpack, elem_size, 0, &t);
+    if (st != FP_OK) return st;
+    std::vector<void*> ptrs((size_t)plan->n + 1);
+    for (int32_t i = 0; i < plan->n; ++i) ptrs[i] = params[i];
+    ptrs[plan->n] = const_cast<void*>(full);
+    return shard0_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------------- helpers
 
 extern "C" fp_status fp_state_bytes(double psi, int32_t world, double k, int32_t stage, double* out) {

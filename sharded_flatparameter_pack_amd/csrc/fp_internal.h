@@ -83,17 +83,23 @@ struct ShardSpan {
     int64_t lo, a, b, hi;
 };
 
-__host__ __device__ inline ShardSpan shard_span(const uint16_t* full, int64_t S, int q) {
-    // element index e is 16-byte aligned in `full` when e % 8 == phase
-    const int64_t phase = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(full) & 15u)) & 15u) >> 1);
+// Elements [lo, lo + len) of a 2-byte stream at `base`, split into whole
+// aligned 16-byte words [a, b) and edge elements [lo, a), [b, hi).
+__host__ __device__ inline ShardSpan elem_span(const uint16_t* base, int64_t lo, int64_t len) {
+    // element index e is 16-byte aligned in `base` when e % 8 == phase
+    const int64_t phase = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(base) & 15u)) & 15u) >> 1);
     ShardSpan s;
-    s.lo = (int64_t)q * S;
-    s.hi = s.lo + S;
+    s.lo = lo;
+    s.hi = lo + len;
     const int64_t up = s.lo + (((phase - s.lo) % 8) + 8) % 8;     // first aligned >= lo
     s.a = up < s.hi ? up : s.hi;
     const int64_t down = s.hi - (((s.hi - phase) % 8) + 8) % 8;   // last aligned <= hi
     s.b = down > s.a ? down : s.a;
     return s;
+}
+
+__host__ __device__ inline ShardSpan shard_span(const uint16_t* full, int64_t S, int q) {
+    return elem_span(full, (int64_t)q * S, S);
 }
 
 // True when shard q's source, read from its first whole word of `full` on,
@@ -212,6 +218,31 @@ inline int64_t unit_tiles(int64_t S) {
     return t > 0 ? t : 1;
 }
 
+// One contiguous copy (or zero fill) of a segment list, in 2-byte units:
+// dst_tab[dst][dst_off, dst_off + len) = src_tab[src][src_off, ...), or
+// zeros when src < 0.  Workgroups [tile0, tile0 + tiles) of a launch take it.
+struct SegDesc {
+    int64_t dst_off;
+    int64_t src_off;
+    int64_t len;
+    int64_t tile0;
+    int32_t dst;
+    int32_t src;
+    int32_t pad[2];
+};
+
+struct SegArgs {
+    const SegDesc* segs;
+    const int32_t* seg_of;        // segment of every workgroup
+    void* const* dst_tab;         // per-call device pointers
+    const void* const* src_tab;
+};
+
+// 16-byte words per lane of a segment copy tile, and the workgroups of one
+// segment of `len` units (at least one, for its edges).
+constexpr int kSegWords = 4;
+inline int64_t segment_tiles(int64_t len) { return ceil_div64(len / 8 + 1, (int64_t)kThreads * kSegWords); }
+
 struct PackArgs {
     const int64_t* offsets;     // [n_tensors + 1] prefix sums, offsets[n] = T
     const int32_t* group_first; // [n_groups + 1] first tensor overlapping each group
@@ -240,6 +271,7 @@ hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
 hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, bool copy_aligned,
                             hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
+hipError_t launch_segments(const SegArgs& a, int64_t n_groups, hipStream_t s);
 // Multi-unit launches: one micro-batch's reduce over all units; the last
 // micro-batch's reduce (+ AdamW when fused) with the copies of all units'
 // other shards (copy_groups workgroups after the reduce tiles); AdamW over

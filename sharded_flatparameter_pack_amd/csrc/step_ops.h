@@ -344,6 +344,18 @@ __device__ __forceinline__ void copy_tile(const uint16_t* src, uint16_t* full, c
     }
 }
 
+// The edge elements of span sp of `full` (those that share a 16-byte word
+// with a neighbour), from src (the source of element sp.lo), one per lane.
+__device__ __forceinline__ void span_edges(const uint16_t* src, uint16_t* full, const ShardSpan& sp,
+                                           int t, int stride) {
+    const int64_t n_head = sp.a - sp.lo;
+    const int64_t n_edge = n_head + (sp.hi - sp.b);
+    for (int64_t k = t; k < n_edge; k += stride) {
+        const int64_t e = k < n_head ? sp.lo + k : sp.b + (k - n_head);
+        full[e] = src != nullptr ? src[e - sp.lo] : (uint16_t)0;
+    }
+}
+
 __device__ __forceinline__ void unshard_edges(const uint16_t* src, uint16_t* full, int64_t S, int q,
                                               int t, int stride) {
     const ShardSpan sp = shard_span(full, S, q);

@@ -244,3 +244,64 @@ def test_units_validation_without_a_device(fp):
     assert _status(L.fp_units_reduce, None, 1.0, 0, None, None, None, None, None) == -1
     assert _status(L.fp_units_step, None, None, None) == -1
     L.fp_units_destroy(None)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_shard0_geometry_and_views_match_oracle(fp, seed):
+    r = np.random.default_rng(100 + seed)
+    shapes = _random_shapes(r)
+    world = int(r.choice([1, 2, 3, 4, 7, 8, 64]))
+    plan = fp.Shard0Plan(shapes, world)
+    c, rows_elems, off, S = oracle.shard0_geometry(shapes, world)
+    assert plan.shard == S
+    assert plan.numel == sum(math.prod(s) for s in shapes)
+    for rank in sorted(set(int(x) for x in r.integers(0, world, size=4))):
+        for i, d in enumerate(plan.view_descriptors(rank)):
+            d0 = shapes[i][0] if shapes[i] else 1
+            real = max(0, min(c[i], d0 - rank * c[i]))
+            assert d["tensor"] == i
+            assert d["buf_offset"] == off[i]
+            assert d["numel"] == real * rows_elems[i]
+            assert d["tensor_offset"] == (rank * c[i] * rows_elems[i] if d["numel"] else 0)
+            assert d["shape"] == (real,) + tuple(shapes[i][1:])
+
+
+def test_shard0_validation_without_a_device(fp):
+    """The dim-0 entry points reject bad arguments before any device call
+    (fake, never-dereferenced addresses)."""
+    L = fp.lib()
+    h = C.c_void_p()
+    nd = (C.c_int32 * 2)(2, 0)
+    dims = (C.c_int64 * 2)(4, 2)
+    assert _status(L.fp_shard0_plan_create, 0, nd, dims, 2, C.byref(h)) == -2
+    assert _status(L.fp_shard0_plan_create, 2, nd, dims, 0, C.byref(h)) == -2
+    assert _status(L.fp_shard0_plan_create, 2, None, dims, 2, C.byref(h)) == -1
+    assert _status(L.fp_shard0_plan_create, 2, nd, None, 2, C.byref(h)) == -1
+    bad = (C.c_int64 * 2)(4, -2)
+    assert _status(L.fp_shard0_plan_create, 2, nd, bad, 2, C.byref(h)) == -2
+    huge = (C.c_int64 * 2)(1 << 40, 1 << 30)
+    assert _status(L.fp_shard0_plan_create, 2, nd, huge, 2, C.byref(h)) == -2
+    plan = fp.Shard0Plan([(4, 2), ()], 2)
+    assert plan.shard == 2 * 2 + 1
+    out = (fp._lib.fp_view * 2)()
+    n = C.c_int32()
+    assert _status(L.fp_shard0_views, plan._h, 0, out, 1, C.byref(n)) == -2 and n.value == 2
+    assert _status(L.fp_shard0_views, plan._h, 2, out, 2, C.byref(n)) == -2
+    assert _status(L.fp_shard0_views, plan._h, -1, out, 2, C.byref(n)) == -2
+    p = (C.c_void_p * 2)(0x100000, 0x200000)
+    dst = C.c_void_p(0x300000)
+    assert _status(L.fp_shard0_pack, plan._h, 3, 0, p, dst, None) == -1        # elem_size
+    assert _status(L.fp_shard0_pack, plan._h, 2, 2, p, dst, None) == -2        # rank
+    assert _status(L.fp_shard0_pack, plan._h, 2, -2, p, dst, None) == -2
+    assert _status(L.fp_shard0_pack, plan._h, 2, 0, None, dst, None) == -1
+    assert _status(L.fp_shard0_pack, plan._h, 2, 0, p, None, None) == -1
+    assert _status(L.fp_shard0_pack, plan._h, 4, 0, p, C.c_void_p(0x300002), None) == -3
+    assert _status(L.fp_shard0_pack, plan._h, 2, 0, (C.c_void_p * 2)(0x100001, 0x200000), dst, None) == -3
+    assert _status(L.fp_shard0_pack, plan._h, 2, 0, (C.c_void_p * 2)(None, 0x200000), dst, None) == -1
+    assert _status(L.fp_shard0_pack, plan._h, 2, -1, (C.c_void_p * 2)(0x300004, 0x200000), dst, None) == -1
+    assert _status(L.fp_shard0_unpack, plan._h, 2, None, p, None) == -1
+    assert _status(L.fp_shard0_unpack, plan._h, 2, dst, (C.c_void_p * 2)(0x300004, 0x200000), None) == -1
+    assert _status(L.fp_shard0_unpack, plan._h, 2, dst, (C.c_void_p * 2)(0x100000, 0x100002), None) == -1
+    assert _status(L.fp_shard0_unpack, None, 2, dst, p, None) == -1
+    assert _status(L.fp_shard0_plan_info, None, None, None) == -1
+    L.fp_shard0_plan_destroy(None)
