@@ -356,6 +356,44 @@ def pack_bench(cfg, dev, reps: int):
     return out
 
 
+def shard0_bench(cfg, dev, reps: int):
+    """The per-parameter dim-0 layout of the workload's parameter group in
+    bf16: fp_shard0_pack of every rank's rows (full-shape gradients to the
+    rank-major reduce-scatter input) and fp_shard0_unpack (the gathered
+    buffer back to full-shape parameters)."""
+    import torch
+    import sharded_flatparameter_pack_amd as fp
+    from workloads import gen
+    plan = fp.Shard0Plan(cfg.shapes, cfg.world)
+    params = [gen.torch_bf16_normal(math.prod(s), 1e-3, cfg.seed, (gen.STREAM_TENSOR, i), dev).view(s)
+              for i, s in enumerate(cfg.shapes)]
+    full = torch.empty(cfg.world * plan.shard, dtype=torch.int16, device=dev)
+    outs = [torch.empty(s, dtype=torch.int16, device=dev) for s in cfg.shapes]
+    T, N, S = plan.numel, cfg.world, plan.shard
+    legs = {"pack_all_ranks": (plan.packer(params, full), 2 * T + 2 * N * S),
+            "unpack": (plan.unpacker(full, outs), 4 * T)}
+    out = {"workload": cfg.name, "params": len(cfg.shapes), "elements": T, "N_d": N,
+           "shard_elems": S, "dtype": "bf16"}
+    for name, (run, alg) in legs.items():
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = alg / (ms * 1e-3) / 1e9
+        out[name] = {"us_per_call": round(ms * 1e3, 2), "alg_bytes": alg, "GBps": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    out["timing"] = (f"hipEvents around {reps} back-to-back calls on one stream (pointer-table upload + "
+                     f"kernel), mean; pack moves 2T + 2*N_d*S bytes (padding rows written), "
+                     f"unpack 4T")
+    plan.close()
+    return out
+
+
 def copy_reference(fp, dev, reps: int = 20):
     """Measured plain-copy bandwidth (fp_unshard of 16 x 8M bf16 shards, 256 MiB each way)."""
     import torch
@@ -536,6 +574,8 @@ def main(argv=None) -> int:
                                     "value_over_copy": round(gbs / copy_gbs, 4)}
         if cfg.shapes is not None:
             result["pack"] = pack_bench(cfg, dev, 20)
+            torch.cuda.empty_cache()
+            result["dim0_layout"] = shard0_bench(cfg, dev, 20)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, rank, args.cpu_seconds)
     print(json.dumps(result), flush=True)

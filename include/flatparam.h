@@ -413,10 +413,13 @@ fp_status fp_shard0_views(const fp_shard0_plan* plan, int32_t rank, fp_view* out
  * buffer aligned to elem_size, not overlapping any parameter.
  * The first call of an (operation, elem_size, rank) on a device builds and
  * uploads that call's segment tables (hipMalloc, synchronous copies; kept
- * until fp_shard0_plan_destroy); every call uploads its pointer table on
- * `stream` from pinned staging, waiting on the host only if the previous
- * upload of the same table has not finished.  Calls on one plan are
- * serialised by a lock; order them on one stream. */
+ * until fp_shard0_plan_destroy).  A call whose pointers differ from the
+ * previous call's of the same table uploads them on `stream` from pinned
+ * staging, waiting on the host only if that previous upload has not
+ * finished; a call with the same pointers only orders `stream` after that
+ * upload.  The device pointer table is shared by the calls of a table: order
+ * the calls of one plan on one stream (a lock serialises the host side).
+ * Not for graph capture. */
 fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
                          const void* const* params, void* dst, void* stream);
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -910,6 +911,8 @@ struct SegTable {
     void** tab = nullptr;
     void** tab_staging = nullptr;
     hipEvent_t uploaded = nullptr;
+    bool have_last = false;          // tab holds (or will hold) last_ptrs
+    std::vector<void*> last_ptrs;
 };
 
 void free_seg_table(SegTable& t) {
@@ -935,6 +938,11 @@ struct fp_shard0_plan {
     int64_t shard = 0, total = 0;
     std::mutex mu;
     std::vector<SegTable> tables;
+    struct Validated {
+        int op, es, rank;
+        std::vector<void*> ptrs;
+    };
+    std::vector<Validated> validated;
 };
 
 namespace {
@@ -944,36 +952,73 @@ int64_t real_rows(const fp_shard0_plan* p, int32_t i, int32_t q) {
 }
 
 // The segment list of an operation, in 2-byte units.  Pointer table: pack ->
-// [dst, params...]; unpack -> [params..., full].
+// [dst, params...]; unpack -> [params..., full].  A parameter whose per-rank
+// piece is below kSegSmallPiece units gets one strided entry for all its
+// pieces; the others one copy entry per piece (and per padding fill).
 std::vector<SegDesc> shard0_segments(const fp_shard0_plan* p, int op, int es, int rank) {
     const int64_t u = es / 2;
+    const int64_t S = p->shard * u;
     std::vector<SegDesc> v;
-    auto add = [&](int32_t dst, int64_t dst_off, int32_t src, int64_t src_off, int64_t len) {
+    auto copy = [&](int32_t dst, int64_t dst_off, int32_t src, int64_t src_off, int64_t len) {
         if (len <= 0) return;
         SegDesc d;
         std::memset(&d, 0, sizeof d);
+        d.kind = kSegCopy;
         d.dst = dst;
-        d.dst_off = dst_off * u;
+        d.dst_off = dst_off;
         d.src = src;
-        d.src_off = src_off * u;
-        d.len = len * u;
+        d.src_off = src_off;
+        d.len = len;
         v.push_back(d);
     };
+    auto strided = [&](int32_t dst, int64_t dst_off, int64_t dst_stride, int32_t src, int64_t src_off,
+                       int64_t src_stride, int64_t piece, int64_t len, int64_t valid) {
+        if (len <= 0) return;
+        SegDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.kind = kSegStrided;
+        d.dst = dst;
+        d.dst_off = dst_off;
+        d.dst_stride = dst_stride;
+        d.src = src;
+        d.src_off = src_off;
+        d.src_stride = src_stride;
+        d.piece = piece;
+        d.len = len;
+        d.valid = valid < 0 ? 0 : (valid < len ? valid : len);
+        v.push_back(d);
+    };
+    auto piece = [&](int32_t i) { return p->rows[i] * p->row_elems[i] * u; };
+    auto small = [&](int32_t i) { return piece(i) < kSegSmallPiece; };
     if (op == kOpUnpack) {
-        for (int32_t i = 0; i < p->n; ++i)
+        for (int32_t i = 0; i < p->n; ++i) {
+            if (small(i)) {
+                strided(i, 0, piece(i), p->n, p->off[i] * u, S, piece(i), p->numel[i] * u, p->numel[i] * u);
+                continue;
+            }
             for (int32_t q = 0; q < p->world; ++q)
-                add(i, (int64_t)q * p->rows[i] * p->row_elems[i], p->n, (int64_t)q * p->shard + p->off[i],
-                    real_rows(p, i, q) * p->row_elems[i]);
+                copy(i, q * piece(i), p->n, q * S + p->off[i] * u, real_rows(p, i, q) * p->row_elems[i] * u);
+        }
         return v;
     }
-    const int32_t q0 = op == kOpPackAll ? 0 : rank, q1 = op == kOpPackAll ? p->world : rank + 1;
+    const bool all = op == kOpPackAll;
+    const int32_t q0 = all ? 0 : rank, q1 = all ? p->world : rank + 1;
     for (int32_t q = q0; q < q1; ++q) {
-        const int64_t base = op == kOpPackAll ? (int64_t)q * p->shard : 0;
+        const int64_t base = all ? q * S : 0;
         for (int32_t i = 0; i < p->n; ++i) {
-            const int64_t real = real_rows(p, i, q) * p->row_elems[i];
-            add(0, base + p->off[i], 1 + i, (int64_t)q * p->rows[i] * p->row_elems[i], real);
-            add(0, base + p->off[i] + real, -1, 0, p->rows[i] * p->row_elems[i] - real);
+            if (small(i)) continue;
+            const int64_t real = real_rows(p, i, q) * p->row_elems[i] * u;
+            copy(0, base + p->off[i] * u, 1 + i, q * piece(i), real);
+            copy(0, base + p->off[i] * u + real, -1, 0, piece(i) - real);
         }
+    }
+    for (int32_t i = 0; i < p->n; ++i) {
+        if (!small(i)) continue;
+        if (all)
+            strided(0, p->off[i] * u, S, 1 + i, 0, piece(i), piece(i), p->world * piece(i), p->numel[i] * u);
+        else
+            strided(0, p->off[i] * u, piece(i), 1 + i, rank * piece(i), piece(i), piece(i), piece(i),
+                    p->numel[i] * u - rank * piece(i));
     }
     return v;
 }
@@ -993,7 +1038,7 @@ fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** o
     int64_t g = 0;
     for (size_t s = 0; s < segs.size(); ++s) {
         segs[s].tile0 = g;
-        const int64_t n = segment_tiles(segs[s].len);
+        const int64_t n = segment_tiles(segs[s]);
         if (g + n > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "layout too large for one launch");
         for (int64_t k = 0; k < n; ++k) seg_of.push_back((int32_t)s);
         g += n;
@@ -1025,16 +1070,26 @@ fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** o
     return FP_OK;
 }
 
-// Uploads the pointer table and launches the segment copy of a table.
+// Uploads the pointer table (unless it holds these pointers already) and
+// launches the segment copy of a table.
 fp_status shard0_run(SegTable* t, void* const* ptrs, hipStream_t s) {
     hipError_t e;
-    // the staging buffer may still feed the previous call's upload
-    if ((e = hipEventSynchronize(t->uploaded)) != hipSuccess) return device_fail(e, "hipEventSynchronize");
-    for (int32_t i = 0; i < t->n_ptrs; ++i) t->tab_staging[i] = ptrs[i];
-    if ((e = hipMemcpyAsync(t->tab, t->tab_staging, (size_t)t->n_ptrs * sizeof(void*),
-                            hipMemcpyHostToDevice, s)) != hipSuccess)
-        return device_fail(e, "uploading the pointer table");
-    if ((e = hipEventRecord(t->uploaded, s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    const bool same = t->have_last && std::equal(ptrs, ptrs + t->n_ptrs, t->last_ptrs.begin());
+    if (same) {
+        // the table's last upload, wherever it was enqueued, comes first
+        if ((e = hipStreamWaitEvent(s, t->uploaded, 0)) != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+    } else {
+        // the staging buffer may still feed the previous call's upload
+        if ((e = hipEventSynchronize(t->uploaded)) != hipSuccess) return device_fail(e, "hipEventSynchronize");
+        for (int32_t i = 0; i < t->n_ptrs; ++i) t->tab_staging[i] = ptrs[i];
+        t->have_last = false;
+        if ((e = hipMemcpyAsync(t->tab, t->tab_staging, (size_t)t->n_ptrs * sizeof(void*),
+                                hipMemcpyHostToDevice, s)) != hipSuccess)
+            return device_fail(e, "uploading the pointer table");
+        if ((e = hipEventRecord(t->uploaded, s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+        t->last_ptrs.assign(ptrs, ptrs + t->n_ptrs);
+        t->have_last = true;
+    }
     if (t->groups == 0) return FP_OK;
     SegArgs a;
     a.segs = t->segs;
@@ -1145,29 +1200,70 @@ extern "C" fp_status fp_shard0_views(const fp_shard0_plan* plan, int32_t rank, f
     return FP_OK;
 }
 
+namespace {
+// The pointer set a call of (op, es, rank) last passed validation with: a
+// call with the same pointers skips the checks (they depend on nothing else).
+bool shard0_validated(fp_shard0_plan* p, int op, int es, int rank, const std::vector<void*>& ptrs) {
+    for (const auto& v : p->validated)
+        if (v.op == op && v.es == es && v.rank == rank) return v.ptrs == ptrs;
+    return false;
+}
+void shard0_remember(fp_shard0_plan* p, int op, int es, int rank, const std::vector<void*>& ptrs) {
+    for (auto& v : p->validated)
+        if (v.op == op && v.es == es && v.rank == rank) {
+            v.ptrs = ptrs;
+            return;
+        }
+    p->validated.push_back({op, es, rank, ptrs});
+}
+
+// Null, alignment and overlap checks of the parameters against `other`
+// (dst or full); with `disjoint`, also of the parameters among themselves
+// (sorted by address: O(n log n)).
+fp_status shard0_check_params(const fp_shard0_plan* p, int32_t es, const void* const* params,
+                              const void* other, int64_t other_elems, const char* other_name, bool disjoint) {
+    std::vector<std::pair<uintptr_t, int32_t>> spans;
+    for (int32_t i = 0; i < p->n; ++i) {
+        if (p->numel[i] == 0) continue;
+        if (params[i] == nullptr) return fail(FP_ERR_INVALID, "params[%d] is NULL", i);
+        if (!aligned(params[i], (uintptr_t)es)) return fail(FP_ERR_ALIGN, "params[%d] misaligned", i);
+        if (overlap(params[i], p->numel[i] * es, other, other_elems * es))
+            return fail(FP_ERR_INVALID, "params[%d] overlaps %s", i, other_name);
+        if (disjoint) spans.emplace_back(reinterpret_cast<uintptr_t>(params[i]), i);
+    }
+    std::sort(spans.begin(), spans.end());
+    for (size_t k = 1; k < spans.size(); ++k) {
+        const int32_t a = spans[k - 1].second, b = spans[k].second;
+        if (overlap(params[a], p->numel[a] * es, params[b], p->numel[b] * es))
+            return fail(FP_ERR_INVALID, "params[%d] overlaps params[%d]", b < a ? b : a, b < a ? a : b);
+    }
+    return FP_OK;
+}
+}  // namespace
+
 extern "C" fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
                                     const void* const* params, void* dst, void* stream) {
     if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
     if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
     if (rank < -1 || rank >= plan->world) return fail(FP_ERR_RANGE, "rank %d outside [-1, %d)", rank, plan->world);
     if (params == nullptr) return fail(FP_ERR_INVALID, "params table is NULL");
-    const int64_t dst_elems = rank < 0 ? plan->shard * plan->world : plan->shard;
-    if (dst == nullptr && dst_elems > 0) return fail(FP_ERR_INVALID, "dst is NULL");
-    if (!aligned(dst, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "dst misaligned");
-    for (int32_t i = 0; i < plan->n; ++i) {
-        if (plan->numel[i] == 0) continue;
-        if (params[i] == nullptr) return fail(FP_ERR_INVALID, "params[%d] is NULL", i);
-        if (!aligned(params[i], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "params[%d] misaligned", i);
-        if (overlap(params[i], plan->numel[i] * elem_size, dst, dst_elems * elem_size))
-            return fail(FP_ERR_INVALID, "params[%d] overlaps dst", i);
-    }
-    std::lock_guard<std::mutex> lock(plan->mu);
-    SegTable* t = nullptr;
-    fp_status st = shard0_table(plan, rank < 0 ? kOpPackAll : kOpPackRank, elem_size, rank < 0 ? 0 : rank, &t);
-    if (st != FP_OK) return st;
+    const int op = rank < 0 ? kOpPackAll : kOpPackRank;
+    const int key_rank = rank < 0 ? 0 : rank;
     std::vector<void*> ptrs((size_t)plan->n + 1);
     ptrs[0] = dst;
     for (int32_t i = 0; i < plan->n; ++i) ptrs[1 + i] = const_cast<void*>(params[i]);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    if (!shard0_validated(plan, op, elem_size, key_rank, ptrs)) {
+        const int64_t dst_elems = rank < 0 ? plan->shard * plan->world : plan->shard;
+        if (dst == nullptr && dst_elems > 0) return fail(FP_ERR_INVALID, "dst is NULL");
+        if (!aligned(dst, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "dst misaligned");
+        fp_status st = shard0_check_params(plan, elem_size, params, dst, dst_elems, "dst", false);
+        if (st != FP_OK) return st;
+        shard0_remember(plan, op, elem_size, key_rank, ptrs);
+    }
+    SegTable* t = nullptr;
+    fp_status st = shard0_table(plan, op, elem_size, key_rank, &t);
+    if (st != FP_OK) return st;
     return shard0_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
 }
 
@@ -1176,26 +1272,21 @@ extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, c
     if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
     if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
     if (params == nullptr) return fail(FP_ERR_INVALID, "params table is NULL");
-    const int64_t full_elems = plan->shard * plan->world;
-    if (full == nullptr && full_elems > 0) return fail(FP_ERR_INVALID, "full is NULL");
-    if (!aligned(full, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "full misaligned");
-    for (int32_t i = 0; i < plan->n; ++i) {
-        if (plan->numel[i] == 0) continue;
-        if (params[i] == nullptr) return fail(FP_ERR_INVALID, "params[%d] is NULL", i);
-        if (!aligned(params[i], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "params[%d] misaligned", i);
-        if (overlap(params[i], plan->numel[i] * elem_size, full, full_elems * elem_size))
-            return fail(FP_ERR_INVALID, "params[%d] overlaps full", i);
-        for (int32_t j = 0; j < i; ++j)
-            if (overlap(params[i], plan->numel[i] * elem_size, params[j], plan->numel[j] * elem_size))
-                return fail(FP_ERR_INVALID, "params[%d] overlaps params[%d]", i, j);
-    }
-    std::lock_guard<std::mutex> lock(plan->mu);
-    SegTable* t = nullptr;
-    fp_status st = shard0_table(plan, kOpUnpack, elem_size, 0, &t);
-    if (st != FP_OK) return st;
     std::vector<void*> ptrs((size_t)plan->n + 1);
     for (int32_t i = 0; i < plan->n; ++i) ptrs[i] = params[i];
     ptrs[plan->n] = const_cast<void*>(full);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    if (!shard0_validated(plan, kOpUnpack, elem_size, 0, ptrs)) {
+        const int64_t full_elems = plan->shard * plan->world;
+        if (full == nullptr && full_elems > 0) return fail(FP_ERR_INVALID, "full is NULL");
+        if (!aligned(full, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "full misaligned");
+        fp_status st = shard0_check_params(plan, elem_size, params, full, full_elems, "full", true);
+        if (st != FP_OK) return st;
+        shard0_remember(plan, kOpUnpack, elem_size, 0, ptrs);
+    }
+    SegTable* t = nullptr;
+    fp_status st = shard0_table(plan, kOpUnpack, elem_size, 0, &t);
+    if (st != FP_OK) return st;
     return shard0_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
 }
 

@@ -218,30 +218,47 @@ inline int64_t unit_tiles(int64_t S) {
     return t > 0 ? t : 1;
 }
 
-// One contiguous copy (or zero fill) of a segment list, in 2-byte units:
-// dst_tab[dst][dst_off, dst_off + len) = src_tab[src][src_off, ...), or
-// zeros when src < 0.  Workgroups [tile0, tile0 + tiles) of a launch take it.
+// One entry of a segment list, in 2-byte units.
+// kind kSegCopy: dst[dst_off + k] = src[src_off + k] for k < len, or zeros
+//   when src < 0; whole 16-byte words of the destination per lane.
+// kind kSegStrided: a set of equal pieces of `piece` units, for groups of
+//   small pieces that would otherwise share destination cache lines between
+//   workgroups: for e < len, q = e / piece, k = e % piece,
+//   dst[dst_off + q * dst_stride + k] = e < valid ? src[src_off + q * src_stride + k] : 0,
+//   one unit per lane (len < 2^31).
+constexpr int32_t kSegCopy = 0, kSegStrided = 1;
 struct SegDesc {
     int64_t dst_off;
     int64_t src_off;
     int64_t len;
-    int64_t tile0;
-    int32_t dst;
-    int32_t src;
-    int32_t pad[2];
+    int64_t tile0;                // first workgroup of the entry
+    int64_t piece;
+    int64_t valid;
+    int64_t dst_stride;
+    int64_t src_stride;
+    int32_t dst;                  // index into the pointer table
+    int32_t src;                  // index into the pointer table, -1: zeros
+    int32_t kind;
+    int32_t pad;
 };
 
 struct SegArgs {
     const SegDesc* segs;
-    const int32_t* seg_of;        // segment of every workgroup
+    const int32_t* seg_of;        // entry of every workgroup
     void* const* dst_tab;         // per-call device pointers
     const void* const* src_tab;
 };
 
-// 16-byte words per lane of a segment copy tile, and the workgroups of one
-// segment of `len` units (at least one, for its edges).
-constexpr int kSegWords = 4;
-inline int64_t segment_tiles(int64_t len) { return ceil_div64(len / 8 + 1, (int64_t)kThreads * kSegWords); }
+// 16-byte words per lane of a copy tile; units per workgroup of a strided
+// entry; pieces below kSegSmallPiece units go to strided entries.
+constexpr int kSegWords = 1;
+constexpr int64_t kSegStridedTile = 4096;
+constexpr int64_t kSegSmallPiece = 2048;
+// Workgroups of one entry (at least one, for a copy's edges).
+inline int64_t segment_tiles(const SegDesc& d) {
+    if (d.kind == kSegStrided) return ceil_div64(d.len, kSegStridedTile);
+    return ceil_div64(d.len / 8 + 1, (int64_t)kThreads * kSegWords);
+}
 
 struct PackArgs {
     const int64_t* offsets;     // [n_tensors + 1] prefix sums, offsets[n] = T

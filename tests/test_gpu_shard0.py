@@ -142,6 +142,67 @@ def test_shard0_random_groups(fp, seed):
         assert _same(w, host[i])
 
 
+@pytest.mark.parametrize("world", [3, 8])
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16])
+def test_shard0_small_and_large_pieces(fp, world, dtype):
+    """Per-rank pieces on both sides of the size where the kernel switches
+    from one copy per piece to one gathering workgroup set per parameter,
+    with uneven last ranks and odd element offsets."""
+    shapes = [(1000, 37), (2047,), (2048 * 3 + 1,), (4096 * 8,), (9, 511), (7, 4097), (1,), (2, 1025)]
+    say(f"shard0 piece sizes world={world} dtype={np.dtype(dtype).name}")
+    r = np.random.default_rng(world)
+    host = _host_params(shapes, dtype, 31 + world, specials=True)
+    params = _params_on_device(host, dtype, r)
+    plan = fp.Shard0Plan(shapes, world)
+    S = plan.shard
+    want_full = np.concatenate([oracle.shard0_pack(host, world, q) for q in range(world)])
+    full = _at_offset(world * S, dtype, 3, fill=-7 if dtype == np.uint16 else float("nan"))
+    plan.pack(params, full)
+    torch.cuda.synchronize()
+    assert _same(to_host(full), want_full)
+    for q in range(world):
+        buf = _at_offset(S, dtype, q % 4, fill=-7 if dtype == np.uint16 else float("nan"))
+        plan.pack(params, buf, rank=q)
+        torch.cuda.synchronize()
+        assert _same(to_host(buf), oracle.shard0_pack(host, world, q)), f"rank {q}"
+    want = oracle.shard0_unpack(want_full, shapes, world)
+    outs = [_at_offset(math.prod(s), dtype, 1 + i % 3, fill=0).view(s) for i, s in enumerate(shapes)]
+    plan.unpack(full, outs)
+    torch.cuda.synchronize()
+    for i, (o, w) in enumerate(zip(outs, want)):
+        assert _same(to_host(o), w), f"parameter {i}"
+
+
+def test_shard0_same_buffers_new_contents(fp):
+    """Calls that reuse the previous call's buffers skip the pointer upload:
+    they must still see the current contents, and a switch to other buffers
+    and back must upload again."""
+    shapes = [(300, 9), (5000,), ()]
+    world = 8
+    plan = fp.Shard0Plan(shapes, world)
+    say("shard0 same buffers, new contents")
+    r = np.random.default_rng(5)
+    sets = []
+    for k in range(2):
+        h = _host_params(shapes, np.uint16, 200 + k)
+        sets.append((h, _params_on_device(h, np.uint16, r)))
+    full = torch.empty(world * plan.shard, dtype=torch.int16, device=dev())
+    outs = []
+    for step, k in enumerate([0, 0, 1, 0, 1, 1]):
+        h, p = sets[k]
+        if step == 1:                       # new contents in the same buffers
+            h = _host_params(shapes, np.uint16, 300)
+            for x, y in zip(p, h):
+                x.copy_(to_dev(y.reshape(-1)).view(y.shape))
+            sets[0] = (h, p)
+        plan.pack(p, full)
+        outs.append((full.clone(), [x.copy() for x in h]))
+    torch.cuda.synchronize()
+    for step, (got, h) in enumerate(outs):
+        want = np.concatenate([oracle.shard0_pack(h, world, q) for q in range(world)])
+        assert _same(to_host(got), want), f"call {step}"
+
+
 def test_shard0_repeated_calls_new_buffers(fp):
     """The per-call pointer table: consecutive calls with other buffers,
     without a synchronisation in between, each see their own pointers."""
