@@ -360,16 +360,24 @@ def shard0_bench(cfg, dev, reps: int):
     """The per-parameter dim-0 layout of the workload's parameter group in
     bf16: fp_shard0_pack of every rank's rows (full-shape gradients to the
     rank-major reduce-scatter input) and fp_shard0_unpack (the gathered
-    buffer back to full-shape parameters)."""
+    buffer back to full-shape parameters).  The parameters (and the unpack's
+    outputs) are consecutive views of one allocation each."""
     import torch
     import sharded_flatparameter_pack_amd as fp
     from workloads import gen
     plan = fp.Shard0Plan(cfg.shapes, cfg.world)
-    params = [gen.torch_bf16_normal(math.prod(s), 1e-3, cfg.seed, (gen.STREAM_TENSOR, i), dev).view(s)
-              for i, s in enumerate(cfg.shapes)]
-    full = torch.empty(cfg.world * plan.shard, dtype=torch.int16, device=dev)
-    outs = [torch.empty(s, dtype=torch.int16, device=dev) for s in cfg.shapes]
     T, N, S = plan.numel, cfg.world, plan.shard
+
+    def split(flat):          # consecutive views of one allocation, one per parameter
+        out, o = [], 0
+        for s in cfg.shapes:
+            n = math.prod(s)
+            out.append(flat[o:o + n].view(s))
+            o += n
+        return out
+    params = split(gen.torch_bf16_normal(T, 1e-3, cfg.seed, (gen.STREAM_TENSOR,), dev))
+    full = torch.empty(N * S, dtype=torch.int16, device=dev)
+    outs = split(torch.empty(T, dtype=torch.int16, device=dev))
     legs = {"pack_all_ranks": (plan.packer(params, full), 2 * T + 2 * N * S),
             "unpack": (plan.unpacker(full, outs), 4 * T)}
     out = {"workload": cfg.name, "params": len(cfg.shapes), "elements": T, "N_d": N,
@@ -498,6 +506,8 @@ def main(argv=None) -> int:
                     help="skip the other modes, the pack and the copy reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run fp_unshard (a plain copy of known size) for counter calibration")
+    ap.add_argument("--dim0-only", action="store_true",
+                    help="only time the per-parameter dim-0 layout's pack and unpack of the workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)
@@ -520,6 +530,12 @@ def main(argv=None) -> int:
     if args.copy_calibration:
         return copy_calibration(fp, dev, args.steps)
     cfg = CONFIGS[args.workload]
+    if args.dim0_only:
+        if cfg.shapes is None:
+            print(f"{cfg.name} has no parameter shapes", file=sys.stderr)
+            return 2
+        print(json.dumps(shard0_bench(cfg, dev, max(1, args.steps))), flush=True)
+        return 0
     rank = cfg.ranks[0]
     world, n = cfg.world, cfg.n_micro
     B = step_bytes_per_elem(world, n)

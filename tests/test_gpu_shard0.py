@@ -251,3 +251,54 @@ def test_shard0_transformer_layer_full_size(fp, name):
     want = oracle.shard0_unpack(want_full, shapes, world)
     for i, (o, w) in enumerate(zip(outs, want)):
         assert _same(to_host(o), w), f"parameter {i}"
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_shard0_step_composition(fp, rank):
+    """One step in the dim-0 layout with the flat step's kernels: every
+    rank's full-shape bf16 gradients to the rank-major layout
+    (fp_shard0_pack), this rank's fixed-order reduce + AdamW + bf16 cast +
+    copy of the other ranks' shards (fp_shard_step on the S-element shard),
+    then the gathered buffer back to full-shape parameters
+    (fp_shard0_unpack); against the oracle's same composition.  Uneven
+    first dims put zero padding rows in the shards: their gradient is 0 and
+    so is their master weight, so they stay 0."""
+    from gpu_common import assert_bf16_within_1ulp, assert_f32_close, hp_kwargs
+    from workloads.configs import AdamW
+    hp = AdamW()
+    shapes = [(48, 32), (48,), (13, 7), (), (5,), (2, 3000)]
+    world, seed = 4, 21
+    say(f"shard0 step composition rank={rank}")
+    plan = fp.Shard0Plan(shapes, world)
+    S = plan.shard
+    grads = [[gen.bf16_normal(math.prod(s), 1e-3, seed, gen.STREAM_GRAD, q, i).reshape(s)
+              for i, s in enumerate(shapes)] for q in range(world)]
+    master = [gen.normal_f32(math.prod(s), 0.02, seed, gen.STREAM_MASTER, i).reshape(s)
+              for i, s in enumerate(shapes)]
+    others = [oracle.f32_to_bf16(oracle.shard0_pack(master, world, q)) for q in range(world)]
+
+    rows_o = [oracle.shard0_pack(grads[q], world, rank) for q in range(world)]
+    th_o = oracle.shard0_pack(master, world, rank)
+    acc_o, m_o, v_o = np.zeros(S, np.float32), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    full_o, flag_o, _ = oracle.shard_step([rows_o], acc_o, th_o, m_o, v_o, others, rank, hp=hp, step=1)
+    params_o = oracle.shard0_unpack(full_o, shapes, world)
+
+    r = np.random.default_rng(rank)
+    bufs = [plan.pack(_params_on_device(grads[q], np.uint16, r)) for q in range(world)]
+    rows = [b[rank * S:(rank + 1) * S] for b in bufs]
+    th = plan.pack(_params_on_device(master, np.float32, r), rank=rank)
+    acc, m, v = (torch.zeros(S, dtype=torch.float32, device=dev()) for _ in range(3))
+    flag = torch.zeros(1, dtype=torch.int32, device=dev())
+    full = torch.zeros(world * S, dtype=torch.int16, device=dev())
+    shards = [to_dev(o) for o in others]
+    shards[rank] = None
+    fp.shard_step(rows, acc, th, m, v, shards, full, rank, scale=1.0 / world, found_inf=flag, step=1,
+                  **hp_kwargs(hp))
+    params = plan.unpack(full)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == flag_o == 0
+    assert_f32_close(to_host(th), th_o, "master shard")
+    assert_f32_close(to_host(m), m_o, "exp_avg")
+    assert_f32_close(to_host(v), v_o, "exp_avg_sq")
+    for i, (p, w) in enumerate(zip(params, params_o)):
+        assert_bf16_within_1ulp(to_host(p).reshape(-1), w.reshape(-1), f"parameter {i}")
