@@ -47,6 +47,12 @@ def lib():
                 "or_adamw": (None, [_i64, _f64, _f64, _f64, _f64, _f64, _i64,
                                     _vp, _vp, _vp, _vp, _i32]),
                 "or_unshard": (None, [_i64, _i32, _vp, _vp]),
+                "or_adamw_coef": (None, [_i64, _f64, _f64, _f64, _f64, _f64, _i64, _f64,
+                                         _vp, _vp, _vp, _vp, _i32]),
+                "or_local_accumulate": (None, [_i64, _vp, _i32, _vp]),
+                "or_local_finish": (None, [_i64, _vp, _i32, _vp, _vp]),
+                "or_grad_coef": (_f64, [_f64, _f32, _f64]),
+                "or_scaler_update": (None, [_i32, _vp, _vp, _f32, _f32, _i32]),
                 "or_state_bytes": (_f64, [_f64, _i32, _f64, _i32]),
                 "or_shard0_geometry": (None, [_i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
                 "or_shard0_pack": (None, [_i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
@@ -204,15 +210,56 @@ def sq_norm(acc: np.ndarray) -> float:
 
 # ---------------------------------------------------------------- AdamW
 def adamw(grad, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps,
-          weight_decay, step: int, skip: bool = False):
-    """In-place AdamW on fp32 master / exp_avg / exp_avg_sq (fp64 arithmetic)."""
+          weight_decay, step: int, skip: bool = False, coef: float = None):
+    """In-place AdamW on fp32 master / exp_avg / exp_avg_sq (fp64 arithmetic);
+    with coef, every gradient element is first multiplied by it in fp64."""
     g = _c(grad, np.float32)
     arrs = [_c(a, np.float32) for a in (master, exp_avg, exp_avg_sq)]
     if any(a.size != g.size for a in arrs):
         raise ValueError("state arrays differ in length")
-    lib().or_adamw(g.size, float(lr), float(beta1), float(beta2), float(eps),
-                   float(weight_decay), int(step), _ptr(g), _ptr(arrs[0]),
-                   _ptr(arrs[1]), _ptr(arrs[2]), int(bool(skip)))
+    if coef is None:
+        lib().or_adamw(g.size, float(lr), float(beta1), float(beta2), float(eps),
+                       float(weight_decay), int(step), _ptr(g), _ptr(arrs[0]),
+                       _ptr(arrs[1]), _ptr(arrs[2]), int(bool(skip)))
+    else:
+        lib().or_adamw_coef(g.size, float(lr), float(beta1), float(beta2), float(eps),
+                            float(weight_decay), int(step), float(coef), _ptr(g), _ptr(arrs[0]),
+                            _ptr(arrs[1]), _ptr(arrs[2]), int(bool(skip)))
+
+
+# ---------------------------------------------------------------- no_sync and the scaler
+def local_accumulate(grad, local=None, accumulate: bool = False) -> np.ndarray:
+    """A rank's fp32 local gradient sum after one more bf16 micro-batch (no exchange)."""
+    g = _c(grad, np.uint16)
+    out = np.empty(g.size, np.float32) if local is None else _c(local, np.float32)
+    if out.size != g.size:
+        raise ValueError("local buffer differs in length")
+    lib().or_local_accumulate(g.size, _ptr(g), int(bool(accumulate)), _ptr(out))
+    return out
+
+
+def local_finish(grad, local=None, accumulate: bool = False) -> np.ndarray:
+    """The rank's bf16 row for the exchange: bf16(local + grad), or bf16(grad)."""
+    g = _c(grad, np.uint16)
+    loc = np.zeros(g.size, np.float32) if local is None else _c(local, np.float32)
+    out = np.empty(g.size, np.uint16)
+    lib().or_local_finish(g.size, _ptr(g), int(bool(accumulate)), _ptr(loc), _ptr(out))
+    return out
+
+
+def grad_coef(sq_norm: float, loss_scale: float, max_norm: float) -> float:
+    """fp64 factor for the loss-scaled reduced gradient: unscale, then clip."""
+    return float(lib().or_grad_coef(float(sq_norm), np.float32(loss_scale), float(max_norm)))
+
+
+def scaler_update(found_inf: int, scale: float, clean_steps: int, *, growth_factor: float = 2.0,
+                  backoff_factor: float = 0.5, growth_interval: int = 2000):
+    """(new fp32 scale, new clean-step count) after one step's overflow decision."""
+    sc = np.array([scale], np.float32)
+    cs = np.array([clean_steps], np.int32)
+    lib().or_scaler_update(int(found_inf), _ptr(sc), _ptr(cs), np.float32(growth_factor),
+                           np.float32(backoff_factor), int(growth_interval))
+    return float(sc[0]), int(cs[0])
 
 
 # ---------------------------------------------------------------- unshard

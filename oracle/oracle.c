@@ -313,6 +313,38 @@ double or_sq_norm(int64_t n, const float* acc)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Local accumulation without communication.  [DP] "Naive Data             */
+/* Parallelism", gradient-accumulation paragraph: the gradients of the     */
+/* first micro-batches are accumulated locally (DDP's no_sync) and only the */
+/* last micro-batch's backward synchronises; [FSDP] section 3.4: gradient   */
+/* accumulation without communication trades memory for fewer exchanges.    */
+/* Reading: a rank keeps an fp32 buffer over its whole unit; micro-batches  */
+/* are added in order in fp32, starting from the first one's value; on the  */
+/* last micro-batch the sum is rounded once to bf16 (the exchange is low     */
+/* precision, [FSDP] section 3.5) and that row enters the reduce above with */
+/* the same scale 1/(N n).                                                  */
+/* ------------------------------------------------------------------------ */
+
+void or_local_accumulate(int64_t n, const uint16_t* grad, int32_t accumulate, float* local)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float g = or_bf16_to_f32(grad[i]);
+        local[i] = accumulate ? local[i] + g : g;
+    }
+}
+
+/* The last micro-batch: out = bf16(local + g), or bf16(g) when nothing was
+ * accumulated (one micro-batch). */
+void or_local_finish(int64_t n, const uint16_t* grad, int32_t accumulate, const float* local,
+                     uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float g = or_bf16_to_f32(grad[i]);
+        out[i] = or_f32_to_bf16(accumulate ? local[i] + g : g);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* AdamW on the shard.  [DP] ZeRO-1 paragraph: AdamW is elementwise, so a   */
 /* rank updates its slice from its averaged gradient and its own moments.   */
 /* [DP] ZeRO figure legend and [GUIDE] section 7: the optimizer state is an */
@@ -322,16 +354,18 @@ double or_sq_norm(int64_t n, const float* acc)
 /* skip != 0: the step is skipped (overflow found) and nothing changes.     */
 /* ------------------------------------------------------------------------ */
 
-void or_adamw(int64_t n, double lr, double beta1, double beta2, double eps,
-              double weight_decay, int64_t step, const float* grad,
-              float* master, float* exp_avg, float* exp_avg_sq, int32_t skip)
+/* coef multiplies every gradient element in fp64 before the update (the   */
+/* unscale of a loss-scaled gradient and the clipping factor, below).       */
+void or_adamw_coef(int64_t n, double lr, double beta1, double beta2, double eps,
+                   double weight_decay, int64_t step, double coef, const float* grad,
+                   float* master, float* exp_avg, float* exp_avg_sq, int32_t skip)
 {
     if (skip)
         return;
     double bias1 = 1.0 - pow(beta1, (double)step);
     double bias2 = 1.0 - pow(beta2, (double)step);
     for (int64_t i = 0; i < n; ++i) {
-        double g = grad[i];
+        double g = (double)grad[i] * coef;
         double theta = master[i];
         double m = exp_avg[i];
         double v = exp_avg_sq[i];
@@ -344,6 +378,53 @@ void or_adamw(int64_t n, double lr, double beta1, double beta2, double eps,
         master[i] = (float)theta;
         exp_avg[i] = (float)m;
         exp_avg_sq[i] = (float)v;
+    }
+}
+
+void or_adamw(int64_t n, double lr, double beta1, double beta2, double eps,
+              double weight_decay, int64_t step, const float* grad,
+              float* master, float* exp_avg, float* exp_avg_sq, int32_t skip)
+{
+    or_adamw_coef(n, lr, beta1, beta2, eps, weight_decay, step, 1.0, grad, master, exp_avg,
+                  exp_avg_sq, skip);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Consumers of the overflow flag and of the gradient norm.  [FSDP] section */
+/* 3.5: the sharded gradient scaler handles overflow of loss-scaled low-    */
+/* precision gradients over sharded state; the pages give no policy, so the */
+/* usual dynamic loss-scaling rule is taken: an overflow skips the step,    */
+/* multiplies the scale by the backoff factor and restarts the count of     */
+/* clean steps; every growth_interval clean steps in a row multiply it by   */
+/* the growth factor.  The scale is an fp32 value.  Global-norm clipping is */
+/* not on the pages; the usual rule is taken: with the unscaled norm        */
+/* ||g|| = sqrt(sum of squares) / scale, gradients are multiplied by        */
+/* min(1, max_norm / (||g|| + 1e-6)); max_norm <= 0 means no clipping.     */
+/* ------------------------------------------------------------------------ */
+
+/* The fp64 coefficient AdamW applies to the (still loss-scaled) gradient. */
+double or_grad_coef(double sq_norm, float loss_scale, double max_norm)
+{
+    double inv = 1.0 / (double)loss_scale;
+    if (max_norm <= 0.0)
+        return inv;
+    double norm = sqrt(sq_norm) * inv;
+    double clip = max_norm / (norm + 1e-6);
+    return clip < 1.0 ? inv * clip : inv;
+}
+
+void or_scaler_update(int32_t found_inf, float* scale, int32_t* clean_steps, float growth_factor,
+                      float backoff_factor, int32_t growth_interval)
+{
+    if (found_inf) {
+        *scale = *scale * backoff_factor;
+        *clean_steps = 0;
+        return;
+    }
+    *clean_steps = *clean_steps + 1;
+    if (*clean_steps == growth_interval) {
+        *scale = *scale * growth_factor;
+        *clean_steps = 0;
     }
 }
 

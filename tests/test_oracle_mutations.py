@@ -51,11 +51,23 @@ MUTATIONS = {
     "shard0_rank_offset_in_rows_not_elements": ("(int64_t)rank * c[i] * r[i] * elem_size;", "(int64_t)rank * c[i] * elem_size;"),
     "shard0_unpack_row_order": ("int64_t q = j / c[i], jj = j % c[i];", "int64_t q = j % world, jj = j / world;"),
     "shard0_row_length_wrong": ("for (int32_t k = 1; k < ndims[i]; ++k)", "for (int32_t k = 2; k < ndims[i]; ++k)"),
+    "local_accumulate_overwrites": ("local[i] = accumulate ? local[i] + g : g;", "local[i] = g;"),
+    "local_finish_drops_last_micro_batch": ("out[i] = or_f32_to_bf16(accumulate ? local[i] + g : g);",
+                                            "out[i] = or_f32_to_bf16(accumulate ? local[i] : g);"),
+    "local_finish_truncates": ("out[i] = or_f32_to_bf16(accumulate ? local[i] + g : g);",
+                               "{ float v = accumulate ? local[i] + g : g; uint32_t u; memcpy(&u, &v, 4); out[i] = (uint16_t)(u >> 16); }"),
+    "grad_coef_norm_not_unscaled": ("double norm = sqrt(sq_norm) * inv;", "double norm = sqrt(sq_norm);"),
+    "grad_coef_clip_not_clamped": ("return clip < 1.0 ? inv * clip : inv;", "return inv * clip;"),
+    "grad_coef_no_epsilon": ("max_norm / (norm + 1e-6)", "max_norm / norm"),
+    "scaler_backoff_keeps_count": ("*clean_steps = 0;\n        return;", "return;"),
+    "scaler_grows_every_step": ("if (*clean_steps == growth_interval) {", "if (1) {"),
+    "scaler_backoff_is_growth": ("*scale = *scale * backoff_factor;", "*scale = *scale * growth_factor;"),
+    "adamw_coef_ignored": ("double g = (double)grad[i] * coef;", "double g = (double)grad[i];"),
 }
 
 PIN_FILES = ["tests/test_oracle_pack.py", "tests/test_oracle_reduce.py",
              "tests/test_oracle_adamw.py", "tests/test_oracle_bf16_memory.py",
-             "tests/test_oracle_shard0.py"]
+             "tests/test_oracle_shard0.py", "tests/test_oracle_nosync_scaler.py"]
 
 
 @pytest.mark.slow
