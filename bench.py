@@ -402,6 +402,40 @@ def shard0_bench(cfg, dev, reps: int):
     return out
 
 
+def nosync_bench(cfg, dev, reps: int):
+    """Accumulation without communication over the rank's whole unit (T
+    elements of the workload, bf16 gradients, fp32 local buffer):
+    fp_local_accumulate of a later micro-batch (reads 2 + 4, writes 4 bytes
+    per element) and fp_local_finish (reads 2 + 4, writes 2)."""
+    import torch
+    import sharded_flatparameter_pack_amd as fp
+    from workloads import gen
+    T = sum(cfg.units())
+    grad = gen.torch_bf16_normal(T, 1e-3, cfg.seed, (gen.STREAM_GRAD,), dev)
+    local = torch.zeros(T, dtype=torch.float32, device=dev)
+    out = torch.empty(T, dtype=torch.int16, device=dev)
+    legs = {"local_accumulate": (lambda: fp.local_accumulate(grad, local, accumulate=True), 10 * T),
+            "local_finish": (lambda: fp.local_finish(grad, out, local, accumulate=True), 8 * T)}
+    res = {"workload": cfg.name, "elements": T, "n_micro": cfg.n_micro}
+    for name, (run, alg) in legs.items():
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = alg / (ms * 1e-3) / 1e9
+        res[name] = {"us_per_call": round(ms * 1e3, 2), "alg_bytes": alg, "GBps": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res["per_step"] = (f"a no_sync step of {cfg.n_micro} micro-batches runs {cfg.n_micro - 1} local "
+                       f"accumulations (the first without the fp32 read) and one finish per rank before "
+                       f"the shard step")
+    return res
+
+
 def copy_reference(fp, dev, reps: int = 20):
     """Measured plain-copy bandwidth (fp_unshard of 16 x 8M bf16 shards, 256 MiB each way)."""
     import torch
@@ -508,6 +542,8 @@ def main(argv=None) -> int:
                     help="only run fp_unshard (a plain copy of known size) for counter calibration")
     ap.add_argument("--dim0-only", action="store_true",
                     help="only time the per-parameter dim-0 layout's pack and unpack of the workload")
+    ap.add_argument("--nosync-only", action="store_true",
+                    help="only time the no_sync local accumulation kernels over the workload's unit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)
@@ -535,6 +571,9 @@ def main(argv=None) -> int:
             print(f"{cfg.name} has no parameter shapes", file=sys.stderr)
             return 2
         print(json.dumps(shard0_bench(cfg, dev, max(1, args.steps))), flush=True)
+        return 0
+    if args.nosync_only:
+        print(json.dumps(nosync_bench(cfg, dev, max(1, args.steps))), flush=True)
         return 0
     rank = cfg.ranks[0]
     world, n = cfg.world, cfg.n_micro
@@ -592,6 +631,9 @@ def main(argv=None) -> int:
             result["pack"] = pack_bench(cfg, dev, 20)
             torch.cuda.empty_cache()
             result["dim0_layout"] = shard0_bench(cfg, dev, 20)
+        if cfg.n_micro > 1:
+            torch.cuda.empty_cache()
+            result["no_sync"] = nosync_bench(cfg, dev, 10)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, rank, args.cpu_seconds)
     print(json.dumps(result), flush=True)

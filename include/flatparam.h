@@ -207,11 +207,17 @@ typedef struct fp_adamw_hparams {
  * If param_bf16 != NULL, param_bf16[i] = bf16 round-to-nearest-even of the
  * (new, or on a skip the unchanged) master[i] -- the low-precision copy
  * that the all-gather moves ([FSDP] section 3.5); usually full + rank * S.
+ * If grad_coef != NULL (device double, read when the kernel starts), g[i]
+ * above is grad[i] * *grad_coef: the unscale and clip factor of
+ * fp_grad_coef ([FSDP] section 3.5, sharded gradient scaler).  It is
+ * applied through the moment weights, (1 - beta1) k and (1 - beta2) k^2,
+ * which equals multiplying the gradient up to fp64 rounding.
  * grad, master, exp_avg, exp_avg_sq: device fp32[S], 16-byte aligned,
  * master / exp_avg / exp_avg_sq distinct; param_bf16: device bf16[S]. */
 fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, const float* grad,
                          float* master, float* exp_avg, float* exp_avg_sq,
-                         const int32_t* found_inf, uint16_t* param_bf16, void* stream);
+                         const int32_t* found_inf, uint16_t* param_bf16, const double* grad_coef,
+                         void* stream);
 
 /* ------------------------------------------------------------------ unshard */
 
@@ -279,6 +285,11 @@ typedef struct fp_step_args {
      * call records on `stream`: before its first kernel, between its first
      * and second kernel, and after its last kernel -- per-kernel timing. */
     void* const* profile_events;
+    /* device double or NULL: the gradient factor of fp_adamw_shard, read
+     * when the step's kernels start, so it cannot depend on this step's own
+     * norm (for clipping by it, use fp_reduce_shard, fp_grad_coef and
+     * fp_adamw_shard) -- the loss scaler's unscale factor, typically. */
+    const double* grad_coef;
 } fp_step_args;
 
 #define FP_STEP_EVENTS 3
@@ -364,6 +375,7 @@ typedef struct fp_units_step_args {
     void* workspace;               /* device, needed with sq_norm */
     int32_t flags;
     void* const* profile_events;
+    const double* grad_coef;       /* as in fp_step_args, may be NULL */
 } fp_units_step_args;
 fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream);
 
@@ -431,6 +443,49 @@ fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
  * fp_shard0_pack. */
 fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* full,
                            void* const* params, void* stream);
+
+/* ------------------------------------------------------------ no_sync, scaler */
+
+/* Gradient accumulation without communication.  [DP] "Naive Data
+ * Parallelism", gradient-accumulation paragraph: the first micro-batches'
+ * gradients are accumulated locally and only the last micro-batch
+ * synchronises (DDP's no_sync); [FSDP] section 3.4: accumulation without
+ * communication trades memory for fewer exchanges.  A rank keeps an fp32
+ * buffer `local` over its whole unit (n elements, 4 bytes each):
+ *   fp_local_accumulate: local[i] = (accumulate ? local[i] : 0) + f32(grad[i])
+ *     for each micro-batch but the last, in micro-batch order;
+ *   fp_local_finish: out[i] = bf16(local[i] + f32(grad[i])) (or bf16 of
+ *     grad[i] alone when accumulate == 0) for the last one, round to nearest
+ *     even: the bf16 row this rank contributes to the reduce-scatter, which
+ *     then runs as fp_reduce_shard / fp_shard_step with the usual scale
+ *     1 / (N_d n).  With one micro-batch the row is the gradient itself and
+ *     this call is not needed.
+ * grad, out: device bf16[n] (2-byte aligned); local: device fp32[n], 16-byte
+ * aligned; out may not overlap local or grad.  n >= 0. */
+fp_status fp_local_accumulate(int64_t n, const uint16_t* grad, int32_t accumulate, float* local,
+                              void* stream);
+fp_status fp_local_finish(int64_t n, const uint16_t* grad, int32_t accumulate, const float* local,
+                          uint16_t* out, void* stream);
+
+/* The factor AdamW applies to a loss-scaled reduced gradient (device
+ * double *coef): 1 / scale with scale = *loss_scale (1 when loss_scale is
+ * NULL), times min(1, max_norm / (||g|| + 1e-6)) with ||g|| =
+ * sqrt(*sq_norm) / scale when max_norm > 0 (global-norm clipping; sq_norm
+ * then required: this rank's Sum g^2 from the reduce, or the sum over ranks
+ * after their exchange).  [FSDP] section 3.5 (sharded gradient scaler); the
+ * pages give no policy, so the usual unscale-then-clip rule is used.  One
+ * lane, enqueued on `stream`. */
+fp_status fp_grad_coef(const double* sq_norm, const float* loss_scale, double max_norm, double* coef,
+                       void* stream);
+
+/* Dynamic loss scaling after a step's overflow decision (device values):
+ * if *found_inf != 0, *scale *= backoff_factor and *clean_steps = 0;
+ * otherwise ++*clean_steps, and when it reaches growth_interval,
+ * *scale *= growth_factor and *clean_steps = 0 (fp32 arithmetic).  The usual
+ * defaults are 2.0, 0.5 and 2000.  [FSDP] section 3.5; the policy is not on
+ * the pages.  growth_interval >= 1, factors > 0.  One lane, on `stream`. */
+fp_status fp_scaler_update(const int32_t* found_inf, float* scale, int32_t* clean_steps, float growth_factor,
+                           float backoff_factor, int32_t growth_interval, void* stream);
 
 /* ------------------------------------------------------------------ helpers */
 

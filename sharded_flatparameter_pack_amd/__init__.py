@@ -24,7 +24,7 @@ from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_ONE_PASS,  # noqa: F40
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
-__all__ = ["Plan", "Units", "Shard0Plan", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
+__all__ = ["Plan", "Units", "Shard0Plan", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
            "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "library_path"]
@@ -312,9 +312,14 @@ def _hparams(lr, beta1, beta2, eps, weight_decay, step):
                                  float(weight_decay), int(step))
 
 
+def _coef_ptr(grad_coef):
+    return _dev_ptr(grad_coef, (_torch().float64,), 1, "grad_coef") if grad_coef is not None else None
+
+
 def adamw_shard(grad, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps, weight_decay,
-                step: int, found_inf=None, param_bf16=None):
-    """In-place AdamW on fp32 master / exp_avg / exp_avg_sq; bf16 copy to param_bf16."""
+                step: int, found_inf=None, param_bf16=None, grad_coef=None):
+    """In-place AdamW on fp32 master / exp_avg / exp_avg_sq; bf16 copy to param_bf16.
+    grad_coef: optional device float64 factor applied to the gradient (see grad_coef())."""
     torch = _torch()
     S = master.numel()
     hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
@@ -322,7 +327,49 @@ def adamw_shard(grad, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps, wei
     out = _bf16(param_bf16, S, "param_bf16") if param_bf16 is not None else None
     check(lib().fp_adamw_shard(S, C.byref(hp), _f32(grad, S, "grad"), _f32(master, S, "master"),
                                _f32(exp_avg, S, "exp_avg"), _f32(exp_avg_sq, S, "exp_avg_sq"),
-                               fi, out, _stream(master)))
+                               fi, out, _coef_ptr(grad_coef), _stream(master)))
+
+
+# ------------------------------------------------------------------ no_sync and the loss scaler
+def local_accumulate(grad, local, *, accumulate: bool):
+    """local (fp32) = (local if accumulate else 0) + grad (bf16): one micro-batch
+    accumulated without communication."""
+    n = local.numel()
+    check(lib().fp_local_accumulate(n, _bf16(grad, n, "grad"), int(bool(accumulate)),
+                                    _f32(local, n, "local"), _stream(local)))
+    return local
+
+
+def local_finish(grad, out, local=None, *, accumulate: bool):
+    """out (bf16) = bf16(local + grad), or bf16(grad) when not accumulating: the
+    row this rank contributes to the reduce-scatter."""
+    n = out.numel()
+    lp = _f32(local, n, "local") if local is not None else None
+    check(lib().fp_local_finish(n, _bf16(grad, n, "grad"), int(bool(accumulate)), lp, _bf16(out, n, "out"),
+                                _stream(out)))
+    return out
+
+
+def grad_coef(coef, *, sq_norm=None, loss_scale=None, max_norm: float = 0.0):
+    """coef (device float64[1]) = 1 / loss_scale, times the global-norm clip
+    factor min(1, max_norm / (||g|| + 1e-6)) when max_norm > 0."""
+    torch = _torch()
+    sq = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
+    ls = _dev_ptr(loss_scale, (torch.float32,), 1, "loss_scale") if loss_scale is not None else None
+    check(lib().fp_grad_coef(sq, ls, float(max_norm), _dev_ptr(coef, (torch.float64,), 1, "coef"),
+                             _stream(coef)))
+    return coef
+
+
+def scaler_update(found_inf, scale, clean_steps, *, growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                  growth_interval: int = 2000):
+    """Dynamic loss scaling on device values after a step's overflow decision."""
+    torch = _torch()
+    check(lib().fp_scaler_update(_dev_ptr(found_inf, (torch.int32,), 1, "found_inf"),
+                                 _dev_ptr(scale, (torch.float32,), 1, "scale"),
+                                 _dev_ptr(clean_steps, (torch.int32,), 1, "clean_steps"),
+                                 float(growth_factor), float(backoff_factor), int(growth_interval),
+                                 _stream(scale)))
 
 
 # ------------------------------------------------------------------ unshard
@@ -341,12 +388,13 @@ def unshard(shards, full):
 # ------------------------------------------------------------------ step
 def shard_step(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *, scale: float,
                lr, beta1, beta2, eps, weight_decay, step: int, found_inf, accumulate: bool = False,
-               sq_norm=None, workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None):
+               sq_norm=None, workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None,
+               grad_coef=None):
     """Reduce (last micro-batch) + AdamW + bf16 cast + unshard for this rank."""
     ShardStep(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank, scale=scale, lr=lr,
               beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay, found_inf=found_inf,
               accumulate=accumulate, sq_norm=sq_norm, workspace=workspace,
-              flags=flags)(step, profile_events)
+              flags=flags, grad_coef=grad_coef)(step, profile_events)
 
 
 class ShardStep:
@@ -361,7 +409,7 @@ class ShardStep:
     def __init__(self, grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *,
                  scale: float, lr, beta1, beta2, eps, weight_decay, found_inf,
                  accumulate: bool = False, sq_norm=None, workspace=None,
-                 flags: int = FP_STEP_EXACT_SKIP):
+                 flags: int = FP_STEP_EXACT_SKIP, grad_coef=None):
         torch = _torch()
         S = master.numel()
         gptr = _rank_ptrs(grads, S, "grads")
@@ -384,6 +432,7 @@ class ShardStep:
         a.workspace = (_dev_ptr(workspace, (torch.uint8,), workspace_bytes(S), "workspace")
                        if workspace is not None else None)
         a.flags = int(flags)
+        a.grad_coef = _coef_ptr(grad_coef)
         self._args = a
         self._device = master.device
         self._fn = lib().fp_shard_step
@@ -499,7 +548,7 @@ class Units:
 
     def step(self, acc, master, exp_avg, exp_avg_sq, *, scale: float, lr, beta1, beta2, eps,
              weight_decay, step: int, found_inf, accumulate: bool = False, sq_norm=None,
-             workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None):
+             workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None, grad_coef=None):
         torch = _torch()
         P = self.partition
         a = _lib.fp_units_step_args()
@@ -511,6 +560,7 @@ class Units:
         a.sq_norm = self._opt(sq_norm, torch.float64, 1, "sq_norm")
         a.workspace = self._opt(workspace, torch.uint8, self.workspace_bytes, "workspace")
         a.flags = int(flags)
+        a.grad_coef = _coef_ptr(grad_coef)
         ev = None
         if profile_events is not None:
             if len(profile_events) != _lib.FP_STEP_EVENTS:

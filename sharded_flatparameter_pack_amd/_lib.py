@@ -47,14 +47,14 @@ class fp_step_args(C.Structure):
                 ("scale", _f32), ("accumulate", _i32), ("acc", _vp), ("master", _vp),
                 ("exp_avg", _vp), ("exp_avg_sq", _vp), ("hp", fp_adamw_hparams),
                 ("shards", _vp), ("full", _vp), ("found_inf", _vp), ("sq_norm", _vp),
-                ("workspace", _vp), ("flags", _i32), ("profile_events", _vp)]
+                ("workspace", _vp), ("flags", _i32), ("profile_events", _vp), ("grad_coef", _vp)]
 
 
 class fp_units_step_args(C.Structure):
     _fields_ = [("scale", _f32), ("accumulate", _i32), ("acc", _vp), ("master", _vp),
                 ("exp_avg", _vp), ("exp_avg_sq", _vp), ("hp", fp_adamw_hparams),
                 ("found_inf", _vp), ("sq_norm", _vp), ("workspace", _vp), ("flags", _i32),
-                ("profile_events", _vp)]
+                ("profile_events", _vp), ("grad_coef", _vp)]
 
 
 # name -> (restype, argtypes); the export test compares this table with the header
@@ -66,7 +66,7 @@ SIGNATURES = {
     "fp_unpack_views": (_i32, [_vp, _i32, _vp, _i32, _vp]),
     "fp_workspace_bytes": (_i64, [_i64]),
     "fp_reduce_shard": (_i32, [_i64, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp]),
-    "fp_adamw_shard": (_i32, [_i64, C.POINTER(fp_adamw_hparams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "fp_adamw_shard": (_i32, [_i64, C.POINTER(fp_adamw_hparams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp_unshard": (_i32, [_i64, _i32, _vp, _vp, _vp]),
     "fp_shard_step": (_i32, [C.POINTER(fp_step_args), _vp]),
     "fp_step_path": (_i32, [C.POINTER(fp_step_args), C.POINTER(C.c_int32)]),
@@ -82,6 +82,10 @@ SIGNATURES = {
     "fp_shard0_views": (_i32, [_vp, _i32, _vp, _i32, _vp]),
     "fp_shard0_pack": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "fp_shard0_unpack": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+    "fp_local_accumulate": (_i32, [_i64, _vp, _i32, _vp, _vp]),
+    "fp_local_finish": (_i32, [_i64, _vp, _i32, _vp, _vp, _vp]),
+    "fp_grad_coef": (_i32, [_vp, _vp, _f64, _vp, _vp]),
+    "fp_scaler_update": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp]),
     "fp_state_bytes": (_i32, [_f64, _i32, _f64, _i32, C.POINTER(_f64)]),
     "fp_status_string": (C.c_char_p, [_i32]),
     "fp_last_error": (C.c_char_p, []),

@@ -370,7 +370,8 @@ extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_
 
 extern "C" fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, const float* grad,
                                     float* master, float* exp_avg, float* exp_avg_sq,
-                                    const int32_t* found_inf, uint16_t* param_bf16, void* stream) {
+                                    const int32_t* found_inf, uint16_t* param_bf16, const double* grad_coef,
+                                    void* stream) {
     fp_status st;
     if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
     AdamArgs a;
@@ -392,6 +393,8 @@ extern "C" fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, c
             return fail(FP_ERR_INVALID, "param_bf16 overlaps the fp32 buffers");
     }
     if (found_inf != nullptr && !aligned(found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
+    if (grad_coef != nullptr && !aligned(grad_coef, 8)) return fail(FP_ERR_ALIGN, "grad_coef misaligned");
+    a.g_coef = grad_coef;
     a.grad = grad;
     a.master = master;
     a.exp_avg = exp_avg;
@@ -464,6 +467,7 @@ fp_status check_step(const fp_step_args& x, AdamCoef* c) {
         if (!aligned(x.sq_norm, 8)) return fail(FP_ERR_ALIGN, "sq_norm misaligned");
         if (x.workspace == nullptr) return fail(FP_ERR_INVALID, "sq_norm needs a workspace");
     }
+    if (x.grad_coef != nullptr && !aligned(x.grad_coef, 8)) return fail(FP_ERR_ALIGN, "grad_coef misaligned");
     const int64_t b4 = S * 4, b2 = S * 2, bf = S * x.world * 2;
     const void* f32s[4] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq};
     for (int i = 0; i < 4; ++i) {
@@ -534,6 +538,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     a.found_inf = x.found_inf;
     a.partials = x.sq_norm != nullptr ? partials_of(x.workspace) : nullptr;
     a.sq_norm = x.sq_norm;
+    a.g_coef = x.grad_coef;
     a.shard = S;
     a.scale = x.scale;
     a.world = x.world;
@@ -584,6 +589,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     d.found_inf = x.found_inf;
     d.shard = S;
     d.c = a.c;
+    d.g_coef = a.g_coef;
     d.partials = a.partials;
     d.sq_norm = x.sq_norm;
     d.n_partials = (int32_t)reduce_groups;
@@ -863,8 +869,10 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
         if (x.workspace == nullptr) return fail(FP_ERR_INVALID, "sq_norm needs a workspace");
         if (!aligned(x.workspace, 16)) return fail(FP_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
+    if (x.grad_coef != nullptr && !aligned(x.grad_coef, 8)) return fail(FP_ERR_ALIGN, "grad_coef misaligned");
     if ((st = check_units_device(units)) != FP_OK) return st;
     const bool no_skip = (x.flags & FP_STEP_NO_SKIP) != 0;
+    a.g_coef = x.grad_coef;
     a.acc = x.acc;
     a.master = x.master;
     a.exp_avg = x.exp_avg;
@@ -1288,6 +1296,80 @@ extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, c
     fp_status st = shard0_table(plan, kOpUnpack, elem_size, 0, &t);
     if (st != FP_OK) return st;
     return shard0_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------- no_sync, scaler
+
+namespace {
+fp_status local_call(int64_t n, const uint16_t* grad, int32_t accumulate, const float* local, uint16_t* out,
+                     bool finish, void* stream) {
+    if (n < 0) return fail(FP_ERR_RANGE, "n must be >= 0");
+    if (n == 0) return FP_OK;
+    if (grad == nullptr) return fail(FP_ERR_INVALID, "grad is NULL");
+    if (!aligned(grad, 2)) return fail(FP_ERR_ALIGN, "grad misaligned");
+    if (accumulate || !finish) {
+        fp_status st = check_f32(local, n, "local");
+        if (st != FP_OK) return st;
+        if (overlap(grad, n * 2, local, n * 4)) return fail(FP_ERR_INVALID, "grad overlaps local");
+    }
+    bool al = is_aligned8(grad);
+    if (finish) {
+        if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+        if (!aligned(out, 2)) return fail(FP_ERR_ALIGN, "out misaligned");
+        if (overlap(out, n * 2, grad, n * 2)) return fail(FP_ERR_INVALID, "out overlaps grad");
+        if (accumulate && overlap(out, n * 2, local, n * 4)) return fail(FP_ERR_INVALID, "out overlaps local");
+        al = al && is_aligned8(out);
+    }
+    LocalArgs a;
+    a.grad = grad;
+    a.local = const_cast<float*>(local);
+    a.out = out;
+    a.n = n;
+    hipError_t e = launch_local(a, finish, accumulate != 0, al, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "local accumulation launch");
+    return FP_OK;
+}
+}  // namespace
+
+extern "C" fp_status fp_local_accumulate(int64_t n, const uint16_t* grad, int32_t accumulate, float* local,
+                                         void* stream) {
+    return local_call(n, grad, accumulate, local, nullptr, false, stream);
+}
+
+extern "C" fp_status fp_local_finish(int64_t n, const uint16_t* grad, int32_t accumulate, const float* local,
+                                     uint16_t* out, void* stream) {
+    return local_call(n, grad, accumulate, local, out, true, stream);
+}
+
+extern "C" fp_status fp_grad_coef(const double* sq_norm, const float* loss_scale, double max_norm, double* coef,
+                                  void* stream) {
+    if (coef == nullptr) return fail(FP_ERR_INVALID, "coef is NULL");
+    if (!aligned(coef, 8)) return fail(FP_ERR_ALIGN, "coef misaligned");
+    if (!(max_norm == max_norm)) return fail(FP_ERR_INVALID, "max_norm is NaN");
+    if (max_norm > 0.0) {
+        if (sq_norm == nullptr) return fail(FP_ERR_INVALID, "clipping needs sq_norm");
+        if (!aligned(sq_norm, 8)) return fail(FP_ERR_ALIGN, "sq_norm misaligned");
+    }
+    if (loss_scale != nullptr && !aligned(loss_scale, 4)) return fail(FP_ERR_ALIGN, "loss_scale misaligned");
+    hipError_t e = launch_grad_coef(max_norm > 0.0 ? sq_norm : nullptr, loss_scale, max_norm, coef,
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "grad coef launch");
+    return FP_OK;
+}
+
+extern "C" fp_status fp_scaler_update(const int32_t* found_inf, float* scale, int32_t* clean_steps,
+                                      float growth_factor, float backoff_factor, int32_t growth_interval,
+                                      void* stream) {
+    if (found_inf == nullptr || scale == nullptr || clean_steps == nullptr)
+        return fail(FP_ERR_INVALID, "found_inf, scale and clean_steps are required");
+    if (!aligned(found_inf, 4) || !aligned(scale, 4) || !aligned(clean_steps, 4))
+        return fail(FP_ERR_ALIGN, "scaler values misaligned");
+    if (growth_interval < 1) return fail(FP_ERR_RANGE, "growth_interval must be >= 1");
+    if (!(growth_factor > 0.0f) || !(backoff_factor > 0.0f)) return fail(FP_ERR_RANGE, "factors must be > 0");
+    hipError_t e = launch_scaler_update(found_inf, scale, clean_steps, growth_factor, backoff_factor,
+                                        growth_interval, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "scaler update launch");
+    return FP_OK;
 }
 
 // ---------------------------------------------------------------------- helpers

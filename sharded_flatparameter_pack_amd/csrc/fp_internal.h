@@ -121,6 +121,7 @@ struct AdamArgs {
     const int32_t* found_inf;   // may be null: never skip
     int64_t shard;
     AdamCoef c;
+    const double* g_coef;       // factor applied to the gradient, may be null (1)
     // optional finalisation of the reduce's norm partials by workgroup 0
     const double* partials;
     double* sq_norm;
@@ -150,6 +151,7 @@ struct StepArgs {
     double* sq_norm;         // one-pass: finalised by workgroup 0 after the barrier
     int64_t shard;
     AdamCoef c;
+    const double* g_coef;    // factor applied to the gradient, may be null (1)
     float scale;
     int32_t world;
     int32_t rank;
@@ -197,6 +199,7 @@ struct UnitsArgs {
     double* partials;
     double* sq_norm;             // AdamW launch: finalised by workgroup 0
     AdamCoef c;
+    const double* g_coef;        // factor applied to the gradient, may be null (1)
     int64_t reduce_groups;
     int64_t record_bytes;
     float scale;
@@ -260,6 +263,14 @@ inline int64_t segment_tiles(const SegDesc& d) {
     return ceil_div64(d.len / 8 + 1, (int64_t)kThreads * kSegWords);
 }
 
+// Local accumulation without communication over n elements of a rank's unit.
+struct LocalArgs {
+    const uint16_t* grad;   // bf16[n]
+    float* local;           // fp32[n], 16-byte aligned (read only by the finish)
+    uint16_t* out;          // bf16[n] (finish)
+    int64_t n;
+};
+
 struct PackArgs {
     const int64_t* offsets;     // [n_tensors + 1] prefix sums, offsets[n] = T
     const int32_t* group_first; // [n_groups + 1] first tensor overlapping each group
@@ -289,6 +300,12 @@ hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool align
                             hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
 hipError_t launch_segments(const SegArgs& a, int64_t n_groups, hipStream_t s);
+hipError_t launch_local(const LocalArgs& a, bool finish, bool accumulate, bool aligned, hipStream_t s);
+hipError_t launch_grad_coef(const double* sq_norm, const float* loss_scale, double max_norm, double* coef,
+                            hipStream_t s);
+hipError_t launch_scaler_update(const int32_t* found_inf, float* scale, int32_t* clean_steps,
+                                float growth_factor, float backoff_factor, int32_t growth_interval,
+                                hipStream_t s);
 // Multi-unit launches: one micro-batch's reduce over all units; the last
 // micro-batch's reduce (+ AdamW when fused) with the copies of all units'
 // other shards (copy_groups workgroups after the reduce tiles); AdamW over

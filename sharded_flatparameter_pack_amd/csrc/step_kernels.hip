@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     }
 
     // reduce and speculative update, all in registers
+    const AdamCoef c = coef_for(a.c, a.g_coef);
     const Quads<kQ> Q = lane_quads<kQ>(blockIdx.x, nq > 0 ? nq : 1);
     State<kQ> st;
     uint2 old_bf16[kQ];
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
             check_quad(y[u], bad, sq, want_sq);
             if (a.keep_grad) st_f32q(a.acc, Q, u, y[u]);
         }
-        adamw_quads<kQ>(a.c, y, st);
+        adamw_quads<kQ>(c, y, st);
     }
     const int64_t tail0 = nq << 2;
     const bool has_tail = blockIdx.x == 0 && (int64_t)threadIdx.x < a.shard - tail0;
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
         bad |= !finite_f32(yt);
         if (want_sq) sq += (double)yt * (double)yt;
         if (a.keep_grad) a.acc[j] = yt;
-        adamw_elem(a.c, yt, tt, tm, tv);
+        adamw_elem(c, yt, tt, tm, tv);
     }
     FP_PHASE_MARK(1);
     const int group_bad = __syncthreads_or(bad);

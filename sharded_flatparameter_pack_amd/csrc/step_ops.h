@@ -239,6 +239,20 @@ __device__ __forceinline__ void adamw_elem(const AdamCoef& c, float g, float& th
     v = (float)vd;
 }
 
+// The coefficients for a gradient multiplied by k (the unscale and clip
+// factor of the loss scaler): (1 - beta1) k and (1 - beta2) k^2 take the
+// place of the moment weights, so the per-element arithmetic is unchanged.
+// k is a device value read when the workgroup starts (null: k = 1).
+__device__ __forceinline__ AdamCoef coef_for(const AdamCoef& c, const double* k) {
+    AdamCoef r = c;
+    if (k != nullptr) {
+        const double x = *k;
+        r.one_m_beta1 = c.one_m_beta1 * x;
+        r.one_m_beta2 = c.one_m_beta2 * x * x;
+    }
+    return r;
+}
+
 // The fp32 master and moments of a lane's kU quads.  Callers issue these
 // loads before anything they wait on (gradient quads, the overflow flag), so
 // that a wave pays one memory round trip, not two.
@@ -284,11 +298,12 @@ __device__ __forceinline__ void store_quads(const A& a, const Quads<kU>& Q, bool
 }
 
 template <class A>
-__device__ __forceinline__ void update_elem(const A& a, int64_t j, float y, bool skip, uint16_t* out) {
+__device__ __forceinline__ void update_elem(const A& a, const AdamCoef& c, int64_t j, float y, bool skip,
+                                            uint16_t* out) {
     float th = a.master[j];
     if (!skip) {
         float m = a.exp_avg[j], v = a.exp_avg_sq[j];
-        adamw_elem(a.c, y, th, m, v);
+        adamw_elem(c, y, th, m, v);
         a.master[j] = th;
         a.exp_avg[j] = m;
         a.exp_avg_sq[j] = v;
@@ -496,6 +511,7 @@ __device__ __forceinline__ void adamw_tile(const A& a, const float* grad, int64_
                                            const int32_t* found_inf, uint16_t* out) {
     constexpr int kU = kQuadsPerLane;
     const int64_t nq = a.shard >> 2;
+    const AdamCoef c = coef_for(a.c, a.g_coef);
     if (nq > 0) {
         const Quads<kU> Q = lane_quads<kU>(tile, nq);
         float g[kU][4];
@@ -504,14 +520,14 @@ __device__ __forceinline__ void adamw_tile(const A& a, const float* grad, int64_
         for (int u = 0; u < kU; ++u) ld_f32q(grad, Q, u, g[u]);
         load_state<kU>(a, Q, st);
         const bool skip = found_inf != nullptr && *found_inf != 0;
-        if (!skip) adamw_quads<kU>(a.c, g, st);
+        if (!skip) adamw_quads<kU>(c, g, st);
         store_quads<kAligned, kU>(a, Q, skip, st, out);
     }
     const int64_t tail0 = nq << 2;
     if (tile == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
         const int64_t j = tail0 + threadIdx.x;
         const bool skip = found_inf != nullptr && *found_inf != 0;
-        update_elem(a, j, skip ? 0.0f : grad[j], skip, out);
+        update_elem(a, c, j, skip ? 0.0f : grad[j], skip, out);
     }
 }
 
@@ -540,6 +556,7 @@ __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool 
     constexpr int kU = kQuadsPerLane;
     const int64_t nq = a.shard >> 2;
     const bool want_sq = partial != nullptr;
+    const AdamCoef c = coef_for(a.c, kFused ? a.g_coef : nullptr);
     bool bad = false;
     double sq = 0.0;
     if (nq > 0) {
@@ -555,7 +572,7 @@ __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool 
             if (!kFused || keep_grad) st_f32q(a.acc, Q, u, y[u]);
         }
         if (kFused) {
-            adamw_quads<kU>(a.c, y, st);
+            adamw_quads<kU>(c, y, st);
             store_quads<kAligned, kU>(a, Q, false, st, own);
         }
     }
@@ -566,7 +583,7 @@ __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool 
         bad |= !finite_f32(y);
         if (want_sq) sq += (double)y * (double)y;
         if (!kFused || keep_grad) a.acc[j] = y;
-        if (kFused) update_elem(a, j, y, false, own);
+        if (kFused) update_elem(a, c, j, y, false, own);
     }
     flag_if_any(bad, found_inf);
     if (want_sq) {

@@ -26,6 +26,7 @@ struct UnitView {
     int64_t tile0;
     int64_t copy0;
     AdamCoef c;
+    const double* g_coef;
     float scale;
     int32_t world;
     int32_t rank;
@@ -61,6 +62,7 @@ __device__ __forceinline__ UnitView unit_view(const UnitsArgs& a, int64_t group)
     v.tile0 = d.tile0;
     v.copy0 = d.copy0;
     v.c = a.c;
+    v.g_coef = a.g_coef;
     v.scale = a.scale;
     v.world = a.world;
     v.rank = a.rank;

@@ -52,7 +52,8 @@ def test_struct_layouts_match_the_header(fp):
     assert _lib.fp_step_args.grads.offset == 16
     assert _lib.fp_step_args.hp.offset == 64
     assert _lib.fp_step_args.flags.offset == 152
-    assert C.sizeof(_lib.fp_step_args) == 64 + 48 + 5 * 8 + 8 + 8
+    assert _lib.fp_step_args.grad_coef.offset == 64 + 48 + 5 * 8 + 8 + 8
+    assert C.sizeof(_lib.fp_step_args) == 64 + 48 + 5 * 8 + 8 + 8 + 8
 
 
 def _random_shapes(r):
@@ -163,14 +164,16 @@ def test_device_entry_points_reject_bad_arguments(fp):
 
     hp = _lib.fp_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0)
     ptr = [C.c_void_p(0x100000 * (i + 1)) for i in range(4)]
-    assert _status(L.fp_adamw_shard, 64, C.byref(hp), *ptr, None, None, None) == -2  # step 0
+    assert _status(L.fp_adamw_shard, 64, C.byref(hp), *ptr, None, None, None, None) == -2  # step 0
     hp.step, hp.beta2 = 1, 1.0
-    assert _status(L.fp_adamw_shard, 64, C.byref(hp), *ptr, None, None, None) == -2  # beta2 = 1
+    assert _status(L.fp_adamw_shard, 64, C.byref(hp), *ptr, None, None, None, None) == -2  # beta2 = 1
     hp.beta2 = 0.999
-    assert _status(L.fp_adamw_shard, 64, C.byref(hp), ptr[0], ptr[1], ptr[1], ptr[3], None, None, None) == -1
+    assert _status(L.fp_adamw_shard, 64, C.byref(hp), ptr[0], ptr[1], ptr[1], ptr[3], None, None, None,
+                   None) == -1
     assert _status(L.fp_adamw_shard, 64, C.byref(hp), ptr[0], C.c_void_p(0x200008), ptr[2], ptr[3],
-                   None, None, None) == -3
-    assert _status(L.fp_adamw_shard, 64, None, *ptr, None, None, None) == -1
+                   None, None, None, None) == -3
+    assert _status(L.fp_adamw_shard, 64, None, *ptr, None, None, None, None) == -1
+    assert _status(L.fp_adamw_shard, 64, C.byref(hp), *ptr, None, None, C.c_void_p(0x300004), None) == -3
 
     sh = (C.c_void_p * 2)(0x10000, 0x20000)
     assert _status(L.fp_unshard, 16, 2, sh, C.c_void_p(0x10010), None) == -1   # source inside full
@@ -305,3 +308,34 @@ def test_shard0_validation_without_a_device(fp):
     assert _status(L.fp_shard0_unpack, None, 2, dst, p, None) == -1
     assert _status(L.fp_shard0_plan_info, None, None, None) == -1
     L.fp_shard0_plan_destroy(None)
+
+
+def test_local_and_scaler_validation_without_a_device(fp):
+    """no_sync accumulation, the gradient factor and the loss-scale update
+    reject bad arguments before any launch (fake addresses)."""
+    L = fp.lib()
+    g, loc, out = C.c_void_p(0x100000), C.c_void_p(0x200000), C.c_void_p(0x300000)
+    assert _status(L.fp_local_accumulate, -1, g, 0, loc, None) == -2
+    assert _status(L.fp_local_accumulate, 0, None, 0, None, None) == 0          # nothing to do
+    assert _status(L.fp_local_accumulate, 16, None, 0, loc, None) == -1
+    assert _status(L.fp_local_accumulate, 16, C.c_void_p(0x100001), 0, loc, None) == -3
+    assert _status(L.fp_local_accumulate, 16, g, 1, C.c_void_p(0x200008), None) == -3
+    assert _status(L.fp_local_accumulate, 16, g, 1, None, None) == -1
+    assert _status(L.fp_local_accumulate, 16, C.c_void_p(0x200010), 1, loc, None) == -1   # grad inside local
+    assert _status(L.fp_local_finish, 16, g, 1, loc, None, None) == -1
+    assert _status(L.fp_local_finish, 16, g, 1, None, out, None) == -1                      # accumulate needs local
+    assert _status(L.fp_local_finish, 16, g, 0, None, C.c_void_p(0x300001), None) == -3
+    assert _status(L.fp_local_finish, 16, g, 0, None, C.c_void_p(0x100008), None) == -1     # out overlaps grad
+    assert _status(L.fp_local_finish, 16, g, 1, loc, C.c_void_p(0x200010), None) == -1      # out overlaps local
+    coef, sq, ls = C.c_void_p(0x400000), C.c_void_p(0x500000), C.c_void_p(0x600000)
+    assert _status(L.fp_grad_coef, sq, ls, 1.0, None, None) == -1
+    assert _status(L.fp_grad_coef, sq, ls, 1.0, C.c_void_p(0x400004), None) == -3
+    assert _status(L.fp_grad_coef, None, ls, 1.0, coef, None) == -1                # clipping needs the norm
+    assert _status(L.fp_grad_coef, C.c_void_p(0x500004), ls, 1.0, coef, None) == -3
+    assert _status(L.fp_grad_coef, None, C.c_void_p(0x600002), 0.0, coef, None) == -3
+    assert _status(L.fp_grad_coef, None, None, float("nan"), coef, None) == -1
+    fi, sc, cs = C.c_void_p(0x700000), C.c_void_p(0x700010), C.c_void_p(0x700020)
+    assert _status(L.fp_scaler_update, None, sc, cs, 2.0, 0.5, 2000, None) == -1
+    assert _status(L.fp_scaler_update, fi, sc, cs, 2.0, 0.5, 0, None) == -2
+    assert _status(L.fp_scaler_update, fi, sc, cs, 0.0, 0.5, 10, None) == -2
+    assert _status(L.fp_scaler_update, fi, C.c_void_p(0x700011), cs, 2.0, 0.5, 10, None) == -3
