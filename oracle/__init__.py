@@ -42,6 +42,7 @@ def lib():
                 "or_f32_to_bf16": (C.c_uint16, [_f32]),
                 "or_f32_to_bf16_array": (None, [_i64, _vp, _vp]),
                 "or_reduce": (None, [_i64, _i32, _vp, _f32, _i32, _vp]),
+                "or_reduce_hybrid": (None, [_i64, _i32, _i32, _vp, _f32, _i32, _vp]),
                 "or_found_inf": (_i32, [_i64, _vp]),
                 "or_sq_norm": (_f64, [_i64, _vp]),
                 "or_adamw": (None, [_i64, _f64, _f64, _f64, _f64, _f64, _i64,
@@ -195,6 +196,22 @@ def reduce(grads, scale: float, acc: np.ndarray = None, accumulate: bool = False
     acc = _c(acc, np.float32)
     lib().or_reduce(S, len(grads), _ptr_table(grads), np.float32(scale), int(bool(accumulate)),
                     _ptr(acc))
+    return acc
+
+
+def reduce_hybrid(grads, group: int, scale: float, acc: np.ndarray = None,
+                  accumulate: bool = False) -> np.ndarray:
+    """Two-level reduce of hybrid sharding: sums inside each group of `group`
+    ranks, then across the groups, then one multiply by scale."""
+    rows = [_c(g, np.uint16) for g in grads]
+    S = rows[0].size
+    if len(rows) % group != 0:
+        raise ValueError("world must be a multiple of the group size")
+    if acc is None:
+        acc = np.zeros(S, np.float32)
+    _c(acc, np.float32)
+    lib().or_reduce_hybrid(S, len(rows), int(group), _ptr_table(rows), np.float32(scale),
+                           int(bool(accumulate)), _ptr(acc))
     return acc
 
 

@@ -293,6 +293,35 @@ void or_reduce(int64_t shard, int32_t world, const uint16_t* const* grads,
     }
 }
 
+/* Hybrid sharding with factor F ([FSDP] section 3.3 and the sharding-factor */
+/* bullet: groups of F GPUs fully shard, the W/F groups replicate; [GUIDE]  */
+/* HYBRID_SHARD: reduce-scatter inside the group, all-reduce across the     */
+/* groups).  The unit is split into F slices; rank (group g, position p)    */
+/* owns slice p, and its reduced gradient averages all W ranks' gradients   */
+/* of that slice in two levels: each group's F gradients summed in rank     */
+/* order, then the W/F group sums in group order, then one multiply by the  */
+/* scale (1/(W n)).  grads[g*F + j] is rank j of group g.  F = W (one group) */
+/* and F = 1 (one rank per group) are the flat rank order above.            */
+void or_reduce_hybrid(int64_t shard, int32_t world, int32_t group, const uint16_t* const* grads,
+                      float scale, int32_t accumulate, float* acc)
+{
+    int32_t n_groups = world / group;
+    for (int64_t i = 0; i < shard; ++i) {
+        float total = 0.0f;
+        for (int32_t g = 0; g < n_groups; ++g) {
+            float part = or_bf16_to_f32(grads[g * group][i]);
+            for (int32_t j = 1; j < group; ++j)
+                part = part + or_bf16_to_f32(grads[g * group + j][i]);
+            total = g == 0 ? part : total + part;
+        }
+        float y = total * scale;
+        if (accumulate)
+            acc[i] = acc[i] + y;
+        else
+            acc[i] = y;
+    }
+}
+
 /* Overflow check of the sharded gradient scaler ([FSDP] section 3.5): 1 if
  * any reduced gradient element is +-inf or NaN. */
 int32_t or_found_inf(int64_t n, const float* acc)

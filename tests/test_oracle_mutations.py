@@ -63,11 +63,16 @@ MUTATIONS = {
     "scaler_grows_every_step": ("if (*clean_steps == growth_interval) {", "if (1) {"),
     "scaler_backoff_is_growth": ("*scale = *scale * backoff_factor;", "*scale = *scale * growth_factor;"),
     "adamw_coef_ignored": ("double g = (double)grad[i] * coef;", "double g = (double)grad[i];"),
+    "hybrid_total_from_plus_zero": ("total = g == 0 ? part : total + part;", "total = total + part;"),
+    "hybrid_strided_groups": ("grads[g * group + j][i]", "grads[j * n_groups + g][i]"),
+    "hybrid_sum_not_mean": ("float y = total * scale;", "float y = total;"),
+    "hybrid_last_group_dropped": ("for (int32_t g = 0; g < n_groups; ++g) {", "for (int32_t g = 0; g < n_groups - (n_groups > 1); ++g) {"),
 }
 
 PIN_FILES = ["tests/test_oracle_pack.py", "tests/test_oracle_reduce.py",
              "tests/test_oracle_adamw.py", "tests/test_oracle_bf16_memory.py",
-             "tests/test_oracle_shard0.py", "tests/test_oracle_nosync_scaler.py"]
+             "tests/test_oracle_shard0.py", "tests/test_oracle_nosync_scaler.py",
+             "tests/test_oracle_hybrid.py"]
 
 
 @pytest.mark.slow
