@@ -178,6 +178,27 @@ fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_t* const* g
                           float scale, int32_t accumulate, float* acc, int32_t* found_inf,
                           double* sq_norm, void* workspace, void* stream);
 
+/* The reduce of hybrid sharding with sharding factor F = group.  [FSDP]
+ * section 3.3 and the sharding-factor bullet (groups of F GPUs fully shard,
+ * the W / F groups replicate; F = 1 is DDP, F = W full sharding); [GUIDE]
+ * HYBRID_SHARD row and tip (reduce-scatter inside the group, all-reduce
+ * across groups).  The unit is planned with world = F (fp_plan_create), so
+ * S = P / F and a rank at position p of its group owns slice p.  grads:
+ * host array of world = W device pointers to the W ranks' bf16 gradients
+ * over that slice; entry g * F + j is rank j of group g.  For each i:
+ *   t_g = f32(g[gF][i]) + ... + f32(g[gF + F - 1][i])   (rank order, fp32)
+ *   s = t_0 + t_1 + ... + t_{W/F - 1}                     (group order, fp32)
+ *   y = s * scale (normally 1 / (W n)); acc as in fp_reduce_shard.
+ * The two levels are the intra-group reduce-scatter and the inter-group
+ * all-reduce, summed exactly in fp32 with no intermediate rounding; F = W
+ * and F = 1 give fp_reduce_shard's order.  Everything else (flag, norm,
+ * alignment, workspace) as fp_reduce_shard.  FP_ERR_RANGE unless F divides
+ * W.  The AdamW, cast and unshard of a hybrid step are fp_adamw_shard and
+ * fp_unshard with world = F. */
+fp_status fp_reduce_shard_hybrid(int64_t shard, int32_t world, int32_t group, const uint16_t* const* grads,
+                                 float scale, int32_t accumulate, float* acc, int32_t* found_inf,
+                                 double* sq_norm, void* workspace, void* stream);
+
 /* ------------------------------------------------------------------ adamw */
 
 /* Hyperparameters in fp64; the library derives every coefficient in fp64. */

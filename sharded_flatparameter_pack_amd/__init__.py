@@ -24,7 +24,7 @@ from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_ONE_PASS,  # noqa: F40
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
-__all__ = ["Plan", "Units", "Shard0Plan", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
+__all__ = ["Plan", "Units", "Shard0Plan", "reduce_shard_hybrid", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
            "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "library_path"]
@@ -303,6 +303,22 @@ def reduce_shard(grads, acc, *, scale: float, accumulate: bool = False, found_in
     ws = _dev_ptr(workspace, (torch.uint8,), workspace_bytes(S), "workspace") if workspace is not None else None
     check(lib().fp_reduce_shard(S, len(ptrs), _ptr_table(ptrs), float(scale), int(bool(accumulate)),
                                 C.c_void_p(_f32(acc, S, "acc")), fi, sq, ws, _stream(acc)))
+    return acc
+
+
+def reduce_shard_hybrid(grads, acc, *, group: int, scale: float, accumulate: bool = False, found_inf=None,
+                        sq_norm=None, workspace=None):
+    """acc (= or +=) scale * two-level sum of the W ranks' bf16 gradients: inside
+    each group of `group` consecutive ranks, then across the groups."""
+    torch = _torch()
+    S = acc.numel()
+    ptrs = _rank_ptrs(grads, S, "grads")
+    fi = _dev_ptr(found_inf, (torch.int32,), 1, "found_inf") if found_inf is not None else None
+    sq = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
+    ws = _dev_ptr(workspace, (torch.uint8,), workspace_bytes(S), "workspace") if workspace is not None else None
+    check(lib().fp_reduce_shard_hybrid(S, len(ptrs), int(group), _ptr_table(ptrs), float(scale),
+                                       int(bool(accumulate)), C.c_void_p(_f32(acc, S, "acc")), fi, sq, ws,
+                                       _stream(acc)))
     return acc
 
 

@@ -66,6 +66,7 @@ SIGNATURES = {
     "fp_unpack_views": (_i32, [_vp, _i32, _vp, _i32, _vp]),
     "fp_workspace_bytes": (_i64, [_i64]),
     "fp_reduce_shard": (_i32, [_i64, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "fp_reduce_shard_hybrid": (_i32, [_i64, _i32, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "fp_adamw_shard": (_i32, [_i64, C.POINTER(fp_adamw_hparams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp_unshard": (_i32, [_i64, _i32, _vp, _vp, _vp]),
     "fp_shard_step": (_i32, [C.POINTER(fp_step_args), _vp]),

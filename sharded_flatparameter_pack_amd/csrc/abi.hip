@@ -329,9 +329,11 @@ extern "C" int64_t fp_workspace_bytes(int64_t shard) {
     return kWorkspaceHeader + 8 * partial_slots(shard);
 }
 
-extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_t* const* grads,
-                                     float scale, int32_t accumulate, float* acc, int32_t* found_inf,
-                                     double* sq_norm, void* workspace, void* stream) {
+namespace {
+// Checks of the reduce's arguments and the filled kernel arguments.
+fp_status reduce_args(int64_t shard, int32_t world, const uint16_t* const* grads, float scale, int32_t accumulate,
+                      float* acc, int32_t* found_inf, double* sq_norm, void* workspace, ReduceArgs* a,
+                      bool* aligned_grads) {
     fp_status st;
     if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
     if ((st = check_world(world)) != FP_OK) return st;
@@ -345,28 +347,58 @@ extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_
     }
     for (int32_t q = 0; q < world; ++q)
         if (overlap(grads[q], shard * 2, acc, shard * 4)) return fail(FP_ERR_INVALID, "grads[%d] overlaps acc", q);
+    for (int32_t q = 0; q < world; ++q) a->grads[q] = grads[q];
+    a->acc = acc;
+    a->found_inf = found_inf;
+    a->partials = sq_norm != nullptr ? partials_of(workspace) : nullptr;
+    a->shard = shard;
+    a->scale = scale;
+    a->world = world;
+    a->accumulate = accumulate ? 1 : 0;
+    bool al = true;
+    for (int32_t q = 0; q < world; ++q) al = al && is_aligned8(grads[q]);
+    *aligned_grads = al;
+    return FP_OK;
+}
+}  // namespace
+
+extern "C" fp_status fp_reduce_shard(int64_t shard, int32_t world, const uint16_t* const* grads,
+                                     float scale, int32_t accumulate, float* acc, int32_t* found_inf,
+                                     double* sq_norm, void* workspace, void* stream) {
     ReduceArgs a;
     std::memset(&a, 0, sizeof a);
-    for (int32_t q = 0; q < world; ++q) a.grads[q] = grads[q];
-    a.acc = acc;
-    a.found_inf = found_inf;
-    a.partials = sq_norm != nullptr ? partials_of(workspace) : nullptr;
-    a.shard = shard;
-    a.scale = scale;
-    a.world = world;
-    a.accumulate = accumulate ? 1 : 0;
-    bool aligned = true;
-    for (int32_t q = 0; q < world; ++q) aligned = aligned && is_aligned8(grads[q]);
+    bool al = false;
+    fp_status st = reduce_args(shard, world, grads, scale, accumulate, acc, found_inf, sq_norm, workspace, &a, &al);
+    if (st != FP_OK) return st;
     const int64_t grid = stream_grid(shard);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_reduce(a, grid, aligned, s);
+    hipError_t e = launch_reduce(a, grid, al, s);
     if (e != hipSuccess) return device_fail(e, "reduce launch");
     if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)grid, sq_norm, s)) != hipSuccess)
         return device_fail(e, "norm launch");
     return FP_OK;
 }
 
-// ---------------------------------------------------------------------- adamw
+extern "C" fp_status fp_reduce_shard_hybrid(int64_t shard, int32_t world, int32_t group,
+                                            const uint16_t* const* grads, float scale, int32_t accumulate,
+                                            float* acc, int32_t* found_inf, double* sq_norm, void* workspace,
+                                            void* stream) {
+    if (group < 1 || group > world || (world > 0 && world % group != 0))
+        return fail(FP_ERR_RANGE, "group %d must divide world %d", group, world);
+    HybridArgs a;
+    std::memset(&a, 0, sizeof a);
+    bool al = false;
+    fp_status st = reduce_args(shard, world, grads, scale, accumulate, acc, found_inf, sq_norm, workspace, &a, &al);
+    if (st != FP_OK) return st;
+    a.group = group;
+    const int64_t grid = stream_grid(shard);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_reduce_hybrid(a, grid, al, s);
+    if (e != hipSuccess) return device_fail(e, "hybrid reduce launch");
+    if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)grid, sq_norm, s)) != hipSuccess)
+        return device_fail(e, "norm launch");
+    return FP_OK;
+}
 
 extern "C" fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, const float* grad,
                                     float* master, float* exp_avg, float* exp_avg_sq,

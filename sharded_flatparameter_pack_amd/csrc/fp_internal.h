@@ -71,6 +71,12 @@ struct ReduceArgs {
     int32_t accumulate;
 };
 
+// The reduce of hybrid sharding: world = W ranks in groups of `group` = F
+// consecutive ranks; the order is two-level (see hybrid_kernels.hip).
+struct HybridArgs : ReduceArgs {
+    int32_t group;
+};
+
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t tiles_of(int64_t quads) { return ceil_div64(quads, kTileQuads); }
 // Copy tiles per shard: the whole 16-byte words of a shard number at most S/8 + 1.
@@ -300,6 +306,7 @@ hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool align
                             hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
 hipError_t launch_segments(const SegArgs& a, int64_t n_groups, hipStream_t s);
+hipError_t launch_reduce_hybrid(const HybridArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_local(const LocalArgs& a, bool finish, bool accumulate, bool aligned, hipStream_t s);
 hipError_t launch_grad_coef(const double* sq_norm, const float* loss_scale, double max_norm, double* coef,
                             hipStream_t s);

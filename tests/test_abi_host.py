@@ -339,3 +339,16 @@ def test_local_and_scaler_validation_without_a_device(fp):
     assert _status(L.fp_scaler_update, fi, sc, cs, 2.0, 0.5, 0, None) == -2
     assert _status(L.fp_scaler_update, fi, sc, cs, 0.0, 0.5, 10, None) == -2
     assert _status(L.fp_scaler_update, fi, C.c_void_p(0x700011), cs, 2.0, 0.5, 10, None) == -3
+
+
+def test_hybrid_validation_without_a_device(fp):
+    L = fp.lib()
+    g = (C.c_void_p * 4)(0x10000, 0x20000, 0x30000, 0x40000)
+    acc = C.c_void_p(0x50000)
+    assert _status(L.fp_reduce_shard_hybrid, 16, 4, 3, g, 1.0, 0, acc, None, None, None, None) == -2
+    assert _status(L.fp_reduce_shard_hybrid, 16, 4, 0, g, 1.0, 0, acc, None, None, None, None) == -2
+    assert _status(L.fp_reduce_shard_hybrid, 16, 4, 8, g, 1.0, 0, acc, None, None, None, None) == -2
+    assert _status(L.fp_reduce_shard_hybrid, 16, 4, 2, g, 1.0, 0, C.c_void_p(0x50004), None, None, None,
+                   None) == -3
+    g_null = (C.c_void_p * 4)(0x10000, None, 0x30000, 0x40000)
+    assert _status(L.fp_reduce_shard_hybrid, 16, 4, 2, g_null, 1.0, 0, acc, None, None, None, None) == -1
