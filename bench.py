@@ -436,6 +436,40 @@ def nosync_bench(cfg, dev, reps: int):
     return res
 
 
+def hybrid_bench(cfg, dev, reps: int, replicas: int = 2):
+    """The hybrid-sharding reduce of the workload's unit with sharding factor
+    F = N_d and W = replicas * F ranks (groups of F, e.g. one 8-GPU node per
+    group): one micro-batch's fp_reduce_shard_hybrid over the W ranks' bf16
+    rows of this rank's slice, against fp_reduce_shard over the same rows
+    (the flat order)."""
+    import torch
+    import sharded_flatparameter_pack_amd as fp
+    from workloads import gen
+    F = cfg.world
+    W = replicas * F
+    S = fp.Plan(cfg.shapes, F).shard if cfg.shapes is not None else cfg.units()[0] // F
+    rows = gen.torch_bf16_normal(W * S, 1e-3, cfg.seed, (gen.STREAM_GRAD,), dev).view(W, S)
+    acc = torch.zeros(S, dtype=torch.float32, device=dev)
+    legs = {"hybrid": lambda: fp.reduce_shard_hybrid(rows, acc, group=F, scale=1.0 / W),
+            "flat_same_rows": lambda: fp.reduce_shard(rows, acc, scale=1.0 / W)}
+    alg = (2 * W + 4) * S
+    res = {"workload": cfg.name, "W": W, "F": F, "shard_elems": S, "alg_bytes": alg}
+    for name, run in legs.items():
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = alg / (ms * 1e-3) / 1e9
+        res[name] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def copy_reference(fp, dev, reps: int = 20):
     """Measured plain-copy bandwidth (fp_unshard of 16 x 8M bf16 shards, 256 MiB each way)."""
     import torch
@@ -544,6 +578,8 @@ def main(argv=None) -> int:
                     help="only time the per-parameter dim-0 layout's pack and unpack of the workload")
     ap.add_argument("--nosync-only", action="store_true",
                     help="only time the no_sync local accumulation kernels over the workload's unit")
+    ap.add_argument("--hybrid-only", action="store_true",
+                    help="only time the hybrid-sharding reduce (F = N_d, W = 2F) against the flat one")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)
@@ -571,6 +607,9 @@ def main(argv=None) -> int:
             print(f"{cfg.name} has no parameter shapes", file=sys.stderr)
             return 2
         print(json.dumps(shard0_bench(cfg, dev, max(1, args.steps))), flush=True)
+        return 0
+    if args.hybrid_only:
+        print(json.dumps(hybrid_bench(cfg, dev, max(1, args.steps))), flush=True)
         return 0
     if args.nosync_only:
         print(json.dumps(nosync_bench(cfg, dev, max(1, args.steps))), flush=True)
@@ -631,6 +670,8 @@ def main(argv=None) -> int:
             result["pack"] = pack_bench(cfg, dev, 20)
             torch.cuda.empty_cache()
             result["dim0_layout"] = shard0_bench(cfg, dev, 20)
+            torch.cuda.empty_cache()
+            result["hybrid_reduce"] = hybrid_bench(cfg, dev, 20)
         if cfg.n_micro > 1:
             torch.cuda.empty_cache()
             result["no_sync"] = nosync_bench(cfg, dev, 10)

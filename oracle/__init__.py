@@ -43,6 +43,7 @@ def lib():
                 "or_f32_to_bf16_array": (None, [_i64, _vp, _vp]),
                 "or_reduce": (None, [_i64, _i32, _vp, _f32, _i32, _vp]),
                 "or_reduce_hybrid": (None, [_i64, _i32, _i32, _vp, _f32, _i32, _vp]),
+                "or_reshard": (None, [_i64, _i32, _i32, _i32, _i32, _vp, _vp]),
                 "or_found_inf": (_i32, [_i64, _vp]),
                 "or_sq_norm": (_f64, [_i64, _vp]),
                 "or_adamw": (None, [_i64, _f64, _f64, _f64, _f64, _f64, _i64,
@@ -167,6 +168,22 @@ def shard0_unpack(full: np.ndarray, shapes, world: int):
                            _ptr(full if full.size else np.zeros(1, full.dtype)),
                            _ptr_table([o.reshape(-1) if o.size else np.zeros(1, full.dtype) for o in outs]))
     return outs
+
+
+def reshard(old_shards, numel: int, world_new: int, new_rank: int = -1) -> np.ndarray:
+    """The new ranks' shards (new_rank = -1: all, concatenated) of a flat buffer
+    of numel elements held as len(old_shards) old shards."""
+    rows = [np.ascontiguousarray(x) for x in old_shards]
+    dtype = rows[0].dtype
+    if dtype.itemsize not in (2, 4) or any(r.dtype != dtype for r in rows):
+        raise TypeError("reshard needs shards of one 2- or 4-byte dtype")
+    N = len(rows)
+    s_new = -(-numel // world_new)
+    n_out = s_new * (world_new if new_rank < 0 else 1)
+    out = np.empty(max(n_out, 1), dtype=dtype)
+    lib().or_reshard(int(numel), N, int(world_new), dtype.itemsize, int(new_rank),
+                     _ptr_table([r if r.size else np.zeros(1, dtype) for r in rows]), _ptr(out))
+    return out[:n_out]
 
 
 # ---------------------------------------------------------------- bf16

@@ -234,6 +234,37 @@ void or_shard0_unpack(int32_t n, const int32_t* ndims, const int64_t* shapes,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Resharding a flat buffer from N to N' ranks.  [DP] FSDP2 checkpoint      */
+/* paragraphs: a sharded checkpoint may be loaded into a different number   */
+/* of ranks.  The flat buffer (T elements, then zero padding) is the same;  */
+/* only the cut changes: new rank q' holds flat[q'S', (q'+1)S'), read from  */
+/* the old shards (old rank q holds flat[qS, (q+1)S)), zeros past T.        */
+/* new_rank = -1 writes every new rank's shard, one after the other.        */
+/* ------------------------------------------------------------------------ */
+
+void or_reshard(int64_t t, int32_t world_old, int32_t world_new, int32_t elem_size, int32_t new_rank,
+                const void* const* old_shards, void* out)
+{
+    int64_t s_old = (t + world_old - 1) / world_old;
+    int64_t s_new = (t + world_new - 1) / world_new;
+    int32_t q0 = new_rank < 0 ? 0 : new_rank;
+    int32_t q1 = new_rank < 0 ? world_new : new_rank + 1;
+    unsigned char* o = (unsigned char*)out;
+    int64_t k = 0;
+    for (int32_t q = q0; q < q1; ++q) {
+        for (int64_t j = 0; j < s_new; ++j, ++k) {
+            int64_t e = (int64_t)q * s_new + j;
+            if (e < t) {
+                const unsigned char* src = (const unsigned char*)old_shards[e / s_old];
+                memcpy(o + k * elem_size, src + (e % s_old) * elem_size, (size_t)elem_size);
+            } else {
+                memset(o + k * elem_size, 0, (size_t)elem_size);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* bf16 <-> fp32.  A bf16 value is the upper half of an fp32 bit pattern.   */
 /* ------------------------------------------------------------------------ */
 

@@ -66,13 +66,17 @@ MUTATIONS = {
     "hybrid_total_from_plus_zero": ("total = g == 0 ? part : total + part;", "total = total + part;"),
     "hybrid_strided_groups": ("grads[g * group + j][i]", "grads[j * n_groups + g][i]"),
     "hybrid_sum_not_mean": ("float y = total * scale;", "float y = total;"),
+    "reshard_old_rank_by_new_size": ("old_shards[e / s_old]", "old_shards[e / s_new]"),
+    "reshard_copies_old_padding": ("if (e < t) {\n                const unsigned char* src", "if (e < (int64_t)world_old * s_old) {\n                const unsigned char* src"),
+    "reshard_offset_in_old_wrong": ("(e % s_old) * elem_size", "(e % s_new) * elem_size"),
+    "reshard_new_size_rounded_down": ("int64_t s_new = (t + world_new - 1) / world_new;", "int64_t s_new = t / world_new;"),
     "hybrid_last_group_dropped": ("for (int32_t g = 0; g < n_groups; ++g) {", "for (int32_t g = 0; g < n_groups - (n_groups > 1); ++g) {"),
 }
 
 PIN_FILES = ["tests/test_oracle_pack.py", "tests/test_oracle_reduce.py",
              "tests/test_oracle_adamw.py", "tests/test_oracle_bf16_memory.py",
              "tests/test_oracle_shard0.py", "tests/test_oracle_nosync_scaler.py",
-             "tests/test_oracle_hybrid.py"]
+             "tests/test_oracle_hybrid.py", "tests/test_oracle_reshard.py"]
 
 
 @pytest.mark.slow
