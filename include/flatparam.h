@@ -465,6 +465,33 @@ fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
 fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* full,
                            void* const* params, void* stream);
 
+/* ------------------------------------------------------------------ reshard */
+
+/* Resharding a flat buffer from N to N' ranks: [DP] FSDP2 checkpoint
+ * paragraphs (a sharded checkpoint may be loaded into a different number of
+ * ranks).  The flat buffer of T elements is cut into N shards of
+ * S = ceil(T / N) (old rank q holds flat[qS, (q+1)S), zeros past T) and is to
+ * be cut into N' shards of S' = ceil(T / N').  New rank q' receives
+ * flat[q'S' + k] for k < S', read from the old shards, and zeros past T
+ * (the old shards' padding is never read).  The same copy serves the fp32
+ * master and moments (elem_size 4) and the bf16 parameters (elem_size 2) of
+ * a FlatParameter; the geometry is fp_plan's (T, world), so S and S' are the
+ * shard sizes fp_plan_info reports for N and N'.
+ * fp_reshard_plan_create: T in [0, 2^40], N and N' in [1, 2^20]; host only.
+ * fp_reshard: new_rank in [0, N') writes that rank's S' elements to dst;
+ *   new_rank = -1 writes every new rank's shard, dst = N' * S' elements.
+ *   old_shards: host array of N device pointers to S elements each, aligned
+ *   to elem_size (entries of old ranks that hold only padding may be NULL);
+ *   dst: device, aligned to elem_size, not overlapping the old shards.
+ *   Device tables, pointer uploads, validation caching and stream rules as
+ *   in fp_shard0_pack. */
+typedef struct fp_reshard_plan fp_reshard_plan;
+fp_status fp_reshard_plan_create(int64_t numel, int32_t world_old, int32_t world_new, fp_reshard_plan** out);
+void fp_reshard_plan_destroy(fp_reshard_plan* plan);
+fp_status fp_reshard_plan_info(const fp_reshard_plan* plan, int64_t* shard_old, int64_t* shard_new);
+fp_status fp_reshard(fp_reshard_plan* plan, int32_t elem_size, int32_t new_rank, const void* const* old_shards,
+                     void* dst, void* stream);
+
 /* ------------------------------------------------------------ no_sync, scaler */
 
 /* Gradient accumulation without communication.  [DP] "Naive Data

@@ -24,7 +24,7 @@ from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_ONE_PASS,  # noqa: F40
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
-__all__ = ["Plan", "Units", "Shard0Plan", "reduce_shard_hybrid", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
+__all__ = ["Plan", "Units", "Shard0Plan", "ReshardPlan", "reduce_shard_hybrid", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
            "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "library_path"]
@@ -273,6 +273,67 @@ class Shard0Plan:
 
     def unpack(self, full, params=None):
         return self.unpacker(full, params)()
+
+
+class ReshardPlan:
+    """A flat buffer of `numel` elements cut into world_old shards, to be cut
+    into world_new shards (a sharded checkpoint loaded into another rank
+    count): shard sizes ceil(numel / world), zeros past numel."""
+
+    def __init__(self, numel: int, world_old: int, world_new: int):
+        self.numel, self.world_old, self.world_new = int(numel), int(world_old), int(world_new)
+        h = C.c_void_p()
+        check(lib().fp_reshard_plan_create(self.numel, self.world_old, self.world_new, C.byref(h)))
+        self._h = h
+        so, sn = C.c_int64(), C.c_int64()
+        check(lib().fp_reshard_plan_info(self._h, C.byref(so), C.byref(sn)))
+        self.shard_old, self.shard_new = so.value, sn.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().fp_reshard_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def resharder(self, old_shards, dst=None, rank: int = -1):
+        """A callable writing new rank `rank`'s shard (rank = -1: every new
+        rank's, one after the other) from the old shards into dst (allocated
+        here when None) and returning it; pointers are marshalled once."""
+        torch = _torch()
+        if len(old_shards) != self.world_old:
+            raise ValueError(f"need {self.world_old} old shards")
+        given = [t for t in old_shards if t is not None] + ([dst] if dst is not None else [])
+        if not given:
+            raise ValueError("need at least one old shard or dst to know the dtype and device")
+        dtype = given[0].dtype
+        esize = torch.empty(0, dtype=dtype).element_size()
+        ptrs = []
+        for q, t in enumerate(old_shards):
+            if t is None:
+                ptrs.append(None)
+                continue
+            if t.dtype != dtype:
+                raise TypeError("old shards differ in dtype")
+            ptrs.append(_dev_ptr(t, (dtype,), self.shard_old, f"old_shards[{q}]"))
+        n = self.shard_new * (self.world_new if rank < 0 else 1)
+        if dst is None:
+            dst = torch.empty(n, dtype=dtype, device=given[0].device)
+        dptr = C.c_void_p(_dev_ptr(dst, (dtype,), n, "dst"))
+        table = _ptr_table(ptrs)
+        fn, h, r = lib().fp_reshard, self._h, int(rank)
+
+        def run():
+            check(fn(h, esize, r, table, dptr, _stream(dst)))
+            return dst
+        return run
+
+    def reshard(self, old_shards, dst=None, rank: int = -1):
+        return self.resharder(old_shards, dst, rank)()
 
 
 # ------------------------------------------------------------------ reduce

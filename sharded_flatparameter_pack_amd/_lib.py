@@ -83,6 +83,10 @@ SIGNATURES = {
     "fp_shard0_views": (_i32, [_vp, _i32, _vp, _i32, _vp]),
     "fp_shard0_pack": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "fp_shard0_unpack": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+    "fp_reshard_plan_create": (_i32, [_i64, _i32, _i32, C.POINTER(_vp)]),
+    "fp_reshard_plan_destroy": (None, [_vp]),
+    "fp_reshard_plan_info": (_i32, [_vp, _vp, _vp]),
+    "fp_reshard": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "fp_local_accumulate": (_i32, [_i64, _vp, _i32, _vp, _vp]),
     "fp_local_finish": (_i32, [_i64, _vp, _i32, _vp, _vp, _vp]),
     "fp_grad_coef": (_i32, [_vp, _vp, _f64, _vp, _vp]),

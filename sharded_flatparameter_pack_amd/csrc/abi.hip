@@ -968,14 +968,11 @@ void free_seg_table(SegTable& t) {
     t = SegTable();
 }
 
-constexpr int kOpPackRank = 0, kOpPackAll = 1, kOpUnpack = 2;
-}  // namespace
+constexpr int kOpPackRank = 0, kOpPackAll = 1, kOpUnpack = 2, kOpReshardRank = 3, kOpReshardAll = 4;
 
-struct fp_shard0_plan {
-    int32_t n = 0, world = 1;
-    std::vector<int32_t> ndims;
-    std::vector<int64_t> dims, dim_start, d0, rows, row_elems, off, numel;
-    int64_t shard = 0, total = 0;
+// The segment tables of one plan, keyed by (operation, element size, rank),
+// and the pointer sets its calls last validated.
+struct SegCache {
     std::mutex mu;
     std::vector<SegTable> tables;
     struct Validated {
@@ -983,6 +980,18 @@ struct fp_shard0_plan {
         std::vector<void*> ptrs;
     };
     std::vector<Validated> validated;
+    ~SegCache() {
+        for (auto& t : tables) free_seg_table(t);
+    }
+};
+}  // namespace
+
+struct fp_shard0_plan {
+    int32_t n = 0, world = 1;
+    std::vector<int32_t> ndims;
+    std::vector<int64_t> dims, dim_start, d0, rows, row_elems, off, numel;
+    int64_t shard = 0, total = 0;
+    SegCache cache;
 };
 
 namespace {
@@ -1063,17 +1072,19 @@ std::vector<SegDesc> shard0_segments(const fp_shard0_plan* p, int op, int es, in
     return v;
 }
 
-// The device tables of (op, es, rank) on the current device, built on first use.
-fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** out) {
+// The device tables of (op, es, rank) on the current device, built on first
+// use from the segment list that `build` returns.
+template <class Build>
+fp_status seg_table(SegCache& c, int op, int es, int rank, int32_t n_ptrs, Build build, SegTable** out) {
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return device_fail(e, "hipGetDevice");
-    for (auto& t : p->tables)
+    for (auto& t : c.tables)
         if (t.device == device && t.op == op && t.es == es && t.rank == rank) {
             *out = &t;
             return FP_OK;
         }
-    std::vector<SegDesc> segs = shard0_segments(p, op, es, rank);
+    std::vector<SegDesc> segs = build();
     std::vector<int32_t> seg_of;
     int64_t g = 0;
     for (size_t s = 0; s < segs.size(); ++s) {
@@ -1089,7 +1100,7 @@ fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** o
     t.rank = rank;
     t.device = device;
     t.groups = g;
-    t.n_ptrs = p->n + 1;
+    t.n_ptrs = n_ptrs;
     const size_t segs_b = (segs.empty() ? 1 : segs.size()) * sizeof(SegDesc);
     const size_t of_b = (seg_of.empty() ? 1 : seg_of.size()) * sizeof(int32_t);
     const size_t tab_b = (size_t)t.n_ptrs * sizeof(void*);
@@ -1105,14 +1116,18 @@ fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** o
         free_seg_table(t);
         return device_fail(e, "allocating the layout's device tables");
     }
-    p->tables.push_back(t);
-    *out = &p->tables.back();
+    c.tables.push_back(t);
+    *out = &c.tables.back();
     return FP_OK;
+}
+
+fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** out) {
+    return seg_table(p->cache, op, es, rank, p->n + 1, [&] { return shard0_segments(p, op, es, rank); }, out);
 }
 
 // Uploads the pointer table (unless it holds these pointers already) and
 // launches the segment copy of a table.
-fp_status shard0_run(SegTable* t, void* const* ptrs, hipStream_t s) {
+fp_status seg_run(SegTable* t, void* const* ptrs, hipStream_t s) {
     hipError_t e;
     const bool same = t->have_last && std::equal(ptrs, ptrs + t->n_ptrs, t->last_ptrs.begin());
     if (same) {
@@ -1204,8 +1219,6 @@ extern "C" fp_status fp_shard0_plan_create(int32_t n_params, const int32_t* ndim
 }
 
 extern "C" void fp_shard0_plan_destroy(fp_shard0_plan* plan) {
-    if (plan == nullptr) return;
-    for (auto& t : plan->tables) free_seg_table(t);
     delete plan;
 }
 
@@ -1243,18 +1256,18 @@ extern "C" fp_status fp_shard0_views(const fp_shard0_plan* plan, int32_t rank, f
 namespace {
 // The pointer set a call of (op, es, rank) last passed validation with: a
 // call with the same pointers skips the checks (they depend on nothing else).
-bool shard0_validated(fp_shard0_plan* p, int op, int es, int rank, const std::vector<void*>& ptrs) {
-    for (const auto& v : p->validated)
+bool seg_validated(SegCache& c, int op, int es, int rank, const std::vector<void*>& ptrs) {
+    for (const auto& v : c.validated)
         if (v.op == op && v.es == es && v.rank == rank) return v.ptrs == ptrs;
     return false;
 }
-void shard0_remember(fp_shard0_plan* p, int op, int es, int rank, const std::vector<void*>& ptrs) {
-    for (auto& v : p->validated)
+void seg_remember(SegCache& c, int op, int es, int rank, const std::vector<void*>& ptrs) {
+    for (auto& v : c.validated)
         if (v.op == op && v.es == es && v.rank == rank) {
             v.ptrs = ptrs;
             return;
         }
-    p->validated.push_back({op, es, rank, ptrs});
+    c.validated.push_back({op, es, rank, ptrs});
 }
 
 // Null, alignment and overlap checks of the parameters against `other`
@@ -1292,19 +1305,19 @@ extern "C" fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int
     std::vector<void*> ptrs((size_t)plan->n + 1);
     ptrs[0] = dst;
     for (int32_t i = 0; i < plan->n; ++i) ptrs[1 + i] = const_cast<void*>(params[i]);
-    std::lock_guard<std::mutex> lock(plan->mu);
-    if (!shard0_validated(plan, op, elem_size, key_rank, ptrs)) {
+    std::lock_guard<std::mutex> lock(plan->cache.mu);
+    if (!seg_validated(plan->cache, op, elem_size, key_rank, ptrs)) {
         const int64_t dst_elems = rank < 0 ? plan->shard * plan->world : plan->shard;
         if (dst == nullptr && dst_elems > 0) return fail(FP_ERR_INVALID, "dst is NULL");
         if (!aligned(dst, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "dst misaligned");
         fp_status st = shard0_check_params(plan, elem_size, params, dst, dst_elems, "dst", false);
         if (st != FP_OK) return st;
-        shard0_remember(plan, op, elem_size, key_rank, ptrs);
+        seg_remember(plan->cache, op, elem_size, key_rank, ptrs);
     }
     SegTable* t = nullptr;
     fp_status st = shard0_table(plan, op, elem_size, key_rank, &t);
     if (st != FP_OK) return st;
-    return shard0_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+    return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
 }
 
 extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* full,
@@ -1315,19 +1328,123 @@ extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, c
     std::vector<void*> ptrs((size_t)plan->n + 1);
     for (int32_t i = 0; i < plan->n; ++i) ptrs[i] = params[i];
     ptrs[plan->n] = const_cast<void*>(full);
-    std::lock_guard<std::mutex> lock(plan->mu);
-    if (!shard0_validated(plan, kOpUnpack, elem_size, 0, ptrs)) {
+    std::lock_guard<std::mutex> lock(plan->cache.mu);
+    if (!seg_validated(plan->cache, kOpUnpack, elem_size, 0, ptrs)) {
         const int64_t full_elems = plan->shard * plan->world;
         if (full == nullptr && full_elems > 0) return fail(FP_ERR_INVALID, "full is NULL");
         if (!aligned(full, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "full misaligned");
         fp_status st = shard0_check_params(plan, elem_size, params, full, full_elems, "full", true);
         if (st != FP_OK) return st;
-        shard0_remember(plan, kOpUnpack, elem_size, 0, ptrs);
+        seg_remember(plan->cache, kOpUnpack, elem_size, 0, ptrs);
     }
     SegTable* t = nullptr;
     fp_status st = shard0_table(plan, kOpUnpack, elem_size, 0, &t);
     if (st != FP_OK) return st;
-    return shard0_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+    return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------- reshard
+
+struct fp_reshard_plan {
+    int64_t numel = 0, s_old = 0, s_new = 0;
+    int32_t world_old = 1, world_new = 1;
+    SegCache cache;
+};
+
+namespace {
+// Segments of new rank(s) [q0, q1): pieces of the old shards, zeros past T.
+// Pointer table: [dst, old shards...].  Units of 2 bytes.
+std::vector<SegDesc> reshard_segments(const fp_reshard_plan* p, int es, int new_rank) {
+    const int64_t u = es / 2, T = p->numel, So = p->s_old, Sn = p->s_new;
+    const bool all = new_rank < 0;
+    const int32_t q0 = all ? 0 : new_rank, q1 = all ? p->world_new : new_rank + 1;
+    std::vector<SegDesc> v;
+    auto add = [&](int64_t dst_off, int32_t src, int64_t src_off, int64_t len) {
+        if (len <= 0) return;
+        SegDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.kind = kSegCopy;
+        d.dst = 0;
+        d.dst_off = dst_off * u;
+        d.src = src;
+        d.src_off = src_off * u;
+        d.len = len * u;
+        v.push_back(d);
+    };
+    for (int32_t q = q0; q < q1; ++q) {
+        const int64_t base = all ? (int64_t)q * Sn : 0, lo = (int64_t)q * Sn, hi_all = lo + Sn;
+        const int64_t hi = hi_all < T ? hi_all : T;
+        for (int64_t e = lo; e < hi;) {
+            const int64_t o = e / So, end = (o + 1) * So < hi ? (o + 1) * So : hi;
+            add(base + (e - lo), 1 + (int32_t)o, e - o * So, end - e);
+            e = end;
+        }
+        const int64_t z = lo > T ? lo : T;
+        add(base + (z - lo), -1, 0, hi_all - z);
+    }
+    return v;
+}
+}  // namespace
+
+extern "C" fp_status fp_reshard_plan_create(int64_t numel, int32_t world_old, int32_t world_new,
+                                            fp_reshard_plan** out) {
+    if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (numel < 0 || numel > ((int64_t)1 << 40)) return fail(FP_ERR_RANGE, "numel outside [0, 2^40]");
+    if (world_old < 1 || world_old > (1 << 20) || world_new < 1 || world_new > (1 << 20))
+        return fail(FP_ERR_RANGE, "world sizes must be in [1, 2^20]");
+    fp_reshard_plan* p = new (std::nothrow) fp_reshard_plan();
+    if (p == nullptr) return fail(FP_ERR_DEVICE, "out of host memory");
+    p->numel = numel;
+    p->world_old = world_old;
+    p->world_new = world_new;
+    p->s_old = (numel + world_old - 1) / world_old;
+    p->s_new = (numel + world_new - 1) / world_new;
+    *out = p;
+    return FP_OK;
+}
+
+extern "C" void fp_reshard_plan_destroy(fp_reshard_plan* plan) { delete plan; }
+
+extern "C" fp_status fp_reshard_plan_info(const fp_reshard_plan* plan, int64_t* shard_old, int64_t* shard_new) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (shard_old) *shard_old = plan->s_old;
+    if (shard_new) *shard_new = plan->s_new;
+    return FP_OK;
+}
+
+extern "C" fp_status fp_reshard(fp_reshard_plan* plan, int32_t elem_size, int32_t new_rank,
+                                const void* const* old_shards, void* dst, void* stream) {
+    if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
+    if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
+    if (new_rank < -1 || new_rank >= plan->world_new)
+        return fail(FP_ERR_RANGE, "new_rank %d outside [-1, %d)", new_rank, plan->world_new);
+    if (old_shards == nullptr) return fail(FP_ERR_INVALID, "old_shards table is NULL");
+    const int32_t N = plan->world_old;
+    std::vector<void*> ptrs((size_t)N + 1);
+    ptrs[0] = dst;
+    for (int32_t q = 0; q < N; ++q) ptrs[1 + q] = const_cast<void*>(old_shards[q]);
+    const int key = new_rank < 0 ? 0 : new_rank;
+    const int op = new_rank < 0 ? kOpReshardAll : kOpReshardRank;
+    std::lock_guard<std::mutex> lock(plan->cache.mu);
+    if (!seg_validated(plan->cache, op, elem_size, key, ptrs)) {
+        const int64_t dst_elems = plan->s_new * (new_rank < 0 ? plan->world_new : 1);
+        if (dst == nullptr && dst_elems > 0) return fail(FP_ERR_INVALID, "dst is NULL");
+        if (!aligned(dst, (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "dst misaligned");
+        for (int32_t q = 0; q < N; ++q) {
+            if ((int64_t)q * plan->s_old >= plan->numel) continue;   // holds only padding: never read
+            if (old_shards[q] == nullptr) return fail(FP_ERR_INVALID, "old_shards[%d] is NULL", q);
+            if (!aligned(old_shards[q], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "old_shards[%d] misaligned", q);
+            if (overlap(old_shards[q], plan->s_old * elem_size, dst, dst_elems * elem_size))
+                return fail(FP_ERR_INVALID, "old_shards[%d] overlaps dst", q);
+        }
+        seg_remember(plan->cache, op, elem_size, key, ptrs);
+    }
+    SegTable* t = nullptr;
+    fp_status st = seg_table(plan->cache, op, elem_size, key, N + 1,
+                             [&] { return reshard_segments(plan, elem_size, new_rank); }, &t);
+    if (st != FP_OK) return st;
+    return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------------- no_sync, scaler

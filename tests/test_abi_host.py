@@ -352,3 +352,28 @@ def test_hybrid_validation_without_a_device(fp):
                    None) == -3
     g_null = (C.c_void_p * 4)(0x10000, None, 0x30000, 0x40000)
     assert _status(L.fp_reduce_shard_hybrid, 16, 4, 2, g_null, 1.0, 0, acc, None, None, None, None) == -1
+
+
+def test_reshard_plan_and_validation_without_a_device(fp):
+    L = fp.lib()
+    h = C.c_void_p()
+    assert _status(L.fp_reshard_plan_create, -1, 2, 3, C.byref(h)) == -2
+    assert _status(L.fp_reshard_plan_create, 10, 0, 3, C.byref(h)) == -2
+    assert _status(L.fp_reshard_plan_create, 10, 2, 0, C.byref(h)) == -2
+    plan = fp.ReshardPlan(10, 4, 3)
+    assert (plan.shard_old, plan.shard_new) == (3, 4)
+    assert fp.ReshardPlan(0, 4, 3).shard_new == 0
+    old = (C.c_void_p * 4)(0x100000, 0x200000, 0x300000, None)   # rank 3 holds only padding
+    dst = C.c_void_p(0x400000)
+    assert _status(L.fp_reshard, plan._h, 3, -1, old, dst, None) == -1
+    assert _status(L.fp_reshard, plan._h, 2, 3, old, dst, None) == -2
+    assert _status(L.fp_reshard, plan._h, 2, -2, old, dst, None) == -2
+    assert _status(L.fp_reshard, plan._h, 2, -1, None, dst, None) == -1
+    assert _status(L.fp_reshard, plan._h, 2, -1, old, None, None) == -1
+    assert _status(L.fp_reshard, plan._h, 4, -1, old, C.c_void_p(0x400002), None) == -3
+    bad = (C.c_void_p * 4)(0x100000, None, 0x300000, None)
+    assert _status(L.fp_reshard, plan._h, 2, -1, bad, dst, None) == -1
+    ov = (C.c_void_p * 4)(0x100000, 0x400004, 0x300000, None)
+    assert _status(L.fp_reshard, plan._h, 2, -1, ov, dst, None) == -1
+    assert _status(L.fp_reshard_plan_info, None, None, None) == -1
+    L.fp_reshard_plan_destroy(None)
