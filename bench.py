@@ -470,6 +470,41 @@ def hybrid_bench(cfg, dev, reps: int, replicas: int = 2):
     return res
 
 
+def reshard_bench(cfg, dev, reps: int):
+    """Resharding the workload's fp32 flat state (one of master / exp_avg /
+    exp_avg_sq: T elements) from N_d to 2 N_d and to N_d / 2 ranks, every new
+    rank's shard in one call: reads 4T, writes 4 N' S' bytes."""
+    import torch
+    import sharded_flatparameter_pack_amd as fp
+    from workloads import gen
+    T = sum(cfg.units())
+    N = cfg.world
+    res = {"workload": cfg.name, "elements": T, "N_d": N, "dtype": "fp32"}
+    for N2 in (2 * N, max(1, N // 2)):
+        plan = fp.ReshardPlan(T, N, N2)
+        S = plan.shard_old
+        flat = torch.zeros(N * S, dtype=torch.float32, device=dev)
+        flat[:T] = gen.torch_normal_f32(T, 0.02, cfg.seed, (gen.STREAM_MASTER,), dev)
+        run = plan.resharder([flat[q * S:(q + 1) * S] for q in range(N)])
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        alg = 4 * T + 4 * N2 * plan.shard_new
+        gbs = alg / (ms * 1e-3) / 1e9
+        res[f"to_{N2}"] = {"us_per_call": round(ms * 1e3, 2), "alg_bytes": alg, "GBps": round(gbs, 1),
+                           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del flat, run
+        plan.close()
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_reference(fp, dev, reps: int = 20):
     """Measured plain-copy bandwidth (fp_unshard of 16 x 8M bf16 shards, 256 MiB each way)."""
     import torch
@@ -580,6 +615,8 @@ def main(argv=None) -> int:
                     help="only time the no_sync local accumulation kernels over the workload's unit")
     ap.add_argument("--hybrid-only", action="store_true",
                     help="only time the hybrid-sharding reduce (F = N_d, W = 2F) against the flat one")
+    ap.add_argument("--reshard-only", action="store_true",
+                    help="only time resharding the workload's fp32 flat state to 2 N_d and N_d / 2 ranks")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)
@@ -607,6 +644,9 @@ def main(argv=None) -> int:
             print(f"{cfg.name} has no parameter shapes", file=sys.stderr)
             return 2
         print(json.dumps(shard0_bench(cfg, dev, max(1, args.steps))), flush=True)
+        return 0
+    if args.reshard_only:
+        print(json.dumps(reshard_bench(cfg, dev, max(1, args.steps))), flush=True)
         return 0
     if args.hybrid_only:
         print(json.dumps(hybrid_bench(cfg, dev, max(1, args.steps))), flush=True)
@@ -672,6 +712,8 @@ def main(argv=None) -> int:
             result["dim0_layout"] = shard0_bench(cfg, dev, 20)
             torch.cuda.empty_cache()
             result["hybrid_reduce"] = hybrid_bench(cfg, dev, 20)
+        torch.cuda.empty_cache()
+        result["reshard"] = reshard_bench(cfg, dev, 10)
         if cfg.n_micro > 1:
             torch.cuda.empty_cache()
             result["no_sync"] = nosync_bench(cfg, dev, 10)
