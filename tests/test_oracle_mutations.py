@@ -26,7 +26,10 @@ MUTATIONS = {
                                      "float sum = 0.0f;\n        for (int32_t q = 0;"),
     "reduce_wrong_rank_index": ("sum = sum + or_bf16_to_f32(grads[q][i]);",
                                 "sum = sum + or_bf16_to_f32(grads[world - q][i]);"),
-    "reduce_ignores_accumulate": ("acc[i] = acc[i] + y;", "acc[i] = y;"),
+    "reduce_ignores_accumulate": ("float y = sum * scale;\n        if (accumulate)\n            acc[i] = acc[i] + y;",
+                                  "float y = sum * scale;\n        if (accumulate)\n            acc[i] = y;"),
+    "hybrid_ignores_accumulate": ("float y = total * scale;\n        if (accumulate)\n            acc[i] = acc[i] + y;",
+                                  "float y = total * scale;\n        if (accumulate)\n            acc[i] = y;"),
     "reduce_sums_instead_of_mean": ("float y = sum * scale;", "float y = sum;"),
     "adamw_no_bias_correction_1": ("double m_hat = m / bias1;", "double m_hat = m;"),
     "adamw_no_bias_correction_2": ("double v_hat = v / bias2;", "double v_hat = v;"),
