@@ -139,7 +139,7 @@ fp_status fp_unpack_views(const fp_plan* plan, int32_t rank, fp_view* out, int32
 
 /* Size in bytes of the device workspace that fp_reduce_shard (for the
  * gradient norm) and fp_shard_step (norm and one-pass grid barrier) use for
- * a shard of S elements: a small header plus 8 bytes per 2048 elements.
+ * a shard of S elements: a small header plus 8 bytes per 1024 elements.
  * The caller allocates it, zero-fills it once before its first use and then
  * passes it unchanged to later calls; every completed call leaves it
  * reusable.  Calls that may run concurrently need separate workspaces. */

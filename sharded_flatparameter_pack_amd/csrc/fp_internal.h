@@ -17,8 +17,11 @@ constexpr int kWaves = kThreads / 64;
 // quads, kQuadsPerLane per lane, and tiles are numbered in dispatch order,
 // so the workgroups in flight cover one contiguous window of every stream --
 // on MI355X this keeps HBM pages open far better than grid-stride loops,
-// whose concurrent accesses spread over the whole buffer.
-constexpr int kQuadsPerLane = 2;
+// whose concurrent accesses spread over the whole buffer.  One quad per lane
+// (1024 elements per workgroup) measured best for the two-kernel step: fewer
+// registers, more waves in flight (against two: the d=12288 layer's step
+// 2.92 ms vs 3.00, the 10k-tensor step at 64 ranks 3.00 ms vs 3.30).
+constexpr int kQuadsPerLane = 1;
 constexpr int64_t kTileQuads = (int64_t)kThreads * kQuadsPerLane;
 // 16-byte words per lane of a copy workgroup.  Stand-alone copies and the
 // two-pass step use one (consecutive waves then sweep consecutive addresses,

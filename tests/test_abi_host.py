@@ -185,7 +185,7 @@ def test_device_entry_points_reject_bad_arguments(fp):
     a.rank, a.flags = 0, 8
     assert _status(L.fp_shard_step, C.byref(a), None) == -1                      # unknown flag
     assert L.fp_workspace_bytes(0) >= 256 + 8
-    assert L.fp_workspace_bytes(1 << 30) == 16384 + 8 * ((1 << 30) // 8 // 256 + 1)
+    assert L.fp_workspace_bytes(1 << 30) == 16384 + 8 * ((1 << 30) // 4 // 256 + 1)
     assert _status(L.fp_shard_step, None, None) == -1
     assert L.fp_status_string(-3) == b"misaligned pointer"
 
