@@ -100,11 +100,13 @@ fp_status fp_plan_info(const fp_plan* plan, int64_t* numel, int64_t* padded, int
  *   source.
  * On its first call on a device the plan allocates and uploads its tensor
  * tables to that device (hipMalloc / pinned host staging; released by
- * fp_plan_destroy); each call uploads the source pointer table on
- * `stream`.  Calls that share a plan must be ordered on one stream; a call
- * waits on the host only if the previous call's pointer upload from the
- * same plan has not finished yet.  A one-time set-up operation per unit,
- * not part of the per-step path. */
+ * fp_plan_destroy).  A call whose source pointers differ from the previous
+ * call's uploads them on `stream` (waiting on the host only if that
+ * previous upload has not finished); a call with the same pointers only
+ * orders `stream` after it, and a call with the same arguments as the last
+ * validated one skips the argument checks.  Calls that share a plan must be
+ * ordered on one stream.  Not for graph capture.  A one-time set-up
+ * operation per unit, not part of the per-step path. */
 fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const* src, void* flat,
                   void* stream);
 

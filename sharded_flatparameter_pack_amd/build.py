@@ -17,7 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libflatparam.so")
-SOURCES = ["abi.hip", "step_kernels.hip", "unit_kernels.hip", "pack_kernels.hip", "segment_kernels.hip",
+SOURCES = ["abi.hip", "step_kernels.hip", "unit_kernels.hip", "segment_kernels.hip",
            "local_kernels.hip", "hybrid_kernels.hip"]
 ARCH = "gfx950"
 

@@ -102,18 +102,159 @@ fp_status check_world(int32_t world) {
 
 }  // namespace
 
-// ---------------------------------------------------------------------- plan
+// ---------------------------------------------------------------------- segment lists
+// The bit-copy operations (FlatParameter pack, the dim-0 layout, resharding)
+// are lists of copy / zero-fill entries run by one launch of the segment
+// kernel.  A plan keeps, per (operation, element size, rank) and device, the
+// entry list and its per-workgroup index on the device, and a per-call table
+// of the buffers' device pointers that entries name by index.
 
 namespace {
-struct DeviceTables {
+// Device tables of one segment list on one device, and the staging of its
+// per-call pointer table.
+struct SegTable {
+    int op = -1, es = 0, rank = 0;   // what the list is for
     int device = -1;
-    int64_t* offsets = nullptr;
-    int32_t* group_first = nullptr;
-    const void** src = nullptr;        // device copy of the per-call pointer table
-    const void** src_staging = nullptr; // pinned host staging of that table
-    hipEvent_t uploaded = nullptr;      // completion of the last upload from staging
+    int64_t groups = 0;
+    int32_t n_ptrs = 0;
+    SegDesc* segs = nullptr;
+    int32_t* seg_of = nullptr;
+    void** tab = nullptr;
+    void** tab_staging = nullptr;
+    hipEvent_t uploaded = nullptr;
+    bool have_last = false;          // tab holds (or will hold) last_ptrs
+    std::vector<void*> last_ptrs;
 };
+
+void free_seg_table(SegTable& t) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (t.device >= 0) (void)hipSetDevice(t.device);
+    if (t.uploaded) (void)hipEventSynchronize(t.uploaded), (void)hipEventDestroy(t.uploaded);
+    if (t.segs) (void)hipFree(t.segs);
+    if (t.seg_of) (void)hipFree(t.seg_of);
+    if (t.tab) (void)hipFree(t.tab);
+    if (t.tab_staging) (void)hipHostFree(t.tab_staging);
+    if (cur >= 0) (void)hipSetDevice(cur);
+    t = SegTable();
+}
+
+constexpr int kOpPackRank = 0, kOpPackAll = 1, kOpUnpack = 2, kOpReshardRank = 3, kOpReshardAll = 4,
+              kOpFlatPack = 5;
+
+// The segment tables of one plan, keyed by (operation, element size, rank),
+// and the pointer sets its calls last validated.
+struct SegCache {
+    std::mutex mu;
+    std::vector<SegTable> tables;
+    struct Validated {
+        int op, es, rank;
+        std::vector<void*> ptrs;
+    };
+    std::vector<Validated> validated;
+    ~SegCache() {
+        for (auto& t : tables) free_seg_table(t);
+    }
+};
+
+// The device tables of (op, es, rank) on the current device, built on first
+// use from the segment list that `build` returns.
+template <class Build>
+fp_status seg_table(SegCache& c, int op, int es, int rank, int32_t n_ptrs, Build build, SegTable** out) {
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+    for (auto& t : c.tables)
+        if (t.device == device && t.op == op && t.es == es && t.rank == rank) {
+            *out = &t;
+            return FP_OK;
+        }
+    std::vector<SegDesc> segs = build();
+    std::vector<int32_t> seg_of;
+    int64_t g = 0;
+    for (size_t s = 0; s < segs.size(); ++s) {
+        segs[s].tile0 = g;
+        const int64_t n = segment_tiles(segs[s]);
+        if (g + n > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "layout too large for one launch");
+        for (int64_t k = 0; k < n; ++k) seg_of.push_back((int32_t)s);
+        g += n;
+    }
+    SegTable t;
+    t.op = op;
+    t.es = es;
+    t.rank = rank;
+    t.device = device;
+    t.groups = g;
+    t.n_ptrs = n_ptrs;
+    const size_t segs_b = (segs.empty() ? 1 : segs.size()) * sizeof(SegDesc);
+    const size_t of_b = (seg_of.empty() ? 1 : seg_of.size()) * sizeof(int32_t);
+    const size_t tab_b = (size_t)t.n_ptrs * sizeof(void*);
+    if ((e = hipMalloc((void**)&t.segs, segs_b)) != hipSuccess ||
+        (e = hipMalloc((void**)&t.seg_of, of_b)) != hipSuccess ||
+        (e = hipMalloc((void**)&t.tab, tab_b)) != hipSuccess ||
+        (e = hipHostMalloc((void**)&t.tab_staging, tab_b, hipHostMallocDefault)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&t.uploaded, hipEventDisableTiming)) != hipSuccess ||
+        (!segs.empty() && (e = hipMemcpy(t.segs, segs.data(), segs.size() * sizeof(SegDesc),
+                                         hipMemcpyHostToDevice)) != hipSuccess) ||
+        (!seg_of.empty() && (e = hipMemcpy(t.seg_of, seg_of.data(), seg_of.size() * sizeof(int32_t),
+                                           hipMemcpyHostToDevice)) != hipSuccess)) {
+        free_seg_table(t);
+        return device_fail(e, "allocating the layout's device tables");
+    }
+    c.tables.push_back(t);
+    *out = &c.tables.back();
+    return FP_OK;
+}
+
+// Uploads the pointer table (unless it holds these pointers already) and
+// launches the segment copy of a table.
+fp_status seg_run(SegTable* t, void* const* ptrs, hipStream_t s) {
+    hipError_t e;
+    const bool same = t->have_last && std::equal(ptrs, ptrs + t->n_ptrs, t->last_ptrs.begin());
+    if (same) {
+        // the table's last upload, wherever it was enqueued, comes first
+        if ((e = hipStreamWaitEvent(s, t->uploaded, 0)) != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+    } else {
+        // the staging buffer may still feed the previous call's upload
+        if ((e = hipEventSynchronize(t->uploaded)) != hipSuccess) return device_fail(e, "hipEventSynchronize");
+        for (int32_t i = 0; i < t->n_ptrs; ++i) t->tab_staging[i] = ptrs[i];
+        t->have_last = false;
+        if ((e = hipMemcpyAsync(t->tab, t->tab_staging, (size_t)t->n_ptrs * sizeof(void*),
+                                hipMemcpyHostToDevice, s)) != hipSuccess)
+            return device_fail(e, "uploading the pointer table");
+        if ((e = hipEventRecord(t->uploaded, s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+        t->last_ptrs.assign(ptrs, ptrs + t->n_ptrs);
+        t->have_last = true;
+    }
+    if (t->groups == 0) return FP_OK;
+    SegArgs a;
+    a.segs = t->segs;
+    a.seg_of = t->seg_of;
+    a.dst_tab = t->tab;
+    a.src_tab = t->tab;
+    if ((e = launch_segments(a, t->groups, s)) != hipSuccess) return device_fail(e, "segment copy launch");
+    return FP_OK;
+}
+
+// The pointer set a call of (op, es, rank) last passed validation with: a
+// call with the same pointers skips the checks (they depend on nothing else).
+bool seg_validated(SegCache& c, int op, int es, int rank, const std::vector<void*>& ptrs) {
+    for (const auto& v : c.validated)
+        if (v.op == op && v.es == es && v.rank == rank) return v.ptrs == ptrs;
+    return false;
+}
+void seg_remember(SegCache& c, int op, int es, int rank, const std::vector<void*>& ptrs) {
+    for (auto& v : c.validated)
+        if (v.op == op && v.es == es && v.rank == rank) {
+            v.ptrs = ptrs;
+            return;
+        }
+    c.validated.push_back({op, es, rank, ptrs});
+}
+
 }  // namespace
+
+// ---------------------------------------------------------------------- plan
 
 struct fp_plan {
     int32_t n = 0;
@@ -123,26 +264,9 @@ struct fp_plan {
     std::vector<int64_t> dims;
     std::vector<int64_t> numel;
     std::vector<int64_t> offsets;    // n + 1
-    std::vector<int32_t> group_first;
     int64_t total = 0, padded = 0, shard = 0;
-    std::mutex mu;
-    std::vector<DeviceTables> tables;
+    SegCache cache;                  // fp_pack's entry lists
 };
-
-namespace {
-void free_tables(DeviceTables& t) {
-    int cur = -1;
-    (void)hipGetDevice(&cur);
-    if (t.device >= 0) (void)hipSetDevice(t.device);
-    if (t.uploaded) (void)hipEventSynchronize(t.uploaded), (void)hipEventDestroy(t.uploaded);
-    if (t.offsets) (void)hipFree(t.offsets);
-    if (t.group_first) (void)hipFree(t.group_first);
-    if (t.src) (void)hipFree((void*)t.src);
-    if (t.src_staging) (void)hipHostFree((void*)t.src_staging);
-    if (cur >= 0) (void)hipSetDevice(cur);
-    t = DeviceTables();
-}
-}  // namespace
 
 extern "C" fp_status fp_plan_create(int32_t n_tensors, const int32_t* ndims, const int64_t* shapes,
                                     int32_t world, fp_plan** out) {
@@ -193,22 +317,11 @@ extern "C" fp_status fp_plan_create(int32_t n_tensors, const int32_t* ndims, con
     p->total = total;
     p->padded = ceil_div(total, world) * world;
     p->shard = p->padded / world;
-    // first tensor overlapping each pack workgroup's element range
-    const int64_t n_groups = ceil_div(p->padded, kPackBlockElems);
-    p->group_first.resize(n_groups + 1);
-    int32_t t = 0;
-    for (int64_t g = 0; g <= n_groups; ++g) {
-        const int64_t e = g * kPackBlockElems;
-        while (t < n_tensors && p->offsets[t + 1] <= e) ++t;  // also skips empty tensors
-        p->group_first[g] = e < total ? t : n_tensors;
-    }
     *out = p;
     return FP_OK;
 }
 
 extern "C" void fp_plan_destroy(fp_plan* plan) {
-    if (plan == nullptr) return;
-    for (auto& t : plan->tables) free_tables(t);
     delete plan;
 }
 
@@ -258,68 +371,76 @@ extern "C" fp_status fp_unpack_views(const fp_plan* plan, int32_t rank, fp_view*
 
 // ---------------------------------------------------------------------- pack
 
+namespace {
+// FlatParameter construction as a segment list (2-byte units): tensor i is
+// copied to flat[o_i, o_i + n_i) -- one copy entry, or for a tensor under
+// kSegSmallPiece units one strided entry of a single piece, so that tiny
+// tensors do not each cost a workgroup's worth of partial cache lines --
+// and flat[T, P) is zero-filled.  Pointer table: [flat, tensors...].
+std::vector<SegDesc> pack_segments(const fp_plan* p, int es) {
+    const int64_t u = es / 2;
+    std::vector<SegDesc> v;
+    for (int32_t i = 0; i < p->n; ++i) {
+        const int64_t len = p->numel[i] * u;
+        if (len <= 0) continue;
+        SegDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.dst = 0;
+        d.dst_off = p->offsets[i] * u;
+        d.src = 1 + i;
+        d.len = len;
+        if (len < kSegSmallPiece) {
+            d.kind = kSegStrided;
+            d.piece = len;
+            d.valid = len;
+            d.dst_stride = len;
+            d.src_stride = len;
+        } else {
+            d.kind = kSegCopy;
+        }
+        v.push_back(d);
+    }
+    if (p->padded > p->total) {
+        SegDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.kind = kSegCopy;
+        d.dst = 0;
+        d.dst_off = p->total * u;
+        d.src = -1;
+        d.len = (p->padded - p->total) * u;
+        v.push_back(d);
+    }
+    return v;
+}
+}  // namespace
+
 extern "C" fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const* src, void* flat,
                              void* stream) {
     if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
     if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
     if (src == nullptr) return fail(FP_ERR_INVALID, "src table is NULL");
-    if (flat == nullptr) return fail(FP_ERR_INVALID, "flat is NULL");
-    if (!aligned(flat, 16)) return fail(FP_ERR_ALIGN, "flat is not 16-byte aligned");
-    const int64_t flat_bytes = plan->padded * elem_size;
-    for (int32_t i = 0; i < plan->n; ++i) {
-        if (plan->numel[i] == 0) continue;
-        if (src[i] == nullptr) return fail(FP_ERR_INVALID, "src[%d] is NULL", i);
-        if (!aligned(src[i], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "src[%d] misaligned", i);
-        if (overlap(src[i], plan->numel[i] * elem_size, flat, flat_bytes))
-            return fail(FP_ERR_INVALID, "src[%d] overlaps flat", i);
-    }
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    std::lock_guard<std::mutex> lock(plan->mu);
-    DeviceTables* t = nullptr;
-    for (auto& x : plan->tables)
-        if (x.device == device) t = &x;
-    const int64_t n_groups = (int64_t)plan->group_first.size() - 1;
-    if (t == nullptr) {  // first pack on this device: allocate and upload the static tables
-        DeviceTables nt;
-        nt.device = device;
-        const size_t off_b = (plan->n + 1) * sizeof(int64_t);
-        const size_t grp_b = (n_groups + 1) * sizeof(int32_t);
-        const size_t src_b = plan->n * sizeof(void*);
-        if ((e = hipMalloc((void**)&nt.offsets, off_b)) != hipSuccess ||
-            (e = hipMalloc((void**)&nt.group_first, grp_b)) != hipSuccess ||
-            (e = hipMalloc((void**)&nt.src, src_b)) != hipSuccess ||
-            (e = hipHostMalloc((void**)&nt.src_staging, src_b, hipHostMallocDefault)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&nt.uploaded, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipMemcpy(nt.offsets, plan->offsets.data(), off_b, hipMemcpyHostToDevice)) != hipSuccess ||
-            (e = hipMemcpy(nt.group_first, plan->group_first.data(), grp_b, hipMemcpyHostToDevice)) !=
-                hipSuccess) {
-            free_tables(nt);
-            return device_fail(e, "allocating the plan's device tables");
+    std::vector<void*> ptrs((size_t)plan->n + 1);
+    ptrs[0] = flat;
+    for (int32_t i = 0; i < plan->n; ++i) ptrs[1 + i] = const_cast<void*>(src[i]);
+    std::lock_guard<std::mutex> lock(plan->cache.mu);
+    if (!seg_validated(plan->cache, kOpFlatPack, elem_size, 0, ptrs)) {
+        if (flat == nullptr) return fail(FP_ERR_INVALID, "flat is NULL");
+        if (!aligned(flat, 16)) return fail(FP_ERR_ALIGN, "flat is not 16-byte aligned");
+        const int64_t flat_bytes = plan->padded * elem_size;
+        for (int32_t i = 0; i < plan->n; ++i) {
+            if (plan->numel[i] == 0) continue;
+            if (src[i] == nullptr) return fail(FP_ERR_INVALID, "src[%d] is NULL", i);
+            if (!aligned(src[i], (uintptr_t)elem_size)) return fail(FP_ERR_ALIGN, "src[%d] misaligned", i);
+            if (overlap(src[i], plan->numel[i] * elem_size, flat, flat_bytes))
+                return fail(FP_ERR_INVALID, "src[%d] overlaps flat", i);
         }
-        plan->tables.push_back(nt);
-        t = &plan->tables.back();
+        seg_remember(plan->cache, kOpFlatPack, elem_size, 0, ptrs);
     }
-    // the staging buffer may still feed the previous call's upload
-    if ((e = hipEventSynchronize(t->uploaded)) != hipSuccess) return device_fail(e, "hipEventSynchronize");
-    for (int32_t i = 0; i < plan->n; ++i) t->src_staging[i] = src[i];
-    if ((e = hipMemcpyAsync((void*)t->src, (const void*)t->src_staging, plan->n * sizeof(void*),
-                            hipMemcpyHostToDevice, s)) != hipSuccess)
-        return device_fail(e, "uploading the source pointer table");
-    if ((e = hipEventRecord(t->uploaded, s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-    PackArgs a;
-    a.offsets = t->offsets;
-    a.group_first = t->group_first;
-    a.src = t->src;
-    a.flat = flat;
-    a.total = plan->total;
-    a.padded = plan->padded;
-    a.n_tensors = plan->n;
-    if (n_groups == 0) return FP_OK;
-    if ((e = launch_pack(a, elem_size, n_groups, s)) != hipSuccess) return device_fail(e, "pack launch");
-    return FP_OK;
+    SegTable* t = nullptr;
+    fp_status st = seg_table(plan->cache, kOpFlatPack, elem_size, 0, plan->n + 1,
+                             [&] { return pack_segments(plan, elem_size); }, &t);
+    if (st != FP_OK) return st;
+    return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------------- reduce
@@ -939,51 +1060,6 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
 // ---------------------------------------------------------------------- dim-0 layout
 
 namespace {
-// Device tables of one segment list on one device, and the staging of its
-// per-call pointer table.
-struct SegTable {
-    int op = -1, es = 0, rank = 0;   // what the list is for
-    int device = -1;
-    int64_t groups = 0;
-    int32_t n_ptrs = 0;
-    SegDesc* segs = nullptr;
-    int32_t* seg_of = nullptr;
-    void** tab = nullptr;
-    void** tab_staging = nullptr;
-    hipEvent_t uploaded = nullptr;
-    bool have_last = false;          // tab holds (or will hold) last_ptrs
-    std::vector<void*> last_ptrs;
-};
-
-void free_seg_table(SegTable& t) {
-    int cur = -1;
-    (void)hipGetDevice(&cur);
-    if (t.device >= 0) (void)hipSetDevice(t.device);
-    if (t.uploaded) (void)hipEventSynchronize(t.uploaded), (void)hipEventDestroy(t.uploaded);
-    if (t.segs) (void)hipFree(t.segs);
-    if (t.seg_of) (void)hipFree(t.seg_of);
-    if (t.tab) (void)hipFree(t.tab);
-    if (t.tab_staging) (void)hipHostFree(t.tab_staging);
-    if (cur >= 0) (void)hipSetDevice(cur);
-    t = SegTable();
-}
-
-constexpr int kOpPackRank = 0, kOpPackAll = 1, kOpUnpack = 2, kOpReshardRank = 3, kOpReshardAll = 4;
-
-// The segment tables of one plan, keyed by (operation, element size, rank),
-// and the pointer sets its calls last validated.
-struct SegCache {
-    std::mutex mu;
-    std::vector<SegTable> tables;
-    struct Validated {
-        int op, es, rank;
-        std::vector<void*> ptrs;
-    };
-    std::vector<Validated> validated;
-    ~SegCache() {
-        for (auto& t : tables) free_seg_table(t);
-    }
-};
 }  // namespace
 
 struct fp_shard0_plan {
@@ -1072,88 +1148,10 @@ std::vector<SegDesc> shard0_segments(const fp_shard0_plan* p, int op, int es, in
     return v;
 }
 
-// The device tables of (op, es, rank) on the current device, built on first
-// use from the segment list that `build` returns.
-template <class Build>
-fp_status seg_table(SegCache& c, int op, int es, int rank, int32_t n_ptrs, Build build, SegTable** out) {
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    if (e != hipSuccess) return device_fail(e, "hipGetDevice");
-    for (auto& t : c.tables)
-        if (t.device == device && t.op == op && t.es == es && t.rank == rank) {
-            *out = &t;
-            return FP_OK;
-        }
-    std::vector<SegDesc> segs = build();
-    std::vector<int32_t> seg_of;
-    int64_t g = 0;
-    for (size_t s = 0; s < segs.size(); ++s) {
-        segs[s].tile0 = g;
-        const int64_t n = segment_tiles(segs[s]);
-        if (g + n > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "layout too large for one launch");
-        for (int64_t k = 0; k < n; ++k) seg_of.push_back((int32_t)s);
-        g += n;
-    }
-    SegTable t;
-    t.op = op;
-    t.es = es;
-    t.rank = rank;
-    t.device = device;
-    t.groups = g;
-    t.n_ptrs = n_ptrs;
-    const size_t segs_b = (segs.empty() ? 1 : segs.size()) * sizeof(SegDesc);
-    const size_t of_b = (seg_of.empty() ? 1 : seg_of.size()) * sizeof(int32_t);
-    const size_t tab_b = (size_t)t.n_ptrs * sizeof(void*);
-    if ((e = hipMalloc((void**)&t.segs, segs_b)) != hipSuccess ||
-        (e = hipMalloc((void**)&t.seg_of, of_b)) != hipSuccess ||
-        (e = hipMalloc((void**)&t.tab, tab_b)) != hipSuccess ||
-        (e = hipHostMalloc((void**)&t.tab_staging, tab_b, hipHostMallocDefault)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&t.uploaded, hipEventDisableTiming)) != hipSuccess ||
-        (!segs.empty() && (e = hipMemcpy(t.segs, segs.data(), segs.size() * sizeof(SegDesc),
-                                         hipMemcpyHostToDevice)) != hipSuccess) ||
-        (!seg_of.empty() && (e = hipMemcpy(t.seg_of, seg_of.data(), seg_of.size() * sizeof(int32_t),
-                                           hipMemcpyHostToDevice)) != hipSuccess)) {
-        free_seg_table(t);
-        return device_fail(e, "allocating the layout's device tables");
-    }
-    c.tables.push_back(t);
-    *out = &c.tables.back();
-    return FP_OK;
-}
-
 fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** out) {
     return seg_table(p->cache, op, es, rank, p->n + 1, [&] { return shard0_segments(p, op, es, rank); }, out);
 }
 
-// Uploads the pointer table (unless it holds these pointers already) and
-// launches the segment copy of a table.
-fp_status seg_run(SegTable* t, void* const* ptrs, hipStream_t s) {
-    hipError_t e;
-    const bool same = t->have_last && std::equal(ptrs, ptrs + t->n_ptrs, t->last_ptrs.begin());
-    if (same) {
-        // the table's last upload, wherever it was enqueued, comes first
-        if ((e = hipStreamWaitEvent(s, t->uploaded, 0)) != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
-    } else {
-        // the staging buffer may still feed the previous call's upload
-        if ((e = hipEventSynchronize(t->uploaded)) != hipSuccess) return device_fail(e, "hipEventSynchronize");
-        for (int32_t i = 0; i < t->n_ptrs; ++i) t->tab_staging[i] = ptrs[i];
-        t->have_last = false;
-        if ((e = hipMemcpyAsync(t->tab, t->tab_staging, (size_t)t->n_ptrs * sizeof(void*),
-                                hipMemcpyHostToDevice, s)) != hipSuccess)
-            return device_fail(e, "uploading the pointer table");
-        if ((e = hipEventRecord(t->uploaded, s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-        t->last_ptrs.assign(ptrs, ptrs + t->n_ptrs);
-        t->have_last = true;
-    }
-    if (t->groups == 0) return FP_OK;
-    SegArgs a;
-    a.segs = t->segs;
-    a.seg_of = t->seg_of;
-    a.dst_tab = t->tab;
-    a.src_tab = t->tab;
-    if ((e = launch_segments(a, t->groups, s)) != hipSuccess) return device_fail(e, "segment copy launch");
-    return FP_OK;
-}
 }  // namespace
 
 extern "C" fp_status fp_shard0_plan_create(int32_t n_params, const int32_t* ndims, const int64_t* shapes,
@@ -1254,22 +1252,6 @@ extern "C" fp_status fp_shard0_views(const fp_shard0_plan* plan, int32_t rank, f
 }
 
 namespace {
-// The pointer set a call of (op, es, rank) last passed validation with: a
-// call with the same pointers skips the checks (they depend on nothing else).
-bool seg_validated(SegCache& c, int op, int es, int rank, const std::vector<void*>& ptrs) {
-    for (const auto& v : c.validated)
-        if (v.op == op && v.es == es && v.rank == rank) return v.ptrs == ptrs;
-    return false;
-}
-void seg_remember(SegCache& c, int op, int es, int rank, const std::vector<void*>& ptrs) {
-    for (auto& v : c.validated)
-        if (v.op == op && v.es == es && v.rank == rank) {
-            v.ptrs = ptrs;
-            return;
-        }
-    c.validated.push_back({op, es, rank, ptrs});
-}
-
 // Null, alignment and overlap checks of the parameters against `other`
 // (dst or full); with `disjoint`, also of the parameters among themselves
 // (sorted by address: O(n log n)).

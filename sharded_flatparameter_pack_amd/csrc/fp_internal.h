@@ -30,8 +30,6 @@ constexpr int64_t kTileQuads = (int64_t)kThreads * kQuadsPerLane;
 // beside the resident barrier workgroups from the start.
 constexpr int kCopyWordsStream = 1;
 constexpr int kCopyWordsCoop = 4;
-constexpr int kPackBlockElems = 8192;  // flat elements per pack workgroup
-constexpr int kPackLdsTensors = 1024;  // tensor descriptors a pack workgroup stages in LDS
 constexpr int kMaxCoopQuads = 4;       // quads a lane keeps in registers in the one-pass step
 constexpr int kSyncGroups = 32;        // first level of the grid barrier
 constexpr int kLineWords = 32;         // 128-byte cache line in 32-bit words
@@ -280,16 +278,6 @@ struct LocalArgs {
     int64_t n;
 };
 
-struct PackArgs {
-    const int64_t* offsets;     // [n_tensors + 1] prefix sums, offsets[n] = T
-    const int32_t* group_first; // [n_groups + 1] first tensor overlapping each group
-    const void* const* src;     // [n_tensors] device pointers
-    void* flat;
-    int64_t total;              // T
-    int64_t padded;             // P
-    int32_t n_tensors;
-};
-
 // Launchers (return the HIP error of the launch).
 // `aligned`: every bf16 quad stream of the launch (gradients, own shard) is
 // 8-byte aligned; `copy_aligned` (and `aligned` for fp_unshard's kernel):
@@ -307,7 +295,6 @@ hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update
 hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
 hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, bool copy_aligned,
                             hipStream_t s);
-hipError_t launch_pack(const PackArgs& a, int elem_size, int64_t n_groups, hipStream_t s);
 hipError_t launch_segments(const SegArgs& a, int64_t n_groups, hipStream_t s);
 hipError_t launch_reduce_hybrid(const HybridArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_local(const LocalArgs& a, bool finish, bool accumulate, bool aligned, hipStream_t s);
