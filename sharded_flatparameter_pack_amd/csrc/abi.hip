@@ -14,7 +14,7 @@
 #include <new>
 #include <vector>
 
-#include "fp_internal.h"
+#include "fp_extra.h"
 
 using namespace fpk;
 

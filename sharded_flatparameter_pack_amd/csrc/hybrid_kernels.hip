@@ -17,6 +17,7 @@
 // time; the group boundaries only decide which running sum an element is
 // added to.
 
+#include "fp_extra.h"
 #include "step_ops.h"
 
 namespace fpk {

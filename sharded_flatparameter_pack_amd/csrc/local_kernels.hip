@@ -15,6 +15,7 @@
 // gradient (unscale, then clip to a global norm), and that advance the
 // dynamic loss scale after a step's overflow decision.
 
+#include "fp_extra.h"
 #include "step_ops.h"
 
 namespace fpk {

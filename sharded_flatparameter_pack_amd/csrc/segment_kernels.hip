@@ -15,6 +15,7 @@
 // then writes what would otherwise be many workgroups' partial cache lines.
 // Units are 2 bytes, so fp32 and bf16 buffers use the same kernel.
 
+#include "fp_extra.h"
 #include "step_ops.h"
 
 namespace fpk {
