@@ -446,7 +446,9 @@ def hybrid_bench(cfg, dev, reps: int, replicas: int = 2):
     F = cfg.world
     W = replicas * F
     S = fp.Plan(cfg.shapes, F).shard if cfg.shapes is not None else cfg.units()[0] // F
-    rows = gen.torch_bf16_normal(W * S, 1e-3, cfg.seed, (gen.STREAM_GRAD,), dev).view(W, S)
+    # each rank's row starts 16-byte aligned, as separate per-rank buffers would
+    Sp = -(-S // 8) * 8
+    rows = gen.torch_bf16_normal(W * Sp, 1e-3, cfg.seed, (gen.STREAM_GRAD,), dev).view(W, Sp)[:, :S]
     acc = torch.zeros(S, dtype=torch.float32, device=dev)
     legs = {"hybrid": lambda: fp.reduce_shard_hybrid(rows, acc, group=F, scale=1.0 / W),
             "flat_same_rows": lambda: fp.reduce_shard(rows, acc, scale=1.0 / W)}
