@@ -310,14 +310,19 @@ def time_steps(w, K, W, eager, ev):
     for _ in range(max(1, W // n)):
         graph.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    # an event between replays as well, for the spread over replays (one replay = n steps)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    marks[0].record()
+    for r in range(reps):
         graph.replay()
-    e1.record()
+        marks[r + 1].record()
     torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / K
+    step_ms = marks[0].elapsed_time(marks[-1]) / K
+    per_replay = sorted(marks[r].elapsed_time(marks[r + 1]) / n for r in range(reps))
+    time_steps.spread = {"median_ms_per_step": round(per_replay[len(per_replay) // 2], 5),
+                         "min_ms_per_step": round(per_replay[0], 5),
+                         "max_ms_per_step": round(per_replay[-1], 5), "replays": reps,
+                         "steps_per_replay": n}
     del graph
     ev_ms = eager_pass(W + K, min(K, 200))
     return step_ms, ev_ms, K, "HIP graph of one step per buffer set, replayed; span timed by hipEvents " \
@@ -663,7 +668,9 @@ def main(argv=None) -> int:
 
     w = make_workload(cfg, rank, dev, getattr(fp, MODE_FLAGS[args.mode]))
     S = w.S
+    time_steps.spread = None
     step_ms, ev_ms, K, timing = time_steps(w, args.steps, args.warmup, args.eager, ev)
+    spread = time_steps.spread
     bad = w.flagged()
     if bad:
         print(bad, file=sys.stderr)
@@ -687,6 +694,7 @@ def main(argv=None) -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(cfg.name, kernel_id)},
         "timing": timing,
+        "spread": spread,
         "source_hash": kernel_source_hash(),
     }
     if not args.no_extras:
