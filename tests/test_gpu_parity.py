@@ -438,3 +438,36 @@ def test_pack_same_buffers_new_contents(fp):
     torch.cuda.synchronize()
     for step, (got, host) in enumerate(outs):
         assert np.array_equal(to_host(got), oracle.pack(host, 8)), f"call {step}"
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16])
+def test_pack_many_small_tensors(fp, dtype):
+    """20 000 tensors of 0 to 1200 elements (each small tensor one gathering
+    entry) between a few larger ones (copy entries), each source at an odd
+    element offset."""
+    r = np.random.default_rng(17 if dtype == np.float32 else 18)
+    sizes = r.integers(0, 1200, size=20_000)
+    sizes[::997] = 5000                                   # a few copy entries between runs
+    shapes = [(int(n),) for n in sizes]
+    say(f"pack many small tensors dtype={np.dtype(dtype).name}")
+    flat_host = gen.normal_f32(int(sizes.sum()), 1.0, 7, gen.STREAM_TENSOR)
+    if dtype == np.uint16:
+        flat_host = gen.bf16_bits_trunc(flat_host)
+    host, o = [], 0
+    for n in sizes:
+        host.append(flat_host[o:o + n])
+        o += n
+    tdt = torch.float32 if dtype == np.float32 else torch.int16
+    big = torch.zeros(int(sizes.sum()) + 3 * len(sizes) + 8, dtype=tdt, device=dev())
+    srcs, o = [], 0
+    for i, h in enumerate(host):
+        o += 1 + i % 3                                    # odd element offsets
+        v = big[o:o + h.size]
+        if h.size:
+            v.copy_(to_dev(h))
+        srcs.append(v)
+        o += h.size
+    plan = fp.Plan(shapes, 64)
+    flat = plan.pack(srcs)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(flat).view(np.uint8), oracle.pack(host, 64).view(np.uint8))
