@@ -273,7 +273,8 @@ struct fp_plan {
     SegCache cache;                  // fp_pack's entry lists
 };
 
-extern "C" fp_status fp_plan_create(int32_t n_tensors, const int32_t* ndims, const int64_t* shapes,
+namespace {
+fp_status fp_plan_create_impl(int32_t n_tensors, const int32_t* ndims, const int64_t* shapes,
                                     int32_t world, fp_plan** out) {
     if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
     *out = nullptr;
@@ -324,6 +325,18 @@ extern "C" fp_status fp_plan_create(int32_t n_tensors, const int32_t* ndims, con
     p->shard = p->padded / world;
     *out = p;
     return FP_OK;
+}
+}  // namespace
+
+extern "C" fp_status fp_plan_create(int32_t n_tensors, const int32_t* ndims, const int64_t* shapes,
+                                    int32_t world, fp_plan** out) {
+    try {
+        return fp_plan_create_impl(n_tensors, ndims, shapes, world, out);
+    } catch (const std::bad_alloc&) {
+        return fail(FP_ERR_DEVICE, "out of host memory");
+    } catch (...) {
+        return fail(FP_ERR_DEVICE, "unexpected host error");
+    }
 }
 
 extern "C" void fp_plan_destroy(fp_plan* plan) {
@@ -419,7 +432,8 @@ std::vector<SegDesc> pack_segments(const fp_plan* p, int es) {
 }
 }  // namespace
 
-extern "C" fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const* src, void* flat,
+namespace {
+fp_status fp_pack_impl(fp_plan* plan, int32_t elem_size, const void* const* src, void* flat,
                              void* stream) {
     if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
     if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
@@ -446,6 +460,18 @@ extern "C" fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const
                              [&] { return pack_segments(plan, elem_size); }, &t);
     if (st != FP_OK) return st;
     return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+extern "C" fp_status fp_pack(fp_plan* plan, int32_t elem_size, const void* const* src, void* flat,
+                             void* stream) {
+    try {
+        return fp_pack_impl(plan, elem_size, src, flat, stream);
+    } catch (const std::bad_alloc&) {
+        return fail(FP_ERR_DEVICE, "out of host memory");
+    } catch (...) {
+        return fail(FP_ERR_DEVICE, "unexpected host error");
+    }
 }
 
 // ---------------------------------------------------------------------- reduce
@@ -840,7 +866,8 @@ void fill_units_args(const fp_units* u, UnitsArgs* a) {
 }
 }  // namespace
 
-extern "C" fp_status fp_units_create(int32_t n_units, int32_t world, int32_t rank, const int64_t* shard,
+namespace {
+fp_status fp_units_create_impl(int32_t n_units, int32_t world, int32_t rank, const int64_t* shard,
                                      const uint16_t* const* grads, const uint16_t* const* shards,
                                      uint16_t* const* full, fp_units** out) {
     if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
@@ -960,6 +987,19 @@ extern "C" fp_status fp_units_create(int32_t n_units, int32_t world, int32_t ran
     }
     *out = u;
     return FP_OK;
+}
+}  // namespace
+
+extern "C" fp_status fp_units_create(int32_t n_units, int32_t world, int32_t rank, const int64_t* shard,
+                                     const uint16_t* const* grads, const uint16_t* const* shards,
+                                     uint16_t* const* full, fp_units** out) {
+    try {
+        return fp_units_create_impl(n_units, world, rank, shard, grads, shards, full, out);
+    } catch (const std::bad_alloc&) {
+        return fail(FP_ERR_DEVICE, "out of host memory");
+    } catch (...) {
+        return fail(FP_ERR_DEVICE, "unexpected host error");
+    }
 }
 
 extern "C" void fp_units_destroy(fp_units* units) {
@@ -1159,7 +1199,8 @@ fp_status shard0_table(fp_shard0_plan* p, int op, int es, int rank, SegTable** o
 
 }  // namespace
 
-extern "C" fp_status fp_shard0_plan_create(int32_t n_params, const int32_t* ndims, const int64_t* shapes,
+namespace {
+fp_status fp_shard0_plan_create_impl(int32_t n_params, const int32_t* ndims, const int64_t* shapes,
                                            int32_t world, fp_shard0_plan** out) {
     if (out == nullptr) return fail(FP_ERR_INVALID, "out is NULL");
     *out = nullptr;
@@ -1219,6 +1260,18 @@ extern "C" fp_status fp_shard0_plan_create(int32_t n_params, const int32_t* ndim
     p->total = total;
     *out = p;
     return FP_OK;
+}
+}  // namespace
+
+extern "C" fp_status fp_shard0_plan_create(int32_t n_params, const int32_t* ndims, const int64_t* shapes,
+                                           int32_t world, fp_shard0_plan** out) {
+    try {
+        return fp_shard0_plan_create_impl(n_params, ndims, shapes, world, out);
+    } catch (const std::bad_alloc&) {
+        return fail(FP_ERR_DEVICE, "out of host memory");
+    } catch (...) {
+        return fail(FP_ERR_DEVICE, "unexpected host error");
+    }
 }
 
 extern "C" void fp_shard0_plan_destroy(fp_shard0_plan* plan) {
@@ -1281,7 +1334,8 @@ fp_status shard0_check_params(const fp_shard0_plan* p, int32_t es, const void* c
 }
 }  // namespace
 
-extern "C" fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
+namespace {
+fp_status fp_shard0_pack_impl(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
                                     const void* const* params, void* dst, void* stream) {
     if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
     if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
@@ -1306,8 +1360,21 @@ extern "C" fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int
     if (st != FP_OK) return st;
     return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
 }
+}  // namespace
 
-extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* full,
+extern "C" fp_status fp_shard0_pack(fp_shard0_plan* plan, int32_t elem_size, int32_t rank,
+                                    const void* const* params, void* dst, void* stream) {
+    try {
+        return fp_shard0_pack_impl(plan, elem_size, rank, params, dst, stream);
+    } catch (const std::bad_alloc&) {
+        return fail(FP_ERR_DEVICE, "out of host memory");
+    } catch (...) {
+        return fail(FP_ERR_DEVICE, "unexpected host error");
+    }
+}
+
+namespace {
+fp_status fp_shard0_unpack_impl(fp_shard0_plan* plan, int32_t elem_size, const void* full,
                                       void* const* params, void* stream) {
     if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
     if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
@@ -1328,6 +1395,18 @@ extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, c
     fp_status st = shard0_table(plan, kOpUnpack, elem_size, 0, &t);
     if (st != FP_OK) return st;
     return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+extern "C" fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* full,
+                                      void* const* params, void* stream) {
+    try {
+        return fp_shard0_unpack_impl(plan, elem_size, full, params, stream);
+    } catch (const std::bad_alloc&) {
+        return fail(FP_ERR_DEVICE, "out of host memory");
+    } catch (...) {
+        return fail(FP_ERR_DEVICE, "unexpected host error");
+    }
 }
 
 // ---------------------------------------------------------------------- reshard
@@ -1400,7 +1479,8 @@ extern "C" fp_status fp_reshard_plan_info(const fp_reshard_plan* plan, int64_t* 
     return FP_OK;
 }
 
-extern "C" fp_status fp_reshard(fp_reshard_plan* plan, int32_t elem_size, int32_t new_rank,
+namespace {
+fp_status fp_reshard_impl(fp_reshard_plan* plan, int32_t elem_size, int32_t new_rank,
                                 const void* const* old_shards, void* dst, void* stream) {
     if (plan == nullptr) return fail(FP_ERR_INVALID, "plan is NULL");
     if (elem_size != 2 && elem_size != 4) return fail(FP_ERR_INVALID, "elem_size must be 2 or 4");
@@ -1432,6 +1512,18 @@ extern "C" fp_status fp_reshard(fp_reshard_plan* plan, int32_t elem_size, int32_
                              [&] { return reshard_segments(plan, elem_size, new_rank); }, &t);
     if (st != FP_OK) return st;
     return seg_run(t, ptrs.data(), static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+extern "C" fp_status fp_reshard(fp_reshard_plan* plan, int32_t elem_size, int32_t new_rank,
+                                const void* const* old_shards, void* dst, void* stream) {
+    try {
+        return fp_reshard_impl(plan, elem_size, new_rank, old_shards, dst, stream);
+    } catch (const std::bad_alloc&) {
+        return fail(FP_ERR_DEVICE, "out of host memory");
+    } catch (...) {
+        return fail(FP_ERR_DEVICE, "unexpected host error");
+    }
 }
 
 // ---------------------------------------------------------------------- no_sync, scaler
