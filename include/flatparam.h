@@ -12,6 +12,10 @@
  *   unshard -- the bf16 cast and the all-gather's copy of every rank's
  *              shard back into the full flat buffer,
  *   views   -- the original tensors as full, fragment or empty views.
+ * Around that step: the per-parameter dim-0 layout (FSDP2), accumulation
+ * without communication (no_sync), the loss scaler's update and the
+ * gradient factor (unscale, global-norm clipping), the reduce of hybrid
+ * sharding, and resharding a flat buffer to another rank count.
  * On one GPU the N "ranks" are buffers on that GPU.
  *
  * Pages the operations follow (cited by title and section):
@@ -38,7 +42,10 @@
  *   returns a message for the calling thread's most recent failure.
  * The library keeps no global mutable state apart from that message and a
  * per-device cache of occupancy figures (fixed properties of the device and
- * the code object, computed on first use).
+ * the code object, computed on first use).  Plans (fp_plan, fp_units,
+ * fp_shard0_plan, fp_reshard_plan) own the device tables their calls build.
+ * A host allocation failure inside a call returns FP_ERR_DEVICE; no C++
+ * exception crosses this interface.
  */
 #ifndef FLATPARAM_H
 #define FLATPARAM_H
