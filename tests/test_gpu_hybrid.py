@@ -74,3 +74,29 @@ def test_hybrid_reduce_matches_oracle(fp, world, group, S, n_micro, offset):
     if not flag_o:
         want = oracle.sq_norm(acc_o)
         assert abs(float(sq.item()) - want) <= 1e-12 * want
+
+
+def test_hybrid_reduce_layer_d12288_full_size(fp):
+    """The d=12288 layer's slice for F = 8 (226.5M elements) reduced over
+    W = 16 ranks in two groups, compared with the oracle at 2^14 sampled
+    positions, with the overflow flag and the norm's determinism."""
+    from workloads import CONFIGS
+    import math as _m
+    cfg = CONFIGS["c4_layer_d12288_nd8"]
+    F, W = cfg.world, 2 * cfg.world
+    S = fp.Plan(cfg.shapes, F).shard
+    say(f"hybrid full size S={S} W={W} F={F}")
+    rows = gen.torch_bf16_normal(W * S, 1e-3, 5, (gen.STREAM_GRAD,), dev()).view(W, S)
+    idx = torch.from_numpy(np.sort(np.random.default_rng(4).choice(S, 1 << 14, replace=False))).to(dev())
+    acc = torch.empty(S, dtype=torch.float32, device=dev())
+    flag = torch.zeros(1, dtype=torch.int32, device=dev())
+    sq = torch.zeros(2, dtype=torch.float64, device=dev())
+    ws = fp.new_workspace(dev(), S)
+    fp.reduce_shard_hybrid(rows, acc, group=F, scale=1.0 / W, found_inf=flag, sq_norm=sq[0:1], workspace=ws)
+    fp.reduce_shard_hybrid(rows, acc, group=F, scale=1.0 / W, found_inf=flag, sq_norm=sq[1:2], workspace=ws)
+    torch.cuda.synchronize()
+    picked = [a for a in rows.index_select(1, idx).cpu().numpy().view(np.uint16)]
+    want = oracle.reduce_hybrid(picked, F, np.float32(1.0 / W))
+    assert_f32_bitexact(acc.index_select(0, idx).cpu().numpy(), want, "hybrid reduce, sampled")
+    assert int(flag.item()) == 0
+    assert float(sq[0].item()) == float(sq[1].item()) and _m.isfinite(float(sq[0].item()))

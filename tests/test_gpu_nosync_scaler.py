@@ -281,3 +281,33 @@ def test_units_step_with_gradient_factor(fp):
         assert_f32_close(got_th[o:o + S], th_o, f"unit {u} master")
         own = to_host(fulls[u])[rank * S:(rank + 1) * S]
         assert_bf16_within_1ulp(own, oracle.f32_to_bf16(th_o), f"unit {u} own shard")
+
+
+def test_no_sync_full_611m_unit(fp):
+    """The 611M-parameter model's whole unit on one rank, 4 micro-batches
+    accumulated without communication: the fp32 local sum after three and
+    the exchanged bf16 row after the fourth, checked against the oracle at
+    2^14 sampled positions (the oracle gets the gathered inputs)."""
+    from workloads import CONFIGS
+    cfg = CONFIGS["c3_611m_buckets_nd16"]
+    n = sum(cfg.units())
+    say(f"no_sync full unit n={n}")
+    idx = torch.from_numpy(np.sort(np.random.default_rng(3).choice(n, 1 << 14, replace=False))).to(dev())
+    local = torch.empty(n, dtype=torch.float32, device=dev())
+    picked = []
+    for m in range(cfg.n_micro):
+        g = gen.torch_bf16_normal(n, cfg.grad_sigma, cfg.seed, (gen.STREAM_GRAD, m), dev())
+        picked.append(g.index_select(0, idx).cpu().numpy().view(np.uint16))
+        if m < cfg.n_micro - 1:
+            fp.local_accumulate(g, local, accumulate=m > 0)
+        else:
+            out = torch.empty(n, dtype=torch.int16, device=dev())
+            fp.local_finish(g, out, local, accumulate=True)
+        del g
+    torch.cuda.synchronize()
+    loc_o = None
+    for m in range(cfg.n_micro - 1):
+        loc_o = oracle.local_accumulate(picked[m], loc_o, accumulate=m > 0)
+    row_o = oracle.local_finish(picked[-1], loc_o, accumulate=True)
+    assert_f32_bitexact(local.index_select(0, idx).cpu().numpy(), loc_o, "local sum")
+    assert_bf16_equal(out.index_select(0, idx).cpu().numpy().view(np.uint16), row_o, "exchanged row")
