@@ -40,6 +40,15 @@
  *   enqueued, except FP_ERR_DEVICE after a failed launch.  Faults inside a
  *   kernel surface at the caller's next synchronisation.  fp_last_error()
  *   returns a message for the calling thread's most recent failure.
+ * Sizes: a dispatch holds at most (2^32 - 1) / 256 = 16 777 215 workgroups
+ *   of 256 lanes.  A call whose launch would need more returns FP_ERR_RANGE
+ *   before enqueueing anything.  The streaming kernels (reduce, AdamW,
+ *   no_sync) take 1024 elements per workgroup, so S up to about 1.7e10;
+ *   fp_unshard takes 2048 per shard and workgroup.  The two-phase and
+ *   no-skip shard step holds the reduce tiles and the N - 1 other shards'
+ *   copy tiles in its first launch, which bounds S to about 3.8e9 at N = 8.
+ *   The copy kernel of pack, the dim-0 layout and resharding counts the
+ *   workgroups of its whole entry list against the same limit.
  * The library keeps no global mutable state apart from that message and a
  * per-device cache of occupancy figures (fixed properties of the device and
  * the code object, computed on first use).  Plans (fp_plan, fp_units,

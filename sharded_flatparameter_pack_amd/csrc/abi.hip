@@ -44,6 +44,17 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A dispatch packet carries the grid size as a 32-bit count of work-items,
+// so one launch of 256-lane workgroups takes at most this many.
+constexpr int64_t kMaxGroups = 0xFFFFFFFFLL / kThreads;
+
+fp_status check_groups(int64_t groups, const char* what) {
+    if (groups > kMaxGroups)
+        return fail(FP_ERR_RANGE, "%s needs %lld workgroups, more than one launch holds (%lld)", what,
+                    (long long)groups, (long long)kMaxGroups);
+    return FP_OK;
+}
+
 // Workgroups of a tiled stream over S elements in 4-element quads.
 int64_t stream_grid(int64_t shard) {
     const int64_t t = tiles_of(shard >> 2);
@@ -180,7 +191,7 @@ fp_status seg_table(SegCache& c, int op, int es, int rank, int32_t n_ptrs, Build
         segs[s].words = (segs[s].kind == kSegCopy && segs[s].len < ((int64_t)1 << 20)) ? 2 : 1;
         segs[s].tile0 = g;
         const int64_t n = segment_tiles(segs[s]);
-        if (g + n > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "layout too large for one launch");
+        if (g + n > kMaxGroups) return check_groups(g + n, "the copy layout");
         for (int64_t k = 0; k < n; ++k) seg_of.push_back((int32_t)s);
         g += n;
     }
@@ -488,6 +499,7 @@ fp_status reduce_args(int64_t shard, int32_t world, const uint16_t* const* grads
                       bool* aligned_grads) {
     fp_status st;
     if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
+    if ((st = check_groups(stream_grid(shard), "the reduce")) != FP_OK) return st;
     if ((st = check_world(world)) != FP_OK) return st;
     if ((st = check_ptr_table(grads, world, shard, false, "grads")) != FP_OK) return st;
     if ((st = check_f32(acc, shard, "acc")) != FP_OK) return st;
@@ -558,6 +570,7 @@ extern "C" fp_status fp_adamw_shard(int64_t shard, const fp_adamw_hparams* hp, c
                                     void* stream) {
     fp_status st;
     if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
+    if ((st = check_groups(stream_grid(shard), "AdamW")) != FP_OK) return st;
     AdamArgs a;
     std::memset(&a, 0, sizeof a);
     if ((st = check_hparams(hp, &a.c)) != FP_OK) return st;
@@ -598,6 +611,7 @@ extern "C" fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* co
                                 uint16_t* full, void* stream) {
     fp_status st;
     if (shard < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
+    if ((st = check_groups(copy_tiles_per_shard(shard, kCopyWordsStream), "the unshard")) != FP_OK) return st;
     if ((st = check_world(world)) != FP_OK) return st;
     if ((st = check_ptr_table(shards, world, shard, true, "shards")) != FP_OK) return st;
     if (full == nullptr && shard > 0) return fail(FP_ERR_INVALID, "full is NULL");
@@ -631,6 +645,11 @@ fp_status check_step(const fp_step_args& x, AdamCoef* c) {
     if (S < 0) return fail(FP_ERR_RANGE, "shard must be >= 0");
     if ((st = check_world(x.world)) != FP_OK) return st;
     if (x.rank < 0 || x.rank >= x.world) return fail(FP_ERR_RANGE, "rank %d outside [0, %d)", x.rank, x.world);
+    // the first launch of the two-phase and no-skip paths: reduce tiles and
+    // the other shards' copy tiles
+    if ((st = check_groups(stream_grid(S) + (int64_t)(x.world - 1) * copy_tiles_per_shard(S, kCopyWordsStream),
+                           "the step")) != FP_OK)
+        return st;
     if (x.flags & ~(FP_STEP_NO_SKIP | FP_STEP_KEEP_GRAD | FP_STEP_NO_COOP))
         return fail(FP_ERR_INVALID, "unknown flags");
     if ((st = check_hparams(&x.hp, c)) != FP_OK) return st;
@@ -762,7 +781,6 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     a.reduce_groups = (int32_t)reduce_groups;
     a.copy_tiles = (int32_t)copy_tiles_per_shard(S, kCopyWordsStream);
     const int64_t n_groups = reduce_groups + (int64_t)(x.world - 1) * a.copy_tiles;
-    if (n_groups > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "shard too large for one launch");
     AdamArgs d;
     std::memset(&d, 0, sizeof d);
     d.grad = x.acc;
@@ -902,7 +920,7 @@ fp_status fp_units_create_impl(int32_t n_units, int32_t world, int32_t rank, con
         tiles += unit_tiles(S);
         if (unshard) copies += (int64_t)(world - 1) * copy_tiles_per_shard(S, kCopyWordsStream);
     }
-    if (tiles + copies > 0x7FFFFFFF) return fail(FP_ERR_RANGE, "units too large for one launch");
+    if ((st = check_groups(tiles + copies, "the units' step")) != FP_OK) return st;
 
     fp_units* u = new (std::nothrow) fp_units();
     if (u == nullptr) return fail(FP_ERR_DEVICE, "out of host memory");
@@ -1533,11 +1551,12 @@ fp_status local_call(int64_t n, const uint16_t* grad, int32_t accumulate, const 
                      bool finish, void* stream) {
     if (n < 0) return fail(FP_ERR_RANGE, "n must be >= 0");
     if (n == 0) return FP_OK;
+    fp_status st = check_groups(stream_grid(n), "the local accumulation");
+    if (st != FP_OK) return st;
     if (grad == nullptr) return fail(FP_ERR_INVALID, "grad is NULL");
     if (!aligned(grad, 2)) return fail(FP_ERR_ALIGN, "grad misaligned");
     if (accumulate || !finish) {
-        fp_status st = check_f32(local, n, "local");
-        if (st != FP_OK) return st;
+        if ((st = check_f32(local, n, "local")) != FP_OK) return st;
         if (overlap(grad, n * 2, local, n * 4)) return fail(FP_ERR_INVALID, "grad overlaps local");
     }
     bool al = is_aligned8(grad);

@@ -190,6 +190,58 @@ def test_device_entry_points_reject_bad_arguments(fp):
     assert L.fp_status_string(-3) == b"misaligned pointer"
 
 
+# One dispatch carries a 32-bit work-item count: at most (2^32 - 1) // 256
+# workgroups of 256 lanes.  Each streaming kernel covers 1024 elements per
+# workgroup, each copy 2048 (one 16-byte word per lane).
+MAX_GROUPS = (2 ** 32 - 1) // 256
+
+
+def test_launch_size_limit_without_a_device(fp):
+    """Sizes whose grid would not fit one dispatch are refused with
+    FP_ERR_RANGE before any launch, with a message naming the limit;
+    otherwise valid fake addresses are never dereferenced."""
+    from sharded_flatparameter_pack_amd import _lib
+    L = fp.lib()
+    over = MAX_GROUPS * 1024 + 4                 # one streaming tile too many
+    step = 1 << 40                                # keeps the fake buffers apart
+    g = (C.c_void_p * 2)(step, 2 * step)
+    acc = C.c_void_p(3 * step)
+
+    def refused(status):
+        return status == -2 and b"more than one launch holds" in L.fp_last_error()
+
+    assert refused(_status(L.fp_reduce_shard, over, 2, g, 1.0, 0, acc, None, None, None, None))
+    assert refused(_status(L.fp_reduce_shard_hybrid, over, 2, 1, g, 1.0, 0, acc, None, None, None, None))
+    hp = _lib.fp_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    ptr = [C.c_void_p(step * (i + 1)) for i in range(4)]
+    assert refused(_status(L.fp_adamw_shard, over, C.byref(hp), *ptr, None, None, None, None))
+    assert refused(_status(L.fp_local_accumulate, over, g[0], 0, acc, None))
+    assert refused(_status(L.fp_local_finish, over, g[0], 0, None, acc, None))
+    # the unshard: (S / 8 + 1) words per shard, 256 per workgroup
+    sh = (C.c_void_p * 2)(step, 2 * step)
+    s_copy = (MAX_GROUPS * 256 - 1) * 8 + 8
+    assert refused(_status(L.fp_unshard, s_copy, 2, sh, C.c_void_p(4 * step), None))
+    # the two-phase step's first launch holds the reduce tiles and the copy
+    # tiles of the N - 1 other shards: 1 + 7/2 workgroups per 1024 elements
+    # at N = 8, so shards of about 3.8e9 elements (48 bytes each, 180 GB of
+    # HBM) are already too large for it
+    grads = (C.c_void_p * 8)(*[step * (i + 1) for i in range(8)])
+    shards = (C.c_void_p * 8)(None, *[step * (i + 9) for i in range(7)])
+    a = _lib.fp_step_args()
+    a.world, a.rank, a.scale = 8, 0, 0.125
+    a.grads, a.shards = C.cast(grads, C.c_void_p), C.cast(shards, C.c_void_p)
+    a.acc, a.master, a.exp_avg, a.exp_avg_sq = 17 * step, 18 * step, 19 * step, 20 * step
+    a.hp = _lib.fp_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    a.full, a.found_inf = 21 * step, 29 * step
+    a.flags = _lib.FP_STEP_NO_SKIP
+    path = C.c_int32(-1)
+    a.shard = 3_000_000_000
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
+    a.shard = 3_900_000_000
+    assert refused(_status(L.fp_step_path, C.byref(a), C.byref(path)))
+    assert refused(_status(L.fp_shard_step, C.byref(a), None))
+
+
 def test_step_path_without_a_device(fp):
     """fp_step_path validates like fp_shard_step and launches nothing; the
     paths that need no occupancy query are decided on the host (fake,
