@@ -545,6 +545,18 @@ def copy_calibration(fp, dev, launches: int) -> int:
     return 0
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(cfg, rank, budget_s: float):
     """The serial CPU oracle on a bounded sample of the workload, on one host core:
     whole shard steps (all micro-batches) of a shard of at most 2M elements with
@@ -579,7 +591,7 @@ def cpu_baseline(cfg, rank, budget_s: float):
         what += f" of unit 0 (of {len(cfg.units())})"
     return {"value": round(S * reps * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "params_per_s": round(S * reps / dt, 1), "seconds": round(dt, 2),
-            "host_cores_available": len(old), "cpu": platform.processor() or platform.machine(),
+            "host_cores_available": len(old), "cpu": cpu_model(),
             "sample": f"{reps} shard steps of {what} of the {cfg.name} workload (rank {rank}, N_d={world}, "
                       f"{n} micro-batch(es)) by the serial oracle: reduce, AdamW, bf16 cast, unshard"}
 
