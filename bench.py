@@ -96,6 +96,14 @@ class HipEvents:
 
 
 # ------------------------------------------------------------------ workloads
+def row_stride(S: int) -> int:
+    """Elements between consecutive simulated ranks' rows of S bf16 elements
+    cut from one tensor: S rounded up to 64, so that every row starts on a
+    128-byte cache line, as a separate allocation would (the torch allocator
+    aligns blocks to 512 bytes)."""
+    return -(-S // 64) * 64
+
+
 class SingleUnit:
     """Buffer sets of one rank's step on one unit (fp_shard_step)."""
 
@@ -109,9 +117,7 @@ class SingleUnit:
         per_set = S * (2 * world + 16 + 2 * (world - 1) + 2 * world)
         self.n_sets = max(2, math.ceil(ROTATE_BYTES / per_set))
         self.sets = []
-        # each simulated rank's rows start 16-byte aligned, as separate per-rank
-        # buffers would (row stride rounded up to 8 elements)
-        Sp = -(-S // 8) * 8
+        Sp = row_stride(S)
         for k in range(self.n_sets):
             key = lambda stream, q=0: (stream, k, 0, q)  # noqa: E731
             grads = gen.torch_bf16_normal(world * Sp, cfg.grad_sigma, cfg.seed, key(gen.STREAM_GRAD), dev)
@@ -188,11 +194,13 @@ class Bucketed:
             offs.append(offs[-1] + S)
         self.sets = []
         for k in range(self.n_sets):
-            # rank q's gradient (and shard) rows of bucket b are slices of one buffer per set and micro-batch
-            grads = [gen.torch_bf16_normal(N * self.S, cfg.grad_sigma, cfg.seed, (gen.STREAM_GRAD, k, m), dev)
-                     .view(N, self.S) for m in range(n)]
-            others = gen.torch_bf16_normal(N * self.S, cfg.master_sigma, cfg.seed, (gen.STREAM_SHARD, k),
-                                           dev).view(N, self.S)
+            # rank q's gradient (and shard) rows of bucket b are slices of one
+            # buffer per set and micro-batch; rank q's row starts a cache line
+            Rp = row_stride(self.S)
+            grads = [gen.torch_bf16_normal(N * Rp, cfg.grad_sigma, cfg.seed, (gen.STREAM_GRAD, k, m), dev)
+                     .view(N, Rp) for m in range(n)]
+            others = gen.torch_bf16_normal(N * Rp, cfg.master_sigma, cfg.seed, (gen.STREAM_SHARD, k),
+                                           dev).view(N, Rp)
             full = [torch.zeros(N * S, dtype=torch.int16, device=dev) for S in sizes]
             g_rows = [[[grads[m][q, o:o + S] for q in range(N)] for o, S in zip(offs, sizes)]
                       for m in range(n)]
@@ -451,8 +459,7 @@ def hybrid_bench(cfg, dev, reps: int, replicas: int = 2):
     F = cfg.world
     W = replicas * F
     S = fp.Plan(cfg.shapes, F).shard if cfg.shapes is not None else cfg.units()[0] // F
-    # each rank's row starts 16-byte aligned, as separate per-rank buffers would
-    Sp = -(-S // 8) * 8
+    Sp = row_stride(S)
     rows = gen.torch_bf16_normal(W * Sp, 1e-3, cfg.seed, (gen.STREAM_GRAD,), dev).view(W, Sp)[:, :S]
     acc = torch.zeros(S, dtype=torch.float32, device=dev)
     legs = {"hybrid": lambda: fp.reduce_shard_hybrid(rows, acc, group=F, scale=1.0 / W),
