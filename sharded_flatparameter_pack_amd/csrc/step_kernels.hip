@@ -195,9 +195,20 @@ hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipS
     return hipGetLastError();
 }
 
+// Large shards run AdamW with at most four workgroups resident per CU: the
+// launch asks for 40 KiB of dynamic LDS, which the kernel never touches, so
+// that 160 KiB of LDS admits four.  With its four read and four write streams
+// AdamW lost bandwidth at full occupancy on the largest shards (fp_adamw_shard
+// alone on MI355X: 226.5M elements 1231 us uncapped, 1154 us capped; 100M
+// 508 vs 499 us); from 42.6M elements down the cap cost 0.5-2.5 %, so
+// shards under 2^26 elements keep full occupancy.
+constexpr int64_t kAdamCapElems = (int64_t)1 << 26;
+constexpr unsigned kAdamCapLds = 40u << 10;
+
 hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s) {
-    if (aligned) adamw_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(a);
-    else adamw_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(a);
+    const unsigned lds = a.shard >= kAdamCapElems ? kAdamCapLds : 0u;
+    if (aligned) adamw_kernel<true><<<(unsigned)grid, kThreads, lds, s>>>(a);
+    else adamw_kernel<false><<<(unsigned)grid, kThreads, lds, s>>>(a);
     return hipGetLastError();
 }
 
