@@ -113,7 +113,7 @@ fp_status fp_plan_info(const fp_plan* plan, int64_t* numel, int64_t* padded, int
  * src: host array of n_tensors device pointers, each to a contiguous
  *   row-major tensor aligned to elem_size; NULL only for empty tensors.
  * flat: device buffer of P elements, 16-byte aligned, not overlapping any
- *   source.
+ *   source; NULL only when P = 0.
  * On its first call on a device the plan allocates and uploads its tensor
  * tables to that device (hipMalloc / pinned host staging; released by
  * fp_plan_destroy).  A call whose source pointers differ from the previous

@@ -454,7 +454,7 @@ fp_status fp_pack_impl(fp_plan* plan, int32_t elem_size, const void* const* src,
     for (int32_t i = 0; i < plan->n; ++i) ptrs[1 + i] = const_cast<void*>(src[i]);
     std::lock_guard<std::mutex> lock(plan->cache.mu);
     if (!seg_validated(plan->cache, kOpFlatPack, elem_size, 0, ptrs)) {
-        if (flat == nullptr) return fail(FP_ERR_INVALID, "flat is NULL");
+        if (flat == nullptr && plan->padded > 0) return fail(FP_ERR_INVALID, "flat is NULL");
         if (!aligned(flat, 16)) return fail(FP_ERR_ALIGN, "flat is not 16-byte aligned");
         const int64_t flat_bytes = plan->padded * elem_size;
         for (int32_t i = 0; i < plan->n; ++i) {
