@@ -226,7 +226,7 @@ inline int64_t unit_tiles(int64_t S) {
 // `aligned`: every bf16 quad stream of the launch (gradients, own shard) is
 // 8-byte aligned; `copy_aligned` (and `aligned` for fp_unshard's kernel):
 // every copy source is 16-byte aligned at the words the kernel reads.  Then
-// no realignment code runs for those streams.
+// those streams take the aligned form of the accesses.
 hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s);
