@@ -641,6 +641,8 @@ def main(argv=None) -> int:
                     help="only time the hybrid-sharding reduce (F = N_d, W = 2F) against the flat one")
     ap.add_argument("--reshard-only", action="store_true",
                     help="only time resharding the workload's fp32 flat state to 2 N_d and N_d / 2 ranks")
+    ap.add_argument("--pack-only", action="store_true",
+                    help="only time fp_pack of the workload's FlatParameter (fp32 tensors)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)
@@ -668,6 +670,12 @@ def main(argv=None) -> int:
             print(f"{cfg.name} has no parameter shapes", file=sys.stderr)
             return 2
         print(json.dumps(shard0_bench(cfg, dev, max(1, args.steps))), flush=True)
+        return 0
+    if args.pack_only:
+        if cfg.shapes is None:
+            print(f"{cfg.name} has no tensor shapes", file=sys.stderr)
+            return 2
+        print(json.dumps(pack_bench(cfg, dev, max(1, args.steps))), flush=True)
         return 0
     if args.reshard_only:
         print(json.dumps(reshard_bench(cfg, dev, max(1, args.steps))), flush=True)
