@@ -31,6 +31,20 @@ constexpr int64_t kTileQuads = (int64_t)kThreads * kQuadsPerLane;
 constexpr int kCopyWordsStream = 1;
 constexpr int kCopyWordsCoop = 4;
 constexpr int kMaxCoopQuads = 4;       // quads a lane keeps in registers in the one-pass step
+
+// Streaming kernels with many loads in flight per lane (the reduce, AdamW)
+// run shards of kCapElems elements and more with at most four workgroups
+// resident per CU: the launch asks for kCapLds bytes of dynamic LDS, which
+// the kernels never touch, so that 160 KiB of LDS admits four.  Measured on
+// MI355X at full occupancy they lost bandwidth on the largest shards
+// (fp_adamw_shard at 226.5M elements: 1231 us uncapped, 1154 us capped;
+// fp_reduce_shard of 8 ranks: 906 vs 844 us; at 100M 508 vs 499 and 389
+// vs 379 us), while from 42.6M elements down the cap cost up to 2.5 %.
+// Copies (few loads per lane) lose under the cap, so launches that copy
+// keep full occupancy.
+constexpr int64_t kCapElems = (int64_t)1 << 26;
+constexpr unsigned kCapLds = 40u << 10;
+inline unsigned capped_lds(int64_t shard) { return shard >= kCapElems ? kCapLds : 0u; }
 constexpr int kSyncGroups = 32;        // first level of the grid barrier
 constexpr int kLineWords = 32;         // 128-byte cache line in 32-bit words
 

@@ -171,8 +171,9 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
 
 template <bool kAligned, bool kAcc, bool kNorm>
 void reduce_launch(const ReduceArgs& a, dim3 g, bool wide, hipStream_t s) {
-    if (wide) reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, 0, s>>>(a);
-    else reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, 0, s>>>(a);
+    const unsigned lds = capped_lds(a.shard);
+    if (wide) reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, lds, s>>>(a);
+    else reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, lds, s>>>(a);
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStream_t s) {
@@ -195,18 +196,8 @@ hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipS
     return hipGetLastError();
 }
 
-// Large shards run AdamW with at most four workgroups resident per CU: the
-// launch asks for 40 KiB of dynamic LDS, which the kernel never touches, so
-// that 160 KiB of LDS admits four.  With its four read and four write streams
-// AdamW lost bandwidth at full occupancy on the largest shards (fp_adamw_shard
-// alone on MI355X: 226.5M elements 1231 us uncapped, 1154 us capped; 100M
-// 508 vs 499 us); from 42.6M elements down the cap cost 0.5-2.5 %, so
-// shards under 2^26 elements keep full occupancy.
-constexpr int64_t kAdamCapElems = (int64_t)1 << 26;
-constexpr unsigned kAdamCapLds = 40u << 10;
-
 hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s) {
-    const unsigned lds = a.shard >= kAdamCapElems ? kAdamCapLds : 0u;
+    const unsigned lds = capped_lds(a.shard);
     if (aligned) adamw_kernel<true><<<(unsigned)grid, kThreads, lds, s>>>(a);
     else adamw_kernel<false><<<(unsigned)grid, kThreads, lds, s>>>(a);
     return hipGetLastError();
