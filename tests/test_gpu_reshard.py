@@ -111,3 +111,27 @@ def test_reshard_layer_parameters_full_size(fp, N2):
     del out
     want = oracle.reshard([host[q * S:(q + 1) * S] for q in range(N)], T, N2)
     assert _same(got, want)
+
+
+@pytest.mark.parametrize("N2", [128, 32])
+def test_reshard_ragged_10k_fp32_full_size(fp, N2):
+    """The 10k-tensor FlatParameter's fp32 state (2.73G elements, as the bench
+    times it) cut for 64 ranks recut for 128 and for 32, every new rank's
+    shard in one call, compared in full with the oracle."""
+    cfg = CONFIGS["c5_ragged10k_nd64"]
+    T = sum(math.prod(s) for s in cfg.shapes)
+    N = cfg.world
+    say(f"reshard full size fp32 T={T} {N} -> {N2}")
+    plan = fp.ReshardPlan(T, N, N2)
+    S = plan.shard_old
+    flat = torch.zeros(N * S, dtype=torch.float32, device=dev())
+    flat[:T] = gen.torch_normal_f32(T, 0.02, 4, (gen.STREAM_MASTER,), dev())
+    out = plan.reshard([flat[q * S:(q + 1) * S] for q in range(N)])
+    torch.cuda.synchronize()
+    host = to_host(flat)
+    del flat
+    got = to_host(out)
+    del out
+    want = oracle.reshard([host[q * S:(q + 1) * S] for q in range(N)], T, N2)
+    assert _same(got, want)
+    plan.close()

@@ -9,8 +9,8 @@ from fp_shard0_unpack.  Cases: the pages' worked examples, random groups
 with 0-d, empty and uneven parameters at worlds 1 .. 128, sources and
 destinations at odd element offsets, NaN / -0 payloads, destinations
 pre-filled with garbage (the padding must be written), repeated calls with
-other buffers, and the Transformer-layer group of d=1024 and d=12288 at
-eight ranks at full size.
+other buffers, the Transformer-layer group of d=1024 and d=12288 at eight
+ranks and the 10k-tensor group at 64 ranks at full size.
 """
 
 import math
@@ -251,6 +251,40 @@ def test_shard0_transformer_layer_full_size(fp, name):
     want = oracle.shard0_unpack(want_full, shapes, world)
     for i, (o, w) in enumerate(zip(outs, want)):
         assert _same(to_host(o), w), f"parameter {i}"
+
+
+def test_shard0_ragged_10k_full_size(fp):
+    """The 10k-tensor group at 64 ranks at full size (2.73G bf16 elements, the
+    parameters views of one allocation, as the bench lays them out): every
+    rank's rows in full against the oracle, and the gathered layout back into
+    the parameters, which must reproduce them bit for bit (the oracle's
+    unpack inverts its pack, a CPU pin)."""
+    cfg = CONFIGS["c5_ragged10k_nd64"]
+    world = cfg.world
+    shapes = list(cfg.shapes)
+    numel = [math.prod(s) for s in shapes]
+    T = sum(numel)
+    offs = [0]
+    for n in numel[:-1]:
+        offs.append(offs[-1] + n)
+    say(f"shard0 full size c5: {len(shapes)} parameters, {T} elements, world={world}")
+    flat = gen.torch_bf16_normal(T, 1e-3, 12, (gen.STREAM_TENSOR,), dev())
+    plan = fp.Shard0Plan(shapes, world)
+    full = plan.pack([flat[o:o + n].view(s) for o, n, s in zip(offs, numel, shapes)])
+    torch.cuda.synchronize()
+    host_flat = to_host(flat)
+    host = [host_flat[o:o + n].reshape(s) for o, n, s in zip(offs, numel, shapes)]
+    got = to_host(full)
+    S = plan.shard
+    assert got.size == world * S
+    for q in range(world):
+        assert _same(got[q * S:(q + 1) * S], oracle.shard0_pack(host, world, q)), f"rank {q}"
+    del host, host_flat, got
+    back = torch.empty_like(flat)
+    plan.unpack(full, [back[o:o + n].view(s) for o, n, s in zip(offs, numel, shapes)])
+    torch.cuda.synchronize()
+    assert torch.equal(back, flat)
+    plan.close()
 
 
 @pytest.mark.parametrize("rank", [0, 3])
