@@ -7,6 +7,8 @@ W / F from 8 / 1 to 128 / 16 and 12 / 4, ragged sizes with odd offsets,
 accumulation over micro-batches, injected inf.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -100,3 +102,27 @@ def test_hybrid_reduce_layer_d12288_full_size(fp):
     assert_f32_bitexact(acc.index_select(0, idx).cpu().numpy(), want, "hybrid reduce, sampled")
     assert int(flag.item()) == 0
     assert float(sq[0].item()) == float(sq[1].item()) and _m.isfinite(float(sq[0].item()))
+
+
+@pytest.mark.parametrize("layout", ["line-aligned rows", "packed rows"])
+def test_hybrid_ragged_10k_full_size(fp, layout):
+    """The 10k-tensor group's slice for F = 64 (42.6M elements) reduced over
+    W = 128 ranks in two groups, with each rank's row on a cache line (as the
+    bench lays them out) and packed back to back (rows 4-byte aligned, the
+    unaligned loads), against the oracle at 2^14 sampled positions."""
+    from workloads import CONFIGS
+    cfg = CONFIGS["c5_ragged10k_nd64"]
+    F, W = cfg.world, 2 * cfg.world
+    S = -(-sum(math.prod(s) for s in cfg.shapes) // F)
+    Sp = -(-S // 64) * 64 if layout == "line-aligned rows" else S
+    say(f"hybrid full size S={S} W={W} F={F} {layout}")
+    rows = gen.torch_bf16_normal(W * Sp, 1e-3, 6, (gen.STREAM_GRAD,), dev()).view(W, Sp)[:, :S]
+    idx = torch.from_numpy(np.sort(np.random.default_rng(5).choice(S, 1 << 14, replace=False))).to(dev())
+    acc = torch.empty(S, dtype=torch.float32, device=dev())
+    flag = torch.zeros(1, dtype=torch.int32, device=dev())
+    fp.reduce_shard_hybrid(rows, acc, group=F, scale=1.0 / W, found_inf=flag)
+    torch.cuda.synchronize()
+    picked = [a for a in rows.index_select(1, idx).cpu().numpy().view(np.uint16)]
+    want = oracle.reduce_hybrid(picked, F, np.float32(1.0 / W))
+    assert_f32_bitexact(acc.index_select(0, idx).cpu().numpy(), want, "hybrid reduce, sampled")
+    assert int(flag.item()) == 0
