@@ -6,7 +6,8 @@
   bucket reduced and updated on the GPU; the oracle recomputes 2^14 sampled
   elements per bucket from the same inputs; full-size properties (other
   shards copied bit for bit, own shard = bf16 of the new master).
-* d=12288 layer unit, N_d=8 (226.5M-element shard): sampled oracle parity
+* d=12288 layer unit, N_d=8 (226.5M-element shard): the fp32 pack of its 12
+  tensors checked tensor by tensor; sampled oracle parity of the step
   plus the same properties and the gradient norm against an fp64 sum.
 * 10k ragged tensors (2.73G elements), N_d=64: the pack checked tensor by
   tensor against its source and at sampled positions by the oracle's
@@ -207,6 +208,30 @@ def test_layer_d12288_shard(fp):
     assert torch.equal(full[S:], others[S:])                      # rank 0: every other shard
     norm = float(acc.double().square().sum().item())
     assert float(sq.item()) == pytest.approx(norm, rel=1e-12)
+
+
+def test_layer_d12288_pack(fp):
+    """The d=12288 layer's 12 fp32 tensors (1.81G elements, 7.25 GB) packed as
+    the bench packs them: every tensor's range of the FlatParameter equal to
+    the tensor bit for bit, and every rank's views of the right lengths."""
+    cfg = CONFIGS["c4_layer_d12288_nd8"]
+    numel = [math.prod(s) for s in cfg.shapes]
+    say(f"d12288 pack: {len(numel)} tensors, {sum(numel)} elements")
+    plan = fp.Plan(cfg.shapes, cfg.world)
+    tensors = [gen.torch_normal_f32(n, 1.0, cfg.seed, (gen.STREAM_TENSOR, i), dev()).view(s)
+               for i, (n, s) in enumerate(zip(numel, cfg.shapes))]
+    flat = plan.pack(tensors)
+    torch.cuda.synchronize()
+    o = 0
+    for i, t in enumerate(tensors):
+        assert torch.equal(flat[o:o + numel[i]].view(torch.int32), t.reshape(-1).view(torch.int32)), f"tensor {i}"
+        o += numel[i]
+    assert o == plan.padded                               # 8 divides T: no padding
+    S = plan.shard
+    for q in range(cfg.world):
+        _, ln, _ = oracle.views(numel, cfg.world, q)
+        assert [v.numel() for v in plan.views(flat[q * S:(q + 1) * S], q)] == list(ln)
+    plan.close()
 
 
 # ------------------------------------------------------------------ 10k ragged tensors
