@@ -1122,9 +1122,6 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
 
 // ---------------------------------------------------------------------- dim-0 layout
 
-namespace {
-}  // namespace
-
 struct fp_shard0_plan {
     int32_t n = 0, world = 1;
     std::vector<int32_t> ndims;
