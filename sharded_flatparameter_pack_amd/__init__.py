@@ -67,6 +67,22 @@ def _dev_ptr(t, dtypes, n, name):
     return t.data_ptr()
 
 
+def _one_device(*objs):
+    """All tensors of one call (nested lists and [N, S] tensors included) on one device."""
+    devs = set()
+    todo = list(objs)
+    while todo:
+        o = todo.pop()
+        if o is None:
+            continue
+        if isinstance(o, (list, tuple)):
+            todo.extend(o)
+        else:
+            devs.add(o.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors of one call sit on several devices: {sorted(map(str, devs))}")
+
+
 def _f32(t, n, name):
     return _dev_ptr(t, (_torch().float32,), n, name)
 
@@ -143,6 +159,7 @@ class Plan:
         None) and returns it, with the tensors checked and their pointers
         marshalled once -- for repeated packs of the same buffers.  The
         caller keeps the tensors alive and in place."""
+        _one_device(tensors, flat)
         torch = _torch()
         if len(tensors) != len(self.shapes):
             raise ValueError("tensor count differs from the plan")
@@ -237,6 +254,7 @@ class Shard0Plan:
         """A callable writing rank `rank`'s buffer (rank = -1: every rank's,
         the gathered layout) of `params` into `dst` (allocated here when
         None) and returning it; pointers are marshalled once."""
+        _one_device(params, dst)
         torch = _torch()
         dtype, esize, ptrs = self._params(params)
         n = self.shard * (self.world if rank < 0 else 1)
@@ -258,6 +276,7 @@ class Shard0Plan:
         """A callable writing every parameter (global shape) from the gathered
         buffer `full` into `params` (allocated here when None) and returning
         them."""
+        _one_device(full, params)
         torch = _torch()
         if params is None:
             params = [torch.empty(s, dtype=full.dtype, device=full.device) for s in self.shapes]
@@ -304,6 +323,7 @@ class ReshardPlan:
         """A callable writing new rank `rank`'s shard (rank = -1: every new
         rank's, one after the other) from the old shards into dst (allocated
         here when None) and returning it; pointers are marshalled once."""
+        _one_device(old_shards, dst)
         torch = _torch()
         if len(old_shards) != self.world_old:
             raise ValueError(f"need {self.world_old} old shards")
@@ -356,6 +376,7 @@ def workspace_timeouts(workspace) -> int:
 def reduce_shard(grads, acc, *, scale: float, accumulate: bool = False, found_inf=None,
                  sq_norm=None, workspace=None):
     """acc (= or +=) scale * sum of the ranks' bf16 gradients, fixed rank order."""
+    _one_device(grads, acc, found_inf, sq_norm, workspace)
     torch = _torch()
     S = acc.numel()
     ptrs = _rank_ptrs(grads, S, "grads")
@@ -371,6 +392,7 @@ def reduce_shard_hybrid(grads, acc, *, group: int, scale: float, accumulate: boo
                         sq_norm=None, workspace=None):
     """acc (= or +=) scale * two-level sum of the W ranks' bf16 gradients: inside
     each group of `group` consecutive ranks, then across the groups."""
+    _one_device(grads, acc, found_inf, sq_norm, workspace)
     torch = _torch()
     S = acc.numel()
     ptrs = _rank_ptrs(grads, S, "grads")
@@ -397,6 +419,7 @@ def adamw_shard(grad, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps, wei
                 step: int, found_inf=None, param_bf16=None, grad_coef=None):
     """In-place AdamW on fp32 master / exp_avg / exp_avg_sq; bf16 copy to param_bf16.
     grad_coef: optional device float64 factor applied to the gradient (see grad_coef())."""
+    _one_device(grad, master, exp_avg, exp_avg_sq, found_inf, param_bf16, grad_coef)
     torch = _torch()
     S = master.numel()
     hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
@@ -411,6 +434,7 @@ def adamw_shard(grad, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps, wei
 def local_accumulate(grad, local, *, accumulate: bool):
     """local (fp32) = (local if accumulate else 0) + grad (bf16): one micro-batch
     accumulated without communication."""
+    _one_device(grad, local)
     n = local.numel()
     check(lib().fp_local_accumulate(n, _bf16(grad, n, "grad"), int(bool(accumulate)),
                                     _f32(local, n, "local"), _stream(local)))
@@ -420,6 +444,7 @@ def local_accumulate(grad, local, *, accumulate: bool):
 def local_finish(grad, out, local=None, *, accumulate: bool):
     """out (bf16) = bf16(local + grad), or bf16(grad) when not accumulating: the
     row this rank contributes to the reduce-scatter."""
+    _one_device(grad, out, local)
     n = out.numel()
     lp = _f32(local, n, "local") if local is not None else None
     check(lib().fp_local_finish(n, _bf16(grad, n, "grad"), int(bool(accumulate)), lp, _bf16(out, n, "out"),
@@ -430,6 +455,7 @@ def local_finish(grad, out, local=None, *, accumulate: bool):
 def grad_coef(coef, *, sq_norm=None, loss_scale=None, max_norm: float = 0.0):
     """coef (device float64[1]) = 1 / loss_scale, times the global-norm clip
     factor min(1, max_norm / (||g|| + 1e-6)) when max_norm > 0."""
+    _one_device(coef, sq_norm, loss_scale)
     torch = _torch()
     sq = _dev_ptr(sq_norm, (torch.float64,), 1, "sq_norm") if sq_norm is not None else None
     ls = _dev_ptr(loss_scale, (torch.float32,), 1, "loss_scale") if loss_scale is not None else None
@@ -441,6 +467,7 @@ def grad_coef(coef, *, sq_norm=None, loss_scale=None, max_norm: float = 0.0):
 def scaler_update(found_inf, scale, clean_steps, *, growth_factor: float = 2.0, backoff_factor: float = 0.5,
                   growth_interval: int = 2000):
     """Dynamic loss scaling on device values after a step's overflow decision."""
+    _one_device(found_inf, scale, clean_steps)
     torch = _torch()
     check(lib().fp_scaler_update(_dev_ptr(found_inf, (torch.int32,), 1, "found_inf"),
                                  _dev_ptr(scale, (torch.float32,), 1, "scale"),
@@ -452,6 +479,7 @@ def scaler_update(found_inf, scale, clean_steps, *, growth_factor: float = 2.0, 
 # ------------------------------------------------------------------ unshard
 def unshard(shards, full):
     """full[q*S:(q+1)*S] = shards[q]; a None entry leaves that range untouched."""
+    _one_device(shards, full)
     world = len(shards) if not hasattr(shards, "dim") else shards.shape[0]
     S = full.numel() // world
     if S * world != full.numel():
@@ -487,6 +515,8 @@ class ShardStep:
                  scale: float, lr, beta1, beta2, eps, weight_decay, found_inf,
                  accumulate: bool = False, sq_norm=None, workspace=None,
                  flags: int = FP_STEP_EXACT_SKIP, grad_coef=None):
+        _one_device(grads, acc, master, exp_avg, exp_avg_sq, shards, full, found_inf, sq_norm, workspace,
+                    grad_coef)
         torch = _torch()
         S = master.numel()
         gptr = _rank_ptrs(grads, S, "grads")
@@ -552,6 +582,7 @@ class Units:
     """
 
     def __init__(self, grads, rank: int, shards=None, full=None):
+        _one_device(grads, shards, full)
         torch = _torch()
         n = len(grads)
         if n < 1:
@@ -616,6 +647,7 @@ class Units:
 
     def reduce(self, acc, *, scale: float, accumulate: bool = False, found_inf=None, sq_norm=None,
                workspace=None):
+        _one_device(acc, found_inf, sq_norm, workspace)
         torch = _torch()
         check(lib().fp_units_reduce(
             self._h, float(scale), int(bool(accumulate)), C.c_void_p(_f32(acc, self.partition, "acc")),
@@ -626,6 +658,7 @@ class Units:
     def step(self, acc, master, exp_avg, exp_avg_sq, *, scale: float, lr, beta1, beta2, eps,
              weight_decay, step: int, found_inf, accumulate: bool = False, sq_norm=None,
              workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None, grad_coef=None):
+        _one_device(acc, master, exp_avg, exp_avg_sq, found_inf, sq_norm, workspace, grad_coef)
         torch = _torch()
         P = self.partition
         a = _lib.fp_units_step_args()

@@ -429,3 +429,18 @@ def test_reshard_plan_and_validation_without_a_device(fp):
     assert _status(L.fp_reshard, plan._h, 2, -1, ov, dst, None) == -1
     assert _status(L.fp_reshard_plan_info, None, None, None) == -1
     L.fp_reshard_plan_destroy(None)
+
+
+def test_binding_rejects_tensors_on_several_devices(fp):
+    """The binding checks that one call's tensors share a device before it
+    marshals anything (a CPU and a meta tensor stand in for two devices)."""
+    import torch
+    from sharded_flatparameter_pack_amd import _one_device
+    a, b = torch.empty(8), torch.empty(8, device="meta")
+    _one_device(a, [a, None], None, [[a], (a,)])
+    with pytest.raises(ValueError, match="several devices"):
+        _one_device(a, [[a, b]])
+    with pytest.raises(ValueError, match="several devices"):
+        fp.unshard([a, b], a)
+    with pytest.raises(ValueError, match="several devices"):
+        fp.reduce_shard(torch.empty(2, 8, dtype=torch.int16), b, scale=0.5)
