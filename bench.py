@@ -162,6 +162,9 @@ class SingleUnit:
             return [("step_coop_kernel", "step_coop", step_ms, S * B, 1)]
         k1, k2 = ev_ms[1] - ev_ms[0], ev_ms[2] - ev_ms[1]
         f1 = k1 / (k1 + k2)
+        if self.path == fp.FP_PATH_NO_SKIP_SPLIT:      # fused reduce + AdamW + cast, then the copies
+            return [("step_phase1_kernel<true>", "step_phase1_fused", step_ms * f1, S * (B - 4 * (N - 1)), 1),
+                    ("unshard_kernel", "unshard", step_ms * (1 - f1), S * 4 * (N - 1), 1)]
         return [("step_phase1_kernel<false>", "step_phase1", step_ms * f1, S * (2 * N + 4 * (N - 1)), 1),
                 ("adamw_kernel", "adamw", step_ms * (1 - f1), S * 26, 1)]
 
@@ -691,7 +694,7 @@ def main(argv=None) -> int:
     B = step_bytes_per_elem(world, n)
     ev = HipEvents()
     path_names = {fp.FP_PATH_ONE_PASS: "one-pass", fp.FP_PATH_TWO_PHASE: "two-phase",
-                  fp.FP_PATH_NO_SKIP: "fused-no-skip"}
+                  fp.FP_PATH_NO_SKIP: "fused-no-skip", fp.FP_PATH_NO_SKIP_SPLIT: "fused-no-skip-split"}
 
     w = make_workload(cfg, rank, dev, getattr(fp, MODE_FLAGS[args.mode]))
     S = w.S

@@ -340,12 +340,18 @@ fp_status fp_shard_step(const fp_step_args* args, void* stream);
  *   FP_PATH_ONE_PASS  -- one kernel (then the norm finalisation if sq_norm);
  *   FP_PATH_TWO_PHASE -- reduce + copy kernel, then the AdamW kernel;
  *   FP_PATH_NO_SKIP   -- one fused kernel (then the norm finalisation if
- *                        sq_norm).
+ *                        sq_norm);
+ *   FP_PATH_NO_SKIP_SPLIT -- the no-skip step of a shard of 2^26 elements
+ *                        or more: the fused reduce + AdamW + cast kernel at
+ *                        reduced occupancy, then the copy of the other
+ *                        shards in a kernel of its own (then the norm
+ *                        finalisation if sq_norm).
  * The one-pass choice depends on the device's co-resident capacity, hence
  * on the device current at the call. */
 #define FP_PATH_ONE_PASS 0
 #define FP_PATH_TWO_PHASE 1
 #define FP_PATH_NO_SKIP 2
+#define FP_PATH_NO_SKIP_SPLIT 3
 fp_status fp_step_path(const fp_step_args* args, int32_t* path);
 
 /* ------------------------------------------------------------------ units */

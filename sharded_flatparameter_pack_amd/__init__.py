@@ -20,14 +20,14 @@ import math
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_ONE_PASS,  # noqa: F401
+from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_NO_SKIP_SPLIT, FP_PATH_ONE_PASS,  # noqa: F401
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
 __all__ = ["Plan", "Units", "Shard0Plan", "ReshardPlan", "reduce_shard_hybrid", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
-           "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "library_path"]
+           "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "FP_PATH_NO_SKIP_SPLIT", "library_path"]
 
 
 def library_path() -> str:
@@ -558,7 +558,7 @@ class ShardStep:
         check(self._fn(C.byref(a), _stream(self._device)))
 
     def path(self) -> int:
-        """FP_PATH_ONE_PASS, FP_PATH_TWO_PHASE or FP_PATH_NO_SKIP: the kernels
+        """FP_PATH_ONE_PASS, FP_PATH_TWO_PHASE, FP_PATH_NO_SKIP or FP_PATH_NO_SKIP_SPLIT: the kernels
         a call launches on this device."""
         torch = _torch()
         out = C.c_int32(-1)

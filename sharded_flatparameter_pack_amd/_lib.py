@@ -27,6 +27,7 @@ FP_STEP_EVENTS = 3
 FP_PATH_ONE_PASS = 0
 FP_PATH_TWO_PHASE = 1
 FP_PATH_NO_SKIP = 2
+FP_PATH_NO_SKIP_SPLIT = 3
 FP_WORKSPACE_TIMEOUTS_OFFSET = 8320
 
 _i32, _i64, _f32, _f64, _vp = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p

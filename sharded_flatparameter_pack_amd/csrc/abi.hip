@@ -694,7 +694,7 @@ fp_status step_path(const fp_step_args& x, int32_t* path, int* variant, int* gri
     *variant = -1;
     *grid = 0;
     if (x.flags & FP_STEP_NO_SKIP) {
-        *path = FP_PATH_NO_SKIP;
+        *path = x.shard >= kCapElems ? FP_PATH_NO_SKIP_SPLIT : FP_PATH_NO_SKIP;
         return FP_OK;
     }
     if (x.workspace != nullptr && !(x.flags & FP_STEP_NO_COOP)) {
@@ -728,7 +728,8 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     int variant = -1, grid = 0;
     if ((st = step_path(x, &path, &variant, &grid)) != FP_OK) return st;
 
-    const bool no_skip = path == FP_PATH_NO_SKIP;
+    const bool no_skip = path == FP_PATH_NO_SKIP || path == FP_PATH_NO_SKIP_SPLIT;
+    const bool split = path == FP_PATH_NO_SKIP_SPLIT;
     for (int32_t q = 0; q < x.world; ++q) {
         a.grads[q] = x.grads[q];
         a.shards[q] = q == x.rank ? nullptr : x.shards[q];
@@ -795,8 +796,20 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     d.partials = a.partials;
     d.sq_norm = x.sq_norm;
     d.n_partials = (int32_t)reduce_groups;
-    if ((e = launch_step_phase1(a, n_groups, no_skip, aligned, copy_aligned, s)) != hipSuccess) return device_fail(e, "step launch");
+    if ((e = launch_step_phase1(a, split ? reduce_groups : n_groups, no_skip, split, aligned, copy_aligned, s)) !=
+        hipSuccess)
+        return device_fail(e, "step launch");
     if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (split) {
+        // the copy of the other shards, at full occupancy
+        UnshardArgs u;
+        std::memset(&u, 0, sizeof u);
+        for (int32_t q = 0; q < x.world; ++q) u.shards[q] = a.shards[q];
+        u.full = a.full;
+        u.shard = S;
+        u.world = x.world;
+        if ((e = launch_unshard(u, a.copy_tiles, copy_aligned, s)) != hipSuccess) return device_fail(e, "copy launch");
+    }
     if (no_skip) {
         if (x.sq_norm != nullptr &&
             (e = launch_norm_finalize(a.partials, (int)reduce_groups, x.sq_norm, s)) != hipSuccess)

@@ -245,7 +245,9 @@ hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStr
 hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hipStream_t s);
-hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool aligned,
+// `capped`: the launch holds only the reduce workgroups (the copies run in a
+// launch of their own), which then run at the large-shard occupancy cap.
+hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool capped, bool aligned,
                               bool copy_aligned, hipStream_t s);
 // One-pass exact-skip step: plan_step_coop picks the variant (lanes keep
 // 2 or 4 quads in registers) and a grid that fits the device's co-resident

@@ -212,27 +212,28 @@ hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hi
 
 namespace {
 template <bool kAligned, bool kCopyAligned, bool kFused>
-void phase1_launch(const StepArgs& a, dim3 g, hipStream_t s) {
-    if (wide_group(a.world)) step_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, 0, s>>>(a);
-    else step_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, 0, s>>>(a);
+void phase1_launch(const StepArgs& a, dim3 g, unsigned lds, hipStream_t s) {
+    if (wide_group(a.world)) step_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, lds, s>>>(a);
+    else step_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, lds, s>>>(a);
 }
 
 template <bool kAligned, bool kCopyAligned>
-void phase1_launch(const StepArgs& a, dim3 g, bool fused, hipStream_t s) {
-    if (fused) phase1_launch<kAligned, kCopyAligned, true>(a, g, s);
-    else phase1_launch<kAligned, kCopyAligned, false>(a, g, s);
+void phase1_launch(const StepArgs& a, dim3 g, bool fused, unsigned lds, hipStream_t s) {
+    if (fused) phase1_launch<kAligned, kCopyAligned, true>(a, g, lds, s);
+    else phase1_launch<kAligned, kCopyAligned, false>(a, g, lds, s);
 }
 }  // namespace
 
-hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool aligned,
+hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool capped, bool aligned,
                               bool copy_aligned, hipStream_t s) {
     const dim3 g((unsigned)grid);
+    const unsigned lds = capped ? capped_lds(a.shard) : 0u;
     if (aligned) {
-        if (copy_aligned) phase1_launch<true, true>(a, g, fused_update, s);
-        else phase1_launch<true, false>(a, g, fused_update, s);
+        if (copy_aligned) phase1_launch<true, true>(a, g, fused_update, lds, s);
+        else phase1_launch<true, false>(a, g, fused_update, lds, s);
     } else {
-        if (copy_aligned) phase1_launch<false, true>(a, g, fused_update, s);
-        else phase1_launch<false, false>(a, g, fused_update, s);
+        if (copy_aligned) phase1_launch<false, true>(a, g, fused_update, lds, s);
+        else phase1_launch<false, false>(a, g, fused_update, lds, s);
     }
     return hipGetLastError();
 }

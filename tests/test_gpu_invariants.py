@@ -246,3 +246,47 @@ def test_units_step_equals_single_unit_steps(fp):
         oracle.adamw(acc_o, th_o, m_o, v_o, step=1, skip=False, **hp_kwargs(HP))
         assert_f32_close(to_host(plan.unit_slice(state[1].view, 2)), th_o, "unit 2 master")
         plan.close()
+
+
+@pytest.mark.parametrize("world,rank,full_off", [(8, 3, 0), (3, 1, 1)])
+def test_split_no_skip_step_at_large_shards(fp, world, rank, full_off):
+    """From 2^26 elements on, the no-skip step runs the fused reduce + AdamW +
+    cast at reduced occupancy and the copies in a launch of their own: on
+    overflow-free inputs it ends bitwise where the two-phase exact-skip step
+    does, writes nothing outside its outputs, and its reduced gradient matches
+    the oracle at sampled positions."""
+    S = (1 << 26) + 3
+    say(f"split no-skip vs two-phase: world={world} S={S} rank={rank} full offset={full_off}")
+    grads = [gen.torch_bf16_normal(S, 1e-3, 70, (gen.STREAM_GRAD, q), dev()) for q in range(world)]
+    others = [gen.torch_bf16_normal(S, 0.02, 70, (gen.STREAM_SHARD, q), dev()) for q in range(world)]
+    shards = [None if q == rank else others[q] for q in range(world)]
+    th0 = gen.torch_normal_f32(S, 0.02, 70, (gen.STREAM_MASTER,), dev())
+    m0 = gen.torch_normal_f32(S, 1e-4, 70, (gen.STREAM_EXP_AVG,), dev())
+    v0 = gen.torch_normal_f32(S, 1e-3, 70, (gen.STREAM_EXP_AVG_SQ,), dev()).square()
+    results = {}
+    for name, flags, want in (("split", fp.FP_STEP_NO_SKIP, fp.FP_PATH_NO_SKIP_SPLIT),
+                              ("two-phase", fp.FP_STEP_NO_COOP, fp.FP_PATH_TWO_PHASE)):
+        b = dict(acc=Guarded(S, torch.float32), th=Guarded(S, torch.float32, init=th0),
+                 m=Guarded(S, torch.float32, init=m0), v=Guarded(S, torch.float32, init=v0),
+                 full=Guarded(world * S, torch.int16, off=full_off), sq=Guarded(1, torch.float64),
+                 flag=Guarded(1, torch.int32, init=torch.zeros(1, dtype=torch.int32, device=dev())))
+        ws = Guarded(fp.workspace_bytes(S), torch.uint8,
+                     init=torch.zeros(fp.workspace_bytes(S), dtype=torch.uint8, device=dev()))
+        call = fp.ShardStep(grads, b["acc"].view, b["th"].view, b["m"].view, b["v"].view, shards, b["full"].view,
+                            rank, scale=1.0 / world, found_inf=b["flag"].view, sq_norm=b["sq"].view,
+                            workspace=ws.view, flags=flags | fp.FP_STEP_KEEP_GRAD, **hp_kwargs(HP))
+        assert call.path() == want
+        call(2)
+        _check(*b.values(), ws)
+        assert int(b["flag"].view.item()) == 0
+        results[name] = {k: g.view.clone() for k, g in b.items()}
+        del b, ws, call
+        torch.cuda.empty_cache()
+    for k in ("acc", "th", "m", "v", "full", "flag"):
+        assert torch.equal(results["split"][k].view(torch.uint8), results["two-phase"][k].view(torch.uint8)), k
+    assert float(results["split"]["sq"].item()) == pytest.approx(float(results["two-phase"]["sq"].item()), rel=1e-12)
+    idx = torch.from_numpy(np.sort(np.random.default_rng(3).choice(S, 1 << 12, replace=False))).to(dev())
+    rows = [to_host(g.index_select(0, idx)) for g in grads]
+    want = oracle.reduce(rows, np.float32(1.0 / world))
+    got = to_host(results["split"]["acc"].index_select(0, idx))
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
