@@ -341,7 +341,7 @@ fp_status fp_shard_step(const fp_step_args* args, void* stream);
  *   FP_PATH_TWO_PHASE -- reduce + copy kernel, then the AdamW kernel;
  *   FP_PATH_NO_SKIP   -- one fused kernel (then the norm finalisation if
  *                        sq_norm);
- *   FP_PATH_NO_SKIP_SPLIT -- the no-skip step of a shard of 2^26 elements
+ *   FP_PATH_NO_SKIP_SPLIT -- the no-skip step of a shard of 2^24 elements
  *                        or more: the fused reduce + AdamW + cast kernel at
  *                        reduced occupancy, then the copy of the other
  *                        shards in a kernel of its own (then the norm

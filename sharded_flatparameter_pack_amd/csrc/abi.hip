@@ -694,7 +694,7 @@ fp_status step_path(const fp_step_args& x, int32_t* path, int* variant, int* gri
     *variant = -1;
     *grid = 0;
     if (x.flags & FP_STEP_NO_SKIP) {
-        *path = x.shard >= kCapElems ? FP_PATH_NO_SKIP_SPLIT : FP_PATH_NO_SKIP;
+        *path = x.shard >= kSplitElems ? FP_PATH_NO_SKIP_SPLIT : FP_PATH_NO_SKIP;
         return FP_OK;
     }
     if (x.workspace != nullptr && !(x.flags & FP_STEP_NO_COOP)) {

@@ -45,6 +45,12 @@ constexpr int kMaxCoopQuads = 4;       // quads a lane keeps in registers in the
 constexpr int64_t kCapElems = (int64_t)1 << 26;
 constexpr unsigned kCapLds = 40u << 10;
 inline unsigned capped_lds(int64_t shard) { return shard >= kCapElems ? kCapLds : 0u; }
+// The fused no-skip step of shards from kSplitElems elements on runs its
+// reduce + AdamW workgroups under the same cap and the copies of the other
+// shards in a launch of their own (measured: the d=12288 layer at 8 ranks
+// 2.64 -> 2.54 ms, the 10k-tensor group at 64 ranks, 42.6M elements, 2.97 ->
+// 2.90 ms); smaller shards keep one launch.
+constexpr int64_t kSplitElems = (int64_t)1 << 24;
 constexpr int kSyncGroups = 32;        // first level of the grid barrier
 constexpr int kLineWords = 32;         // 128-byte cache line in 32-bit words
 
@@ -246,7 +252,7 @@ hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipS
 hipError_t launch_adamw(const AdamArgs& a, int64_t grid, bool aligned, hipStream_t s);
 hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hipStream_t s);
 // `capped`: the launch holds only the reduce workgroups (the copies run in a
-// launch of their own), which then run at the large-shard occupancy cap.
+// launch of their own), which then run at the occupancy cap.
 hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool capped, bool aligned,
                               bool copy_aligned, hipStream_t s);
 // One-pass exact-skip step: plan_step_coop picks the variant (lanes keep

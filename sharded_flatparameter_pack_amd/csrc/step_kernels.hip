@@ -227,7 +227,7 @@ void phase1_launch(const StepArgs& a, dim3 g, bool fused, unsigned lds, hipStrea
 hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update, bool capped, bool aligned,
                               bool copy_aligned, hipStream_t s) {
     const dim3 g((unsigned)grid);
-    const unsigned lds = capped ? capped_lds(a.shard) : 0u;
+    const unsigned lds = capped ? kCapLds : 0u;
     if (aligned) {
         if (copy_aligned) phase1_launch<true, true>(a, g, fused_update, lds, s);
         else phase1_launch<true, false>(a, g, fused_update, lds, s);

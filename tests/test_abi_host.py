@@ -269,14 +269,14 @@ def test_step_path_without_a_device(fp):
     a.master = 0x4000010                       # overlaps acc
     assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -1
     assert _status(L.fp_step_path, C.byref(a), None) == -1
-    # shards of 2^26 elements and more: the no-skip step splits off the copies
+    # shards of 2^24 elements and more: the no-skip step splits off the copies
     step = 1 << 40
     grads2 = (C.c_void_p * 2)(step, 2 * step)
     shards2 = (C.c_void_p * 2)(None, 3 * step)
     a.grads, a.shards = C.cast(grads2, C.c_void_p), C.cast(shards2, C.c_void_p)
     a.acc, a.master, a.exp_avg, a.exp_avg_sq = 4 * step, 5 * step, 6 * step, 7 * step
     a.full, a.found_inf, a.workspace = 8 * step, 9 * step, None
-    for S, want in ((1 << 26, _lib.FP_PATH_NO_SKIP_SPLIT), ((1 << 26) - 4, _lib.FP_PATH_NO_SKIP)):
+    for S, want in ((1 << 24, _lib.FP_PATH_NO_SKIP_SPLIT), ((1 << 24) - 4, _lib.FP_PATH_NO_SKIP)):
         a.shard, a.flags = S, _lib.FP_STEP_NO_SKIP
         assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
         assert path.value == want

@@ -250,12 +250,12 @@ def test_units_step_equals_single_unit_steps(fp):
 
 @pytest.mark.parametrize("world,rank,full_off", [(8, 3, 0), (3, 1, 1)])
 def test_split_no_skip_step_at_large_shards(fp, world, rank, full_off):
-    """From 2^26 elements on, the no-skip step runs the fused reduce + AdamW +
+    """From 2^24 elements on, the no-skip step runs the fused reduce + AdamW +
     cast at reduced occupancy and the copies in a launch of their own: on
     overflow-free inputs it ends bitwise where the two-phase exact-skip step
     does, writes nothing outside its outputs, and its reduced gradient matches
     the oracle at sampled positions."""
-    S = (1 << 26) + 3
+    S = (1 << 24) + 3 if world > 4 else (1 << 26) + 3
     say(f"split no-skip vs two-phase: world={world} S={S} rank={rank} full offset={full_off}")
     grads = [gen.torch_bf16_normal(S, 1e-3, 70, (gen.STREAM_GRAD, q), dev()) for q in range(world)]
     others = [gen.torch_bf16_normal(S, 0.02, 70, (gen.STREAM_SHARD, q), dev()) for q in range(world)]
