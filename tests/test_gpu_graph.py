@@ -9,8 +9,9 @@ eagerly (the kernels are deterministic); one pass sees an injected +inf in
 one set, so the flag cleared inside the graph and the skip it gates are
 replayed too.  The first eager pass is checked against the oracle as well.  Paths: the one-pass step at the d=1024 layer's
 shard shape (S = 1,574,528, N_d = 8), the two-phase and the fused no-skip
-step at the same shape, and the multi-unit reduce + step over unequal units
-with two micro-batches.
+step at the same shape, the no-skip step from 2^24 elements on (fused update
+and copies in two launches) at S = 2^24 + 3, N_d = 8, and the multi-unit
+reduce + step over unequal units with two micro-batches.
 """
 
 import numpy as np
@@ -154,6 +155,86 @@ def test_step_graph_replays_match_eager(fp, flags, path):
         for k, s in enumerate(sets):
             assert fp.workspace_timeouts(s["ws"]) == 0
     del graph
+
+
+def test_split_no_skip_graph_replays_match_eager(fp):
+    world, S, rank = 8, (1 << 24) + 3, 6
+    say(f"graph replays: split no-skip step S={S} N={world}")
+    seed = 43
+    grads = torch.stack([gen.torch_bf16_normal(S, 1e-3, seed, (gen.STREAM_GRAD, q), dev()) for q in range(world)])
+    others = [gen.torch_bf16_normal(S, 0.02, seed, (gen.STREAM_SHARD, q), dev()) for q in range(world)]
+    shards = [None if q == rank else others[q] for q in range(world)]
+    init = [gen.torch_normal_f32(S, 0.02, seed, (gen.STREAM_MASTER,), dev()),
+            gen.torch_normal_f32(S, 1e-4, seed, (gen.STREAM_EXP_AVG,), dev()),
+            gen.torch_normal_f32(S, 1e-3, seed, (gen.STREAM_EXP_AVG_SQ,), dev()).square()]
+    state = [t.clone() for t in init]
+    acc = torch.zeros(S, dtype=torch.float32, device=dev())
+    full = torch.zeros(world * S, dtype=torch.int16, device=dev())
+    flag = torch.zeros(1, dtype=torch.int32, device=dev())
+    sq = torch.zeros(1, dtype=torch.float64, device=dev())
+    ws = fp.new_workspace(dev(), S)
+    call = fp.ShardStep(grads, acc, *state, shards, full, rank, scale=1.0 / world, found_inf=flag, sq_norm=sq,
+                        workspace=ws, flags=fp.FP_STEP_NO_SKIP, **hp_kwargs(HP))
+    assert call.path() == fp.FP_PATH_NO_SKIP_SPLIT
+    pos = S - 2                            # pass 1 sees +inf here in rank 4's row (the ragged tail)
+    keep = int(grads[4, pos].item())
+    scratch = _scratch(fp)
+
+    steps = [2, 3, 2, 3]                   # the step number is a launch argument: one graph per number
+
+    def run(r):
+        if r == 1:
+            grads[4, pos] = 0x7F80
+        flag.zero_()
+        call(steps[r])
+
+    def after(r):
+        if r == 1:
+            grads[4, pos] = keep
+
+    def snap():
+        return [t.clone() for t in (*state, full, flag, sq)]
+
+    eager = []
+    for r in range(REPLAYS):
+        run(r)
+        torch.cuda.synchronize()
+        after(r)
+        eager.append(snap())
+        assert int(flag.item()) == (1 if r == 1 else 0)
+        if r == 0:
+            # the first pass against the oracle at sampled positions
+            idx = torch.from_numpy(np.sort(np.random.default_rng(5).choice(S, 1 << 12, replace=False))).to(dev())
+            rows = [to_host(grads[q].index_select(0, idx)) for q in range(world)]
+            g_o = oracle.reduce(rows, np.float32(1.0 / world))
+            th_o, m_o, v_o = (to_host(t.index_select(0, idx)) for t in init)
+            oracle.adamw(g_o, th_o, m_o, v_o, step=2, skip=False, **hp_kwargs(HP))
+            for name, g, w in zip(("master", "exp_avg", "exp_avg_sq"), state, (th_o, m_o, v_o)):
+                assert_f32_close(to_host(g.index_select(0, idx)), w, name)
+    for t, t0 in zip(state, init):
+        t.copy_(t0)
+    full.zero_()
+    sq.zero_()
+    torch.cuda.synchronize()
+
+    graphs = {}
+    for n in (2, 3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            flag.zero_()
+            call(n)
+        graphs[n] = g
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        if r == 1:
+            grads[4, pos] = 0x7F80
+        graphs[steps[r]].replay()
+        torch.cuda.synchronize()
+        after(r)
+        _assert_same(snap(), eager[r], f"replay {r}")
+        _interleave(fp, scratch)
+        assert fp.workspace_timeouts(ws) == 0
+    del graphs
 
 
 def test_units_graph_replays_match_eager(fp):
