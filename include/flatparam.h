@@ -329,6 +329,18 @@ typedef struct fp_step_args {
      * norm (for clipping by it, use fp_reduce_shard, fp_grad_coef and
      * fp_adamw_shard) -- the loss scaler's unscale factor, typically. */
     const double* grad_coef;
+    /* All three NULL (the state is updated in place), or all three device
+     * fp32[S], distinct from every other buffer of the call: the speculative
+     * form of the step.  The new master / exp_avg / exp_avg_sq go to these
+     * buffers and master / exp_avg / exp_avg_sq are only read, so the
+     * update need not wait for the overflow check.  With FP_STEP_EXACT_SKIP,
+     * on overflow the outputs receive the unchanged input state (and full
+     * the bf16 of the unchanged master), which is the skipped step's result;
+     * the caller swaps input and output buffers after each step either way.
+     * With FP_STEP_NO_SKIP the outputs receive the update regardless. */
+    float* master_out;
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
 } fp_step_args;
 
 #define FP_STEP_EVENTS 3
@@ -336,7 +348,9 @@ typedef struct fp_step_args {
 fp_status fp_shard_step(const fp_step_args* args, void* stream);
 
 /* The kernels fp_shard_step launches for these arguments on the current
- * device, after the same argument checks (nothing is launched):
+ * device, after the same argument checks (nothing is launched).  With the
+ * output state buffers given, FP_STEP_EXACT_SKIP always takes one of the
+ * speculative paths, FP_STEP_NO_SKIP the no-skip ones:
  *   FP_PATH_ONE_PASS  -- one kernel (then the norm finalisation if sq_norm);
  *   FP_PATH_TWO_PHASE -- reduce + copy kernel, then the AdamW kernel;
  *   FP_PATH_NO_SKIP   -- one fused kernel (then the norm finalisation if
@@ -346,12 +360,22 @@ fp_status fp_shard_step(const fp_step_args* args, void* stream);
  *                        reduced occupancy, then the copy of the other
  *                        shards in a kernel of its own (then the norm
  *                        finalisation if sq_norm).
+ *   FP_PATH_SPECULATIVE   -- exact skip with separate output state: the
+ *                        kernels of FP_PATH_NO_SKIP writing the outputs,
+ *                        then a kernel that, on overflow only, copies the
+ *                        input state to the outputs and recasts the own
+ *                        shard; the step moves the bytes of the no-skip
+ *                        step plus one small launch.
+ *   FP_PATH_SPECULATIVE_SPLIT -- the same from 2^24 elements on, with the
+ *                        kernels of FP_PATH_NO_SKIP_SPLIT.
  * The one-pass choice depends on the device's co-resident capacity, hence
  * on the device current at the call. */
 #define FP_PATH_ONE_PASS 0
 #define FP_PATH_TWO_PHASE 1
 #define FP_PATH_NO_SKIP 2
 #define FP_PATH_NO_SKIP_SPLIT 3
+#define FP_PATH_SPECULATIVE 4
+#define FP_PATH_SPECULATIVE_SPLIT 5
 fp_status fp_step_path(const fp_step_args* args, int32_t* path);
 
 /* ------------------------------------------------------------------ units */

@@ -21,13 +21,15 @@ from typing import Optional, Sequence
 
 from . import _lib
 from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_NO_SKIP_SPLIT, FP_PATH_ONE_PASS,  # noqa: F401
+                   FP_PATH_SPECULATIVE, FP_PATH_SPECULATIVE_SPLIT,
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FlatParamError, check, lib)
 
 __all__ = ["Plan", "Units", "Shard0Plan", "ReshardPlan", "reduce_shard_hybrid", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
-           "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "FP_PATH_NO_SKIP_SPLIT", "library_path"]
+           "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "FP_PATH_NO_SKIP_SPLIT", "FP_PATH_SPECULATIVE",
+           "FP_PATH_SPECULATIVE_SPLIT", "library_path"]
 
 
 def library_path() -> str:
@@ -494,12 +496,12 @@ def unshard(shards, full):
 def shard_step(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *, scale: float,
                lr, beta1, beta2, eps, weight_decay, step: int, found_inf, accumulate: bool = False,
                sq_norm=None, workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None,
-               grad_coef=None):
+               grad_coef=None, out=None):
     """Reduce (last micro-batch) + AdamW + bf16 cast + unshard for this rank."""
     ShardStep(grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank, scale=scale, lr=lr,
               beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay, found_inf=found_inf,
               accumulate=accumulate, sq_norm=sq_norm, workspace=workspace,
-              flags=flags, grad_coef=grad_coef)(step, profile_events)
+              flags=flags, grad_coef=grad_coef, out=out)(step, profile_events)
 
 
 class ShardStep:
@@ -509,14 +511,22 @@ class ShardStep:
     each call only sets the step count (and the optional profile events)
     and makes one library call on the current stream of master's device.
     The caller keeps the tensors alive and unchanged in size.
+
+    out: None (the state is updated in place) or (master_out, exp_avg_out,
+    exp_avg_sq_out), three fp32 buffers of the shard's size that receive
+    the new state while master / exp_avg / exp_avg_sq are only read (the
+    speculative step; the caller alternates two ShardStep objects whose
+    input and output buffers are swapped).
     """
 
     def __init__(self, grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *,
                  scale: float, lr, beta1, beta2, eps, weight_decay, found_inf,
                  accumulate: bool = False, sq_norm=None, workspace=None,
-                 flags: int = FP_STEP_EXACT_SKIP, grad_coef=None):
+                 flags: int = FP_STEP_EXACT_SKIP, grad_coef=None, out=None):
         _one_device(grads, acc, master, exp_avg, exp_avg_sq, shards, full, found_inf, sq_norm, workspace,
-                    grad_coef)
+                    grad_coef, out)
+        if out is not None and len(out) != 3:
+            raise ValueError("out is (master_out, exp_avg_out, exp_avg_sq_out)")
         torch = _torch()
         S = master.numel()
         gptr = _rank_ptrs(grads, S, "grads")
@@ -540,6 +550,10 @@ class ShardStep:
                        if workspace is not None else None)
         a.flags = int(flags)
         a.grad_coef = _coef_ptr(grad_coef)
+        if out is not None:
+            a.master_out = _f32(out[0], S, "master_out")
+            a.exp_avg_out = _f32(out[1], S, "exp_avg_out")
+            a.exp_avg_sq_out = _f32(out[2], S, "exp_avg_sq_out")
         self._args = a
         self._device = master.device
         self._fn = lib().fp_shard_step
@@ -558,8 +572,7 @@ class ShardStep:
         check(self._fn(C.byref(a), _stream(self._device)))
 
     def path(self) -> int:
-        """FP_PATH_ONE_PASS, FP_PATH_TWO_PHASE, FP_PATH_NO_SKIP or FP_PATH_NO_SKIP_SPLIT: the kernels
-        a call launches on this device."""
+        """One of the FP_PATH_* values: the kernels a call launches on this device."""
         torch = _torch()
         out = C.c_int32(-1)
         with torch.cuda.device(self._device):

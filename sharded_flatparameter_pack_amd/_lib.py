@@ -28,6 +28,8 @@ FP_PATH_ONE_PASS = 0
 FP_PATH_TWO_PHASE = 1
 FP_PATH_NO_SKIP = 2
 FP_PATH_NO_SKIP_SPLIT = 3
+FP_PATH_SPECULATIVE = 4
+FP_PATH_SPECULATIVE_SPLIT = 5
 FP_WORKSPACE_TIMEOUTS_OFFSET = 8320
 
 _i32, _i64, _f32, _f64, _vp = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p
@@ -48,7 +50,8 @@ class fp_step_args(C.Structure):
                 ("scale", _f32), ("accumulate", _i32), ("acc", _vp), ("master", _vp),
                 ("exp_avg", _vp), ("exp_avg_sq", _vp), ("hp", fp_adamw_hparams),
                 ("shards", _vp), ("full", _vp), ("found_inf", _vp), ("sq_norm", _vp),
-                ("workspace", _vp), ("flags", _i32), ("profile_events", _vp), ("grad_coef", _vp)]
+                ("workspace", _vp), ("flags", _i32), ("profile_events", _vp), ("grad_coef", _vp),
+                ("master_out", _vp), ("exp_avg_out", _vp), ("exp_avg_sq_out", _vp)]
 
 
 class fp_units_step_args(C.Structure):

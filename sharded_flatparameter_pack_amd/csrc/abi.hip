@@ -671,16 +671,24 @@ fp_status check_step(const fp_step_args& x, AdamCoef* c) {
         if (x.workspace == nullptr) return fail(FP_ERR_INVALID, "sq_norm needs a workspace");
     }
     if (x.grad_coef != nullptr && !aligned(x.grad_coef, 8)) return fail(FP_ERR_ALIGN, "grad_coef misaligned");
+    const int n_out = (x.master_out != nullptr) + (x.exp_avg_out != nullptr) + (x.exp_avg_sq_out != nullptr);
+    if (n_out != 0 && n_out != 3)
+        return fail(FP_ERR_INVALID, "master_out / exp_avg_out / exp_avg_sq_out: give all three or none");
+    if (n_out == 3 && ((st = check_f32(x.master_out, S, "master_out")) != FP_OK ||
+                       (st = check_f32(x.exp_avg_out, S, "exp_avg_out")) != FP_OK ||
+                       (st = check_f32(x.exp_avg_sq_out, S, "exp_avg_sq_out")) != FP_OK))
+        return st;
     const int64_t b4 = S * 4, b2 = S * 2, bf = S * x.world * 2;
-    const void* f32s[4] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = i + 1; j < 4; ++j)
+    const void* f32s[7] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq, x.master_out, x.exp_avg_out, x.exp_avg_sq_out};
+    const int n_f32 = 4 + n_out;
+    for (int i = 0; i < n_f32; ++i) {
+        for (int j = i + 1; j < n_f32; ++j)
             if (overlap(f32s[i], b4, f32s[j], b4)) return fail(FP_ERR_INVALID, "fp32 buffers overlap");
         if (overlap(f32s[i], b4, x.full, bf)) return fail(FP_ERR_INVALID, "an fp32 buffer overlaps full");
     }
     for (int32_t q = 0; q < x.world; ++q) {
         if (overlap(x.grads[q], b2, x.full, bf)) return fail(FP_ERR_INVALID, "grads[%d] overlaps full", q);
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < n_f32; ++i)
             if (overlap(x.grads[q], b2, f32s[i], b4)) return fail(FP_ERR_INVALID, "grads[%d] overlaps state", q);
         if (q != x.rank && overlap(x.shards[q], b2, x.full, bf))
             return fail(FP_ERR_INVALID, "shards[%d] overlaps full", q);
@@ -695,6 +703,10 @@ fp_status step_path(const fp_step_args& x, int32_t* path, int* variant, int* gri
     *grid = 0;
     if (x.flags & FP_STEP_NO_SKIP) {
         *path = x.shard >= kSplitElems ? FP_PATH_NO_SKIP_SPLIT : FP_PATH_NO_SKIP;
+        return FP_OK;
+    }
+    if (x.master_out != nullptr) {
+        *path = x.shard >= kSplitElems ? FP_PATH_SPECULATIVE_SPLIT : FP_PATH_SPECULATIVE;
         return FP_OK;
     }
     if (x.workspace != nullptr && !(x.flags & FP_STEP_NO_COOP)) {
@@ -728,8 +740,11 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     int variant = -1, grid = 0;
     if ((st = step_path(x, &path, &variant, &grid)) != FP_OK) return st;
 
-    const bool no_skip = path == FP_PATH_NO_SKIP || path == FP_PATH_NO_SKIP_SPLIT;
-    const bool split = path == FP_PATH_NO_SKIP_SPLIT;
+    const bool speculative = path == FP_PATH_SPECULATIVE || path == FP_PATH_SPECULATIVE_SPLIT;
+    // the fused launch(es) without a gate: no-skip, and speculative (gate after)
+    const bool no_skip = path == FP_PATH_NO_SKIP || path == FP_PATH_NO_SKIP_SPLIT || speculative;
+    const bool split = path == FP_PATH_NO_SKIP_SPLIT || path == FP_PATH_SPECULATIVE_SPLIT;
+    const bool out_of_place = x.master_out != nullptr;
     for (int32_t q = 0; q < x.world; ++q) {
         a.grads[q] = x.grads[q];
         a.shards[q] = q == x.rank ? nullptr : x.shards[q];
@@ -750,6 +765,9 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     a.accumulate = x.accumulate ? 1 : 0;
     a.keep_grad = (x.flags & FP_STEP_KEEP_GRAD) ? 1 : 0;
     a.sync = x.workspace != nullptr ? static_cast<GridSync*>(x.workspace) : nullptr;
+    a.master_out = out_of_place ? x.master_out : x.master;
+    a.exp_avg_out = out_of_place ? x.exp_avg_out : x.exp_avg;
+    a.exp_avg_sq_out = out_of_place ? x.exp_avg_sq_out : x.exp_avg_sq;
 
     uint16_t* own = x.full + (int64_t)x.rank * S;
     bool aligned = is_aligned8(own), copy_aligned = true;
@@ -814,6 +832,21 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
         if (x.sq_norm != nullptr &&
             (e = launch_norm_finalize(a.partials, (int)reduce_groups, x.sq_norm, s)) != hipSuccess)
             return device_fail(e, "norm launch");
+        if (speculative && S > 0) {
+            // the skip rule, applied after the update: restore on overflow
+            ResolveArgs r;
+            std::memset(&r, 0, sizeof r);
+            r.found_inf = x.found_inf;
+            r.master = x.master;
+            r.exp_avg = x.exp_avg;
+            r.exp_avg_sq = x.exp_avg_sq;
+            r.master_out = x.master_out;
+            r.exp_avg_out = x.exp_avg_out;
+            r.exp_avg_sq_out = x.exp_avg_sq_out;
+            r.own = own;
+            r.shard = S;
+            if ((e = launch_step_resolve(r, s)) != hipSuccess) return device_fail(e, "resolve launch");
+        }
     } else {
         if ((e = launch_adamw(d, stream_grid(S), is_aligned8(own), s)) != hipSuccess)
             return device_fail(e, "adamw launch");

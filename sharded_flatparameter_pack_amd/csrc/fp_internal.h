@@ -181,6 +181,25 @@ struct StepArgs {
     int32_t reduce_groups;   // workgroups of the reduce role (barrier members in one pass)
     int32_t copy_tiles;      // copy tiles per shard
     GridSync* sync;          // one-pass: barrier state in the workspace
+    // Where the fused update stores the state: separate buffers for the
+    // speculative step, else master / exp_avg / exp_avg_sq themselves.
+    float* master_out;
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
+};
+
+// The speculative step's last kernel: if *found_inf is set, the output state
+// takes the input state and own (the rank's slice of full) its bf16 cast.
+struct ResolveArgs {
+    const int32_t* found_inf;
+    const float* master;
+    const float* exp_avg;
+    const float* exp_avg_sq;
+    float* master_out;
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
+    uint16_t* own;
+    int64_t shard;
 };
 
 // One unit of a multi-unit launch: a device record of kUnitHeader bytes
@@ -261,6 +280,7 @@ hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update
 hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
 hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, bool copy_aligned,
                             hipStream_t s);
+hipError_t launch_step_resolve(const ResolveArgs& r, hipStream_t s);
 // Multi-unit launches: one micro-batch's reduce over all units; the last
 // micro-batch's reduce (+ AdamW when fused) with the copies of all units'
 // other shards (copy_groups workgroups after the reduce tiles); AdamW over

@@ -53,6 +53,26 @@ __global__ __launch_bounds__(kThreads) void step_phase1_kernel(const StepArgs a)
                                        a.partials != nullptr ? a.partials + blockIdx.x : nullptr);
 }
 
+// Last kernel of the speculative exact-skip step.  The fused pass before it
+// stored the updated state to separate output buffers without waiting for
+// the overflow check; the skip rule is applied here instead: if the flag
+// (the OR over the step's micro-batches) is set, the outputs receive the
+// unchanged input state and the rank's slice of full the bf16 cast of the
+// unchanged master, as a skipped step leaves them.  Without overflow, the
+// common case, every workgroup reads the flag and returns.  The copy is a
+// plain grid-stride loop: it only runs on a skipped step.
+__global__ __launch_bounds__(kThreads) void step_resolve_kernel(const ResolveArgs r) {
+    if (*r.found_inf == 0) return;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < r.shard; j += stride) {
+        const float th = r.master[j];
+        r.master_out[j] = th;
+        r.exp_avg_out[j] = r.exp_avg[j];
+        r.exp_avg_sq_out[j] = r.exp_avg_sq[j];
+        r.own[j] = (uint16_t)bf16x2(th, 0.0f);
+    }
+}
+
 // One-pass exact-skip step.  Workgroups [0, reduce_groups) take part in a
 // grid barrier and must be resident together (the grid is sized for it);
 // each of their lanes loads, for its kQ quads, the fp32 master / moments and
@@ -193,6 +213,15 @@ hipError_t launch_reduce(const ReduceArgs& a, int64_t grid, bool aligned, hipStr
 
 hipError_t launch_norm_finalize(const double* partials, int n, double* out, hipStream_t s) {
     norm_finalize_kernel<<<1, kThreads, 0, s>>>(partials, n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_resolve(const ResolveArgs& r, hipStream_t s) {
+    constexpr int64_t kMaxResolveGroups = 2048;
+    int64_t grid = (r.shard + kThreads - 1) / kThreads;
+    if (grid > kMaxResolveGroups) grid = kMaxResolveGroups;
+    if (grid < 1) grid = 1;
+    step_resolve_kernel<<<(unsigned)grid, kThreads, 0, s>>>(r);
     return hipGetLastError();
 }
 

@@ -295,18 +295,35 @@ __device__ __forceinline__ void store_quads(const A& a, const Quads<kU>& Q, bool
     }
 }
 
-template <class A>
-__device__ __forceinline__ void update_elem(const A& a, const AdamCoef& c, int64_t j, float y, bool skip,
-                                            uint16_t* out) {
+// One element: the state read through `a`, stored through `o`.
+template <class A, class O>
+__device__ __forceinline__ void update_elem(const A& a, const O& o, const AdamCoef& c, int64_t j, float y,
+                                            bool skip, uint16_t* out) {
     float th = a.master[j];
     if (!skip) {
         float m = a.exp_avg[j], v = a.exp_avg_sq[j];
         adamw_elem(c, y, th, m, v);
-        a.master[j] = th;
-        a.exp_avg[j] = m;
-        a.exp_avg_sq[j] = v;
+        o.master[j] = th;
+        o.exp_avg[j] = m;
+        o.exp_avg_sq[j] = v;
     }
     if (out != nullptr) out[j] = (uint16_t)bf16x2(th, 0.0f);
+}
+
+// The buffers a fused update stores the state to: the step's output buffers
+// (the speculative step's separate ones, else its inputs); other views
+// update in place.
+struct StateOut {
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+};
+template <class A>
+__device__ __forceinline__ StateOut state_out(const A& a) {
+    return {a.master, a.exp_avg, a.exp_avg_sq};
+}
+__device__ __forceinline__ StateOut state_out(const StepArgs& a) {
+    return {a.master_out, a.exp_avg_out, a.exp_avg_sq_out};
 }
 
 // ---------------------------------------------------------------- unshard
@@ -527,7 +544,7 @@ __device__ __forceinline__ void adamw_tile(const A& a, const float* grad, int64_
     if (tile == 0 && (int64_t)threadIdx.x < a.shard - tail0) {
         const int64_t j = tail0 + threadIdx.x;
         const bool skip = found_inf != nullptr && *found_inf != 0;
-        update_elem(a, c, j, skip ? 0.0f : grad[j], skip, out);
+        update_elem(a, a, c, j, skip ? 0.0f : grad[j], skip, out);
     }
 }
 
@@ -547,7 +564,8 @@ __device__ __forceinline__ void copy_role(const A& a, unsigned idx) {
 // Reduce tile of the last micro-batch in a step: kFused = false writes the
 // reduced gradient to acc for the AdamW kernel that follows once the
 // overflow flag of the whole step is known; kFused = true also runs AdamW
-// and the cast to `own` in the same pass (no gate).  keep_grad: with
+// and the cast to `own` in the same pass (no gate), the new state stored to
+// state_out(a).  keep_grad: with
 // kFused, also leave the reduced gradient in acc.
 template <bool kAligned, bool kFused, int kG, class A>
 __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool accumulate,
@@ -573,7 +591,7 @@ __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool 
         }
         if (kFused) {
             adamw_quads<kU>(c, y, st);
-            store_quads<kAligned, kU>(a, Q, false, st, own);
+            store_quads<kAligned, kU>(state_out(a), Q, false, st, own);
         }
     }
     const int64_t tail0 = nq << 2;
@@ -583,7 +601,7 @@ __device__ __forceinline__ void step_reduce_tile(const A& a, int64_t tile, bool 
         bad |= !finite_f32(y);
         if (want_sq) sq += (double)y * (double)y;
         if (!kFused || keep_grad) a.acc[j] = y;
-        if (kFused) update_elem(a, c, j, y, false, own);
+        if (kFused) update_elem(a, state_out(a), c, j, y, false, own);
     }
     flag_if_any(bad, found_inf);
     if (want_sq) {

@@ -53,7 +53,9 @@ def test_struct_layouts_match_the_header(fp):
     assert _lib.fp_step_args.hp.offset == 64
     assert _lib.fp_step_args.flags.offset == 152
     assert _lib.fp_step_args.grad_coef.offset == 64 + 48 + 5 * 8 + 8 + 8
-    assert C.sizeof(_lib.fp_step_args) == 64 + 48 + 5 * 8 + 8 + 8 + 8
+    assert _lib.fp_step_args.master_out.offset == 64 + 48 + 5 * 8 + 8 + 8 + 8
+    assert _lib.fp_step_args.exp_avg_sq_out.offset == 64 + 48 + 5 * 8 + 8 + 8 + 8 + 16
+    assert C.sizeof(_lib.fp_step_args) == 64 + 48 + 5 * 8 + 8 + 8 + 8 + 24
 
 
 def _random_shapes(r):
@@ -283,6 +285,46 @@ def test_step_path_without_a_device(fp):
         a.flags = _lib.FP_STEP_EXACT_SKIP
         assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
         assert path.value == _lib.FP_PATH_TWO_PHASE
+
+
+def test_speculative_step_path_and_checks(fp):
+    """With output state buffers, the exact-skip step takes the speculative
+    paths (split from 2^24 elements on) and the no-skip step writes the
+    outputs; the output buffers come as all three or none, and may overlap
+    no other buffer of the call."""
+    from sharded_flatparameter_pack_amd import _lib
+    L = fp.lib()
+    step = 1 << 40
+    grads = (C.c_void_p * 2)(step, 2 * step)
+    shards = (C.c_void_p * 2)(None, 3 * step)
+    a = _lib.fp_step_args()
+    a.world, a.rank, a.scale = 2, 0, 0.5
+    a.grads, a.shards = C.cast(grads, C.c_void_p), C.cast(shards, C.c_void_p)
+    a.acc, a.master, a.exp_avg, a.exp_avg_sq = 4 * step, 5 * step, 6 * step, 7 * step
+    a.hp = _lib.fp_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    a.full, a.found_inf, a.workspace = 8 * step, 9 * step, 10 * step
+    a.master_out, a.exp_avg_out, a.exp_avg_sq_out = 11 * step, 12 * step, 13 * step
+    path = C.c_int32(-1)
+    for S, spec, nsk in ((1 << 24, _lib.FP_PATH_SPECULATIVE_SPLIT, _lib.FP_PATH_NO_SKIP_SPLIT),
+                         ((1 << 24) - 1, _lib.FP_PATH_SPECULATIVE, _lib.FP_PATH_NO_SKIP),
+                         (5, _lib.FP_PATH_SPECULATIVE, _lib.FP_PATH_NO_SKIP)):
+        a.shard = S
+        for flags, want in ((_lib.FP_STEP_EXACT_SKIP, spec), (_lib.FP_STEP_NO_COOP, spec),
+                            (_lib.FP_STEP_KEEP_GRAD, spec), (_lib.FP_STEP_NO_SKIP, nsk)):
+            a.flags = flags
+            assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
+            assert path.value == want, (S, flags)
+    a.flags = _lib.FP_STEP_EXACT_SKIP
+    a.exp_avg_out = None                       # two of three
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -1
+    a.exp_avg_out = 12 * step + 2              # misaligned
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -3
+    for alias in (5 * step + 16, 4 * step, 11 * step + 16, 8 * step, step):
+        a.exp_avg_out = alias                  # overlaps master, acc, master_out, full, a gradient row
+        assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -1, hex(alias)
+        assert _status(L.fp_shard_step, C.byref(a), None) == -1
+    a.exp_avg_out = 12 * step
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
 
 
 def test_units_validation_without_a_device(fp):
