@@ -1,7 +1,7 @@
 """Throughput of one rank's shard step (reduce + AdamW + bf16 cast + unshard).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--mode exact|twophase|noskip] [--eager]
+                    [--mode exact|twophase|noskip|speculative] [--eager]
 
 A step is the whole per-step hot path for rank r's shard: the fixed-order
 reduce of the N_d ranks' bf16 gradients for every micro-batch, the AdamW
@@ -47,7 +47,10 @@ KERNEL_SOURCES = ["sharded_flatparameter_pack_amd/csrc/step_kernels.hip",
                   "sharded_flatparameter_pack_amd/csrc/step_ops.h",
                   "sharded_flatparameter_pack_amd/csrc/fp_device.h",
                   "sharded_flatparameter_pack_amd/csrc/fp_internal.h"]
-MODE_FLAGS = {"exact": "FP_STEP_EXACT_SKIP", "twophase": "FP_STEP_NO_COOP", "noskip": "FP_STEP_NO_SKIP"}
+MODE_FLAGS = {"exact": "FP_STEP_EXACT_SKIP", "twophase": "FP_STEP_NO_COOP", "noskip": "FP_STEP_NO_SKIP",
+              "speculative": "FP_STEP_EXACT_SKIP"}
+# modes that give the step separate output state buffers (single-unit workloads only)
+OUT_OF_PLACE_MODES = {"speculative"}
 
 
 def step_bytes_per_elem(world: int, n_micro: int) -> int:
@@ -107,11 +110,14 @@ def row_stride(S: int) -> int:
 class SingleUnit:
     """Buffer sets of one rank's step on one unit (fp_shard_step)."""
 
-    def __init__(self, cfg, rank, dev, flags):
+    supports_out_of_place = True
+
+    def __init__(self, cfg, rank, dev, flags, out_of_place=False):
         import torch
         import sharded_flatparameter_pack_amd as fp
         from workloads import gen
         self.cfg, self.rank, self.world, self.n_micro = cfg, rank, cfg.world, cfg.n_micro
+        self.dev = dev
         self.S = S = -(-cfg.units()[0] // cfg.world)
         world = self.world
         per_set = S * (2 * world + 16 + 2 * (world - 1) + 2 * world)
@@ -132,37 +138,57 @@ class SingleUnit:
                      found_inf=torch.zeros(1, dtype=torch.int32, device=dev),
                      workspace=fp.new_workspace(dev, S))
             self.sets.append(s)
-        self.set_flags(flags)
+        self.set_flags(flags, out_of_place)
 
-    def set_flags(self, flags):
+    def set_flags(self, flags, out_of_place=False):
+        """Calls of every set with these flags.  out_of_place: each set also
+        gets output state buffers; the step alternates two calls whose input
+        and output buffers are swapped (a graph of one step per set replays
+        the first of them, which moves the same bytes)."""
+        import torch
         import sharded_flatparameter_pack_amd as fp
         hp, world = self.cfg.hp, self.world
-        self.calls = [fp.ShardStep(s["grads"], s["acc"], s["master"], s["exp_avg"], s["exp_avg_sq"],
-                                   s["shards"], s["full"], self.rank, scale=1.0 / world, lr=hp.lr,
-                                   beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
-                                   weight_decay=hp.weight_decay, found_inf=s["found_inf"],
-                                   workspace=s["workspace"], flags=flags)
-                      for s in self.sets]
-        self.path = self.calls[0].path()
+
+        def call(s, state, out):
+            return fp.ShardStep(s["grads"], s["acc"], *state, s["shards"], s["full"], self.rank,
+                                scale=1.0 / world, lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
+                                weight_decay=hp.weight_decay, found_inf=s["found_inf"],
+                                workspace=s["workspace"], flags=flags, out=out)
+
+        self.calls = []
+        for s in self.sets:
+            state = [s["master"], s["exp_avg"], s["exp_avg_sq"]]
+            if not out_of_place:
+                s.pop("out", None)
+                self.calls.append([call(s, state, None)])
+                continue
+            if "out" not in s:
+                s["out"] = [torch.zeros(self.S, dtype=torch.float32, device=self.dev) for _ in range(3)]
+            self.calls.append([call(s, state, s["out"]), call(s, s["out"], state)])
+        self.path = self.calls[0][0].path()
 
     def n_events(self):
         return 3
 
     def step(self, i, events=None):
-        self.calls[i % self.n_sets](i // self.n_sets + 1, events)
+        calls = self.calls[i % self.n_sets]
+        k = i // self.n_sets
+        calls[k % len(calls)](k + 1, events)
 
     def kernels(self, step_ms, ev_ms):
         """(name, rocprof id, ms per launch, algorithmic bytes per launch, launches per step)."""
         import sharded_flatparameter_pack_amd as fp
         S, N = self.S, self.world
         B = step_bytes_per_elem(N, 1)
-        if self.path == fp.FP_PATH_NO_SKIP:
+        if self.path in (fp.FP_PATH_NO_SKIP, fp.FP_PATH_SPECULATIVE):
+            # (the speculative step's restore kernel returns at once without overflow)
             return [("step_phase1_kernel<true>", "step_phase1_fused", step_ms, S * B, 1)]
         if self.path == fp.FP_PATH_ONE_PASS:
             return [("step_coop_kernel", "step_coop", step_ms, S * B, 1)]
         k1, k2 = ev_ms[1] - ev_ms[0], ev_ms[2] - ev_ms[1]
         f1 = k1 / (k1 + k2)
-        if self.path == fp.FP_PATH_NO_SKIP_SPLIT:      # fused reduce + AdamW + cast, then the copies
+        if self.path in (fp.FP_PATH_NO_SKIP_SPLIT, fp.FP_PATH_SPECULATIVE_SPLIT):
+            # fused reduce + AdamW + cast, then the copies
             return [("step_phase1_kernel<true>", "step_phase1_fused", step_ms * f1, S * (B - 4 * (N - 1)), 1),
                     ("unshard_kernel", "unshard", step_ms * (1 - f1), S * 4 * (N - 1), 1)]
         return [("step_phase1_kernel<false>", "step_phase1", step_ms * f1, S * (2 * N + 4 * (N - 1)), 1),
@@ -181,11 +207,14 @@ class Bucketed:
     """Buffer sets of one rank's step on all buckets of a bucketed model: one
     multi-unit reduce launch per earlier micro-batch, then fp_units_step."""
 
-    def __init__(self, cfg, rank, dev, flags):
+    supports_out_of_place = True
+
+    def __init__(self, cfg, rank, dev, flags, out_of_place=False):
         import torch
         import sharded_flatparameter_pack_amd as fp
         from workloads import gen
         self.cfg, self.rank, self.world, self.n_micro = cfg, rank, cfg.world, cfg.n_micro
+        self.dev = dev
         N, n = cfg.world, cfg.n_micro
         sizes = [-(-T // N) for T in cfg.units()]
         self.sizes = sizes
@@ -270,11 +299,13 @@ class Bucketed:
         return None
 
 
-def make_workload(cfg, rank, dev, flags):
+def make_workload(cfg, rank, dev, flags, out_of_place=False):
     if cfg.shapes is None:
+        if out_of_place:
+            raise ValueError("the multi-unit step updates its state in place")
         return Bucketed(cfg, rank, dev, flags)
     if cfg.n_micro == 1:
-        return SingleUnit(cfg, rank, dev, flags)
+        return SingleUnit(cfg, rank, dev, flags, out_of_place)
     raise ValueError("single-unit workloads with several micro-batches are not benchmarked")
 
 
@@ -628,7 +659,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="c2_layer_d1024_nd8")
     ap.add_argument("--mode", choices=list(MODE_FLAGS), default="exact",
                     help="exact: exact overflow skip (one-pass kernel when the shard fits); "
-                         "twophase: exact skip with two kernels; noskip: one pass, no gate")
+                         "twophase: exact skip with two kernels; noskip: one pass, no gate; "
+                         "speculative: exact skip with separate output state buffers (the no-skip "
+                         "pass, then a restore kernel that acts only on overflow)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python with per-kernel events (launch-bound for "
                          "small shards) instead of replaying a captured HIP graph")
@@ -694,9 +727,10 @@ def main(argv=None) -> int:
     B = step_bytes_per_elem(world, n)
     ev = HipEvents()
     path_names = {fp.FP_PATH_ONE_PASS: "one-pass", fp.FP_PATH_TWO_PHASE: "two-phase",
-                  fp.FP_PATH_NO_SKIP: "fused-no-skip", fp.FP_PATH_NO_SKIP_SPLIT: "fused-no-skip-split"}
+                  fp.FP_PATH_NO_SKIP: "fused-no-skip", fp.FP_PATH_NO_SKIP_SPLIT: "fused-no-skip-split",
+                  fp.FP_PATH_SPECULATIVE: "speculative", fp.FP_PATH_SPECULATIVE_SPLIT: "speculative-split"}
 
-    w = make_workload(cfg, rank, dev, getattr(fp, MODE_FLAGS[args.mode]))
+    w = make_workload(cfg, rank, dev, getattr(fp, MODE_FLAGS[args.mode]), args.mode in OUT_OF_PLACE_MODES)
     S = w.S
     time_steps.spread = None
     step_ms, ev_ms, K, timing = time_steps(w, args.steps, args.warmup, args.eager, ev)
@@ -732,7 +766,9 @@ def main(argv=None) -> int:
         for mode in MODE_FLAGS:
             if mode == args.mode:
                 continue
-            w.set_flags(getattr(fp, MODE_FLAGS[mode]))
+            if mode in OUT_OF_PLACE_MODES and not getattr(w, "supports_out_of_place", False):
+                continue
+            w.set_flags(getattr(fp, MODE_FLAGS[mode]), mode in OUT_OF_PLACE_MODES)
             ms = time_steps(w, min(args.steps, 400), min(args.warmup, 20), args.eager, ev)[0]
             modes[mode] = {"path": path_names[w.path], "ms_per_step": round(ms, 5),
                            "GBps": round(S * B / (ms * 1e-3) / 1e9, 2),
