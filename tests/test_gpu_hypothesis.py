@@ -9,7 +9,7 @@ GPU must match the oracle on each.
   subnormals, the largest finite values, +-inf, NaN) mixed with normals,
   one or two micro-batches: bitwise, non-finite values by class;
 * the shard step on the same kind of inputs (finite gradients whose sum may
-  still overflow fp32), every path.
+  still overflow fp32), every path, in place or with separate output state.
 Examples are derandomised (a fixed sequence per test) so that a failure
 repeats; no example database is written.
 """
@@ -106,8 +106,8 @@ def test_reduce_matches_oracle(fp, world, S, offset, micro, frac, seed):
 @SETTINGS
 @given(world=st.sampled_from([1, 2, 3, 8, 16]), S=st.integers(1, 5000), rank_frac=st.floats(0, 0.999),
        flags=st.sampled_from([0, 1, 4]), step=st.integers(1, 5), frac=st.sampled_from([0.0, 0.2]),
-       seed=st.integers(0, 2 ** 31 - 1))
-def test_step_matches_oracle(fp, world, S, rank_frac, flags, step, frac, seed):
+       out_of_place=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_step_matches_oracle(fp, world, S, rank_frac, flags, step, frac, out_of_place, seed):
     r = np.random.default_rng(seed)
     rank = int(rank_frac * world)
     rows = _grads(r, world, S, FINITE_SPECIALS, frac)
@@ -129,11 +129,17 @@ def test_step_matches_oracle(fp, world, S, rank_frac, flags, step, frac, seed):
     flag = torch.zeros(1, dtype=torch.int32, device=dev())
     ws = fp.new_workspace(dev(), S)
     shards = [None if q == rank else to_dev(others[q]) for q in range(world)]
+    outs = [torch.full((S,), 9.0, dtype=torch.float32, device=dev()) for _ in range(3)] if out_of_place else None
     fp.shard_step(_rows_at(rows, 0), acc, d_th, d_m, d_v, shards, full, rank, scale=1.0 / world, step=step,
-                  found_inf=flag, workspace=ws, flags=flags, **hp_kwargs(HP))
+                  found_inf=flag, workspace=ws, flags=flags, out=outs, **hp_kwargs(HP))
     torch.cuda.synchronize()
     assert int(flag.item()) == flag_o
-    for name, got, want in (("master", d_th, th_o), ("exp_avg", d_m, m_o), ("exp_avg_sq", d_v, v_o)):
+    res = (d_th, d_m, d_v)
+    if out_of_place:
+        for name, got, x in zip(("master", "exp_avg", "exp_avg_sq"), res, (th, m0, v0)):
+            assert_f32_bitexact(to_host(got), x, f"input {name} unchanged")
+        res = outs
+    for name, got, want in zip(("master", "exp_avg", "exp_avg_sq"), res, (th_o, m_o, v_o)):
         if flag_o and not flags & fp.FP_STEP_NO_SKIP:
             assert_f32_bitexact(to_host(got), want, f"{name} untouched on overflow")
         else:
