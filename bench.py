@@ -1,7 +1,7 @@
 """Throughput of one rank's shard step (reduce + AdamW + bf16 cast + unshard).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--mode exact|twophase|noskip|speculative] [--eager]
+                    [--mode speculative|exact|twophase|noskip] [--timing auto|graph|eager]
 
 A step is the whole per-step hot path for rank r's shard: the fixed-order
 reduce of the N_d ranks' bf16 gradients for every micro-batch, the AdamW
@@ -12,15 +12,22 @@ workload runs the multi-unit entry points, one launch per micro-batch over
 all buckets.  Pack and views are one-time set-up per unit and are not part
 of a step; pack throughput is reported on its own.
 
+With no flags the line is the d=12288 layer unit (226.5M-element shard,
+N_d = 8, the largest workload that is one unit on one GPU) with the exact
+overflow skip in its speculative form (separate output state, swapped each
+step); `configs` carries the 10k-tensor group at 64 ranks and the bucketed
+611M model the same way.
+
 All inputs are synthetic and resident in HBM before timing starts.  The
 step rotates over enough buffer sets (>= 1.5 GB) that no step finds its
 data in the 256 MB Infinity Cache left behind by the previous ones.
+Exactly K steps are timed.
 
 Output: one JSON line.  `value` is algorithmic GB/s of the whole step,
 B = 2*N*n + 8*(n-1) + 24 + 2 + 4*(N-1) bytes per shard element; `roofline`
-times the dominant kernel with HIP events recorded around it on the
-library's stream inside the timed region; `cpu_baseline` times the serial
-CPU oracle on a bounded sample of the same workload on one host core.
+takes the dominant kernel's average duration from HIP events that the
+library records around its kernels on its stream; `cpu_baseline` times the
+serial CPU oracle on a bounded sample of the same workload on one host core.
 """
 
 from __future__ import annotations
@@ -47,10 +54,13 @@ KERNEL_SOURCES = ["sharded_flatparameter_pack_amd/csrc/step_kernels.hip",
                   "sharded_flatparameter_pack_amd/csrc/step_ops.h",
                   "sharded_flatparameter_pack_amd/csrc/fp_device.h",
                   "sharded_flatparameter_pack_amd/csrc/fp_internal.h"]
-MODE_FLAGS = {"exact": "FP_STEP_EXACT_SKIP", "twophase": "FP_STEP_NO_COOP", "noskip": "FP_STEP_NO_SKIP",
-              "speculative": "FP_STEP_EXACT_SKIP"}
-# modes that give the step separate output state buffers (single-unit workloads only)
+MODE_FLAGS = {"speculative": "FP_STEP_EXACT_SKIP", "exact": "FP_STEP_EXACT_SKIP", "twophase": "FP_STEP_NO_COOP",
+              "noskip": "FP_STEP_NO_SKIP"}
+# modes that give the step separate output state buffers
 OUT_OF_PLACE_MODES = {"speculative"}
+DEFAULT_WORKLOAD = "c4_layer_d12288_nd8"
+SIDE_WORKLOADS = ("c5_ragged10k_nd64", "c3_611m_buckets_nd16")
+EAGER_MIN_MS = 0.2             # auto timing: steps this long are timed eagerly with per-kernel events
 
 
 def step_bytes_per_elem(world: int, n_micro: int) -> int:
@@ -110,9 +120,7 @@ def row_stride(S: int) -> int:
 class SingleUnit:
     """Buffer sets of one rank's step on one unit (fp_shard_step)."""
 
-    supports_out_of_place = True
-
-    def __init__(self, cfg, rank, dev, flags, out_of_place=False):
+    def __init__(self, cfg, rank, dev, flags, out_of_place=False, n_sets=None):
         import torch
         import sharded_flatparameter_pack_amd as fp
         from workloads import gen
@@ -121,7 +129,7 @@ class SingleUnit:
         self.S = S = -(-cfg.units()[0] // cfg.world)
         world = self.world
         per_set = S * (2 * world + 16 + 2 * (world - 1) + 2 * world)
-        self.n_sets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        self.n_sets = n_sets or max(2, math.ceil(ROTATE_BYTES / per_set))
         self.sets = []
         Sp = row_stride(S)
         for k in range(self.n_sets):
@@ -155,6 +163,7 @@ class SingleUnit:
                                 weight_decay=hp.weight_decay, found_inf=s["found_inf"],
                                 workspace=s["workspace"], flags=flags, out=out)
 
+        self.out_of_place = out_of_place
         self.calls = []
         for s in self.sets:
             state = [s["master"], s["exp_avg"], s["exp_avg_sq"]]
@@ -170,29 +179,38 @@ class SingleUnit:
     def n_events(self):
         return 3
 
+    def state_io(self, i):
+        """(input state, output state or None) of step i on its set."""
+        s = self.sets[i % self.n_sets]
+        state = [s["master"], s["exp_avg"], s["exp_avg_sq"]]
+        if not self.out_of_place:
+            return state, None
+        return (state, s["out"]) if (i // self.n_sets) % 2 == 0 else (s["out"], state)
+
     def step(self, i, events=None):
         calls = self.calls[i % self.n_sets]
         k = i // self.n_sets
         calls[k % len(calls)](k + 1, events)
 
-    def kernels(self, step_ms, ev_ms):
-        """(name, rocprof id, ms per launch, algorithmic bytes per launch, launches per step)."""
+    def kernels(self, ev_ms):
+        """(name, rocprof id, ms per launch, algorithmic bytes per launch, launches per step),
+        durations from the mean event offsets of a step (the library's events)."""
         import sharded_flatparameter_pack_amd as fp
         S, N = self.S, self.world
         B = step_bytes_per_elem(N, 1)
-        if self.path in (fp.FP_PATH_NO_SKIP, fp.FP_PATH_SPECULATIVE):
-            # (the speculative step's restore kernel returns at once without overflow)
-            return [("step_phase1_kernel<true>", "step_phase1_fused", step_ms, S * B, 1)]
-        if self.path == fp.FP_PATH_ONE_PASS:
-            return [("step_coop_kernel", "step_coop", step_ms, S * B, 1)]
         k1, k2 = ev_ms[1] - ev_ms[0], ev_ms[2] - ev_ms[1]
-        f1 = k1 / (k1 + k2)
+        if self.path in (fp.FP_PATH_NO_SKIP, fp.FP_PATH_SPECULATIVE):
+            # (the speculative step's restore kernel runs between the second and third
+            # event and returns at once without overflow)
+            return [("step_phase1_kernel<true>", "step_phase1_fused", k1, S * B, 1)]
+        if self.path == fp.FP_PATH_ONE_PASS:
+            return [("step_coop_kernel", "step_coop", k1, S * B, 1)]
         if self.path in (fp.FP_PATH_NO_SKIP_SPLIT, fp.FP_PATH_SPECULATIVE_SPLIT):
-            # fused reduce + AdamW + cast, then the copies
-            return [("step_phase1_kernel<true>", "step_phase1_fused", step_ms * f1, S * (B - 4 * (N - 1)), 1),
-                    ("unshard_kernel", "unshard", step_ms * (1 - f1), S * 4 * (N - 1), 1)]
-        return [("step_phase1_kernel<false>", "step_phase1", step_ms * f1, S * (2 * N + 4 * (N - 1)), 1),
-                ("adamw_kernel", "adamw", step_ms * (1 - f1), S * 26, 1)]
+            # fused reduce + AdamW + cast, then the copies (and the restore kernel)
+            return [("step_phase1_kernel<true>", "step_phase1_fused", k1, S * (B - 4 * (N - 1)), 1),
+                    ("unshard_kernel", "unshard", k2, S * 4 * (N - 1), 1)]
+        return [("step_phase1_kernel<false>", "step_phase1", k1, S * (2 * N + 4 * (N - 1)), 1),
+                ("adamw_kernel", "adamw", k2, S * 26, 1)]
 
     def flagged(self):
         import sharded_flatparameter_pack_amd as fp
@@ -207,9 +225,7 @@ class Bucketed:
     """Buffer sets of one rank's step on all buckets of a bucketed model: one
     multi-unit reduce launch per earlier micro-batch, then fp_units_step."""
 
-    supports_out_of_place = True
-
-    def __init__(self, cfg, rank, dev, flags, out_of_place=False):
+    def __init__(self, cfg, rank, dev, flags, out_of_place=False, n_sets=None):
         import torch
         import sharded_flatparameter_pack_amd as fp
         from workloads import gen
@@ -220,10 +236,11 @@ class Bucketed:
         self.sizes = sizes
         self.S = sum(sizes)
         per_set = self.S * (2 * N * n + 16 + 4 * N)
-        self.n_sets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        self.n_sets = n_sets or max(2, math.ceil(ROTATE_BYTES / per_set))
         offs = [0]
         for S in sizes[:-1]:
             offs.append(offs[-1] + S)
+        self.offsets = offs
         self.sets = []
         for k in range(self.n_sets):
             # rank q's gradient (and shard) rows of bucket b are slices of one
@@ -248,15 +265,37 @@ class Bucketed:
                                   acc=torch.zeros(P, dtype=torch.float32, device=dev),
                                   found_inf=torch.zeros(1, dtype=torch.int32, device=dev)))
         self.ev = HipEvents()
-        self.set_flags(flags)
+        self.set_flags(flags, out_of_place)
 
-    def set_flags(self, flags):
+    def set_flags(self, flags, out_of_place=False):
+        """Flags of the last micro-batch's call; out_of_place: each set also gets
+        output partitions, and successive steps on a set swap input and output
+        (as the single-unit workload does)."""
+        import torch
         import sharded_flatparameter_pack_amd as fp
         self.flags = flags & fp.FP_STEP_NO_SKIP       # the multi-unit step has no one-pass form
-        self.path = fp.FP_PATH_NO_SKIP if self.flags else fp.FP_PATH_TWO_PHASE
+        self.out_of_place = out_of_place
+        for s in self.sets:
+            if not out_of_place:
+                s.pop("out", None)
+            elif "out" not in s:
+                P = s["plans"][0].partition
+                s["out"] = [torch.zeros(P, dtype=torch.float32, device=self.dev) for _ in range(3)]
+        if self.flags:
+            self.path = fp.FP_PATH_NO_SKIP
+        else:
+            self.path = fp.FP_PATH_SPECULATIVE if out_of_place else fp.FP_PATH_TWO_PHASE
 
     def n_events(self):
         return self.n_micro + 2
+
+    def state_io(self, i):
+        """(input state, output state or None) of step i on its set."""
+        s = self.sets[i % self.n_sets]
+        state = [s["master"], s["exp_avg"], s["exp_avg_sq"]]
+        if not self.out_of_place:
+            return state, None
+        return (state, s["out"]) if (i // self.n_sets) % 2 == 0 else (s["out"], state)
 
     def step(self, i, events=None):
         import torch
@@ -268,29 +307,31 @@ class Bucketed:
             if events is not None:
                 self.ev.record(events[m], stream)
             s["plans"][m].reduce(s["acc"], scale=scale, accumulate=m > 0, found_inf=s["found_inf"])
-        s["plans"][n - 1].step(s["acc"], s["master"], s["exp_avg"], s["exp_avg_sq"], scale=scale,
+        state, out = self.state_io(i)
+        s["plans"][n - 1].step(s["acc"], *state, scale=scale,
                                accumulate=n > 1, lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
                                weight_decay=hp.weight_decay, step=i // self.n_sets + 1,
-                               found_inf=s["found_inf"], flags=self.flags,
+                               found_inf=s["found_inf"], flags=self.flags, out=out,
                                profile_events=None if events is None else events[n - 1:n + 2])
 
-    def kernels(self, step_ms, ev_ms):
+    def kernels(self, ev_ms):
         S, N, n = self.S, self.world, self.n_micro
         d = [ev_ms[i + 1] - ev_ms[i] for i in range(n + 1)]
-        tot = sum(d)
         out = []
         acc_in = 4 if n > 1 else 0
         if n > 1:
-            t_red = sum(d[:n - 1]) / tot * step_ms
+            t_red = sum(d[:n - 1])
             alg_red = S * (2 * N * (n - 1) + 4 + 8 * (n - 2))   # the first writes acc, later ones read + write
             out.append(("units_reduce_kernel", "units_reduce", t_red / (n - 1), alg_red / (n - 1), n - 1))
-        if self.flags:
-            out.append(("units_phase1_kernel<true>", "units_phase1_fused", (d[n - 1] + d[n]) / tot * step_ms,
+        if self.flags or self.out_of_place:
+            # fused reduce + AdamW + casts + copies; the restore kernel (speculative)
+            # follows between the last two events and returns at once without overflow
+            out.append(("units_phase1_kernel<true>", "units_phase1_fused", d[n - 1],
                         S * (2 * N + acc_in + 26 + 4 * (N - 1)), 1))
         else:
-            out.append(("units_phase1_kernel<false>", "units_phase1", d[n - 1] / tot * step_ms,
+            out.append(("units_phase1_kernel<false>", "units_phase1", d[n - 1],
                         S * (2 * N + acc_in + 4 * (N - 1)), 1))
-            out.append(("units_adamw_kernel", "units_adamw", d[n] / tot * step_ms, S * 26, 1))
+            out.append(("units_adamw_kernel", "units_adamw", d[n], S * 26, 1))
         return out
 
     def flagged(self):
@@ -299,45 +340,68 @@ class Bucketed:
         return None
 
 
-def make_workload(cfg, rank, dev, flags, out_of_place=False):
+def make_workload(cfg, rank, dev, flags, out_of_place=False, n_sets=None):
     if cfg.shapes is None:
-        if out_of_place:
-            raise ValueError("the multi-unit step updates its state in place")
-        return Bucketed(cfg, rank, dev, flags)
+        return Bucketed(cfg, rank, dev, flags, out_of_place, n_sets)
     if cfg.n_micro == 1:
-        return SingleUnit(cfg, rank, dev, flags, out_of_place)
+        return SingleUnit(cfg, rank, dev, flags, out_of_place, n_sets)
     raise ValueError("single-unit workloads with several micro-batches are not benchmarked")
 
 
 # ------------------------------------------------------------------ timing
-def time_steps(w, K, W, eager, ev):
-    """(step ms, mean event offsets of an eager pass in ms, steps timed, how)."""
+def time_steps(w, K, W, timing, ev):
+    """Time exactly K steps after W warm-up steps.
+
+    Returns (step ms, mean event offsets of a step in ms, how).  timing:
+    "eager" launches every step from Python with the library's per-kernel
+    events recorded inside the timed region; "graph" replays HIP graphs of
+    one step per buffer set (plus a graph of the K mod sets remaining steps),
+    then takes the per-kernel split from an eager pass with events; "auto"
+    picks eager for steps of EAGER_MIN_MS and more (not launch-bound), else
+    graph."""
     import torch
     for i in range(W):
         w.step(i)
     torch.cuda.synchronize()
-
-    def eager_pass(first, count):
-        evs = [[ev.create() for _ in range(w.n_events())] for _ in range(count)]
+    stream = torch.cuda.current_stream().cuda_stream
+    if timing == "auto":
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(2):
+            w.step(W + i)
+        b.record()
         torch.cuda.synchronize()
+        timing = "eager" if a.elapsed_time(b) / 2 >= EAGER_MIN_MS else "graph"
+        W += 2
+
+    def eager_pass(first, count, span=False):
+        evs = [[ev.create() for _ in range(w.n_events())] for _ in range(count)]
+        marks = [ev.create(), ev.create()]
+        torch.cuda.synchronize()
+        ev.record(marks[0], stream)
         for k in range(count):
             w.step(first + k, evs[k])
+        ev.record(marks[1], stream)
         torch.cuda.synchronize()
+        total = ev.elapsed_ms(marks[0], marks[1])
         mean = [0.0] * w.n_events()
         for e in evs:
             for j in range(1, len(e)):
                 mean[j] += ev.elapsed_ms(e[0], e[j]) / count
             for x in e:
                 ev.destroy(x)
-        return mean
+        for x in marks:
+            ev.destroy(x)
+        return total / count, mean
 
-    if eager:
-        ev_ms = eager_pass(W, K)
-        return ev_ms[-1], ev_ms, K, "eager launches from Python; step and kernel times from hipEvents " \
-                                    "recorded around the library's kernels"
+    time_steps.spread = None
+    if timing == "eager":
+        step_ms, ev_ms = eager_pass(W, K)
+        return step_ms, ev_ms, ("eager launches from Python, exactly K steps; step time from hipEvents around "
+                                "the region, per-kernel times from the hipEvents the library records around "
+                                "its kernels on its stream inside the same region")
     n = w.n_sets
-    reps = max(1, -(-K // n))
-    K = reps * n
+    reps, rem = divmod(K, n)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -345,30 +409,53 @@ def time_steps(w, K, W, eager, ev):
             w.step(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(n):
-            w.step(i)
+    graphs = []
+    for count in (n if reps else 0, rem):
+        if count == 0:
+            graphs.append(None)
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                w.step(i)
+        graphs.append(g)
+    main, tail = graphs
     for _ in range(max(1, W // n)):
-        graph.replay()
+        (main or tail).replay()
     torch.cuda.synchronize()
     # an event between replays as well, for the spread over replays (one replay = n steps)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
     marks[0].record()
     for r in range(reps):
-        graph.replay()
+        main.replay()
         marks[r + 1].record()
+    if tail is not None:
+        tail.replay()
+    marks[-1].record()
     torch.cuda.synchronize()
     step_ms = marks[0].elapsed_time(marks[-1]) / K
-    per_replay = sorted(marks[r].elapsed_time(marks[r + 1]) / n for r in range(reps))
-    time_steps.spread = {"median_ms_per_step": round(per_replay[len(per_replay) // 2], 5),
-                         "min_ms_per_step": round(per_replay[0], 5),
-                         "max_ms_per_step": round(per_replay[-1], 5), "replays": reps,
-                         "steps_per_replay": n}
-    del graph
-    ev_ms = eager_pass(W + K, min(K, 200))
-    return step_ms, ev_ms, K, "HIP graph of one step per buffer set, replayed; span timed by hipEvents " \
-                              "on the replay stream; per-kernel split from hipEvents in an eager pass"
+    if reps:
+        per_replay = sorted(marks[r].elapsed_time(marks[r + 1]) / n for r in range(reps))
+        time_steps.spread = {"median_ms_per_step": round(per_replay[len(per_replay) // 2], 5),
+                             "min_ms_per_step": round(per_replay[0], 5),
+                             "max_ms_per_step": round(per_replay[-1], 5), "replays": reps,
+                             "steps_per_replay": n, "tail_steps": rem}
+    del graphs, main, tail
+    _, ev_ms = eager_pass(W + K, min(K, 200))
+    return step_ms, ev_ms, ("HIP graphs of one step per buffer set (and of the K mod sets remaining steps), "
+                            "replayed for exactly K steps; span timed by hipEvents on the replay stream; "
+                            "per-kernel times from the library's hipEvents in an eager pass of min(K, 200) "
+                            "steps")
+
+
+def measure(w, K, W, timing, ev, B):
+    """One timed run of workload w: the step and its kernels."""
+    step_ms, ev_ms, how = time_steps(w, K, W, timing, ev)
+    kernels = w.kernels(ev_ms)
+    name, kernel_id, dur_ms, alg, _ = max(kernels, key=lambda x: x[2] * x[4])
+    gbs = w.S * B / (step_ms * 1e-3) / 1e9
+    return dict(step_ms=step_ms, gbs=gbs, kernels=kernels, dominant=(name, kernel_id, dur_ms, alg), how=how,
+                spread=time_steps.spread)
 
 
 def pack_bench(cfg, dev, reps: int):
@@ -587,7 +674,16 @@ def copy_calibration(fp, dev, launches: int) -> int:
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    """The host CPU's model name as lscpu reports it, else /proc/cpuinfo's, else
+    the machine type."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -651,22 +747,72 @@ def load_traffic(workload: str, kernel: str):
 
 
 # ------------------------------------------------------------------ main
+PATH_NAMES = {0: "one-pass", 1: "two-phase", 2: "fused-no-skip", 3: "fused-no-skip-split", 4: "speculative",
+              5: "speculative-split"}
+
+
+def kernel_lines(kernels):
+    return [{"name": nm, "avg_us": round(d * 1e3, 3), "launches_per_step": c, "alg_bytes": a,
+             "alg_GBps": round(a / (d * 1e-3) / 1e9, 1)} for nm, _, d, a, c in kernels]
+
+
+def summary(cfg, w, mode, r, B):
+    """The figures of one timed run, for the `configs` and `modes` entries."""
+    name, _, dur_ms, alg = r["dominant"]
+    kgbs = alg / (dur_ms * 1e-3) / 1e9
+    return {"mode": mode, "path": PATH_NAMES[w.path], "ms_per_step": round(r["step_ms"], 5),
+            "GBps": round(r["gbs"], 2), "frac_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4),
+            "params_per_s": round(w.S / (r["step_ms"] * 1e-3), 1),
+            "dominant_kernel": {"name": name, "avg_us": round(dur_ms * 1e3, 3), "alg_bytes": alg,
+                                "alg_GBps": round(kgbs, 1), "frac": round(kgbs / HBM_PEAK_GBS, 4)}}
+
+
+def side_config(name, K, W, timing, ev, dev):
+    """A workload of the `configs` entry: its default (speculative) mode and the
+    in-place exact skip, exactly K steps each."""
+    import torch
+    import sharded_flatparameter_pack_amd as fp
+    from workloads import CONFIGS
+    cfg = CONFIGS[name]
+    rank = cfg.ranks[0]
+    B = step_bytes_per_elem(cfg.world, cfg.n_micro)
+    w = make_workload(cfg, rank, dev, fp.FP_STEP_EXACT_SKIP, True)
+    out = {"workload": name, "N_d": cfg.world, "rank": rank, "shard_elems": w.S, "units": len(cfg.units()),
+           "n_micro": cfg.n_micro, "alg_bytes_per_elem": B, "buffer_sets": w.n_sets, "steps": K}
+    r = measure(w, K, W, timing, ev, B)
+    bad = w.flagged()
+    if bad:
+        raise RuntimeError(f"{name}: {bad}")
+    out.update(summary(cfg, w, "speculative", r, B))
+    out["kernels"] = kernel_lines(r["kernels"])
+    out["timing"] = r["how"]
+    w.set_flags(fp.FP_STEP_EXACT_SKIP, False)
+    r = measure(w, K, W, timing, ev, B)
+    out["in_place_exact"] = summary(cfg, w, "exact", r, B)
+    del w
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="c2_layer_d1024_nd8")
-    ap.add_argument("--mode", choices=list(MODE_FLAGS), default="exact",
-                    help="exact: exact overflow skip (one-pass kernel when the shard fits); "
-                         "twophase: exact skip with two kernels; noskip: one pass, no gate; "
-                         "speculative: exact skip with separate output state buffers (the no-skip "
-                         "pass, then a restore kernel that acts only on overflow)")
-    ap.add_argument("--eager", action="store_true",
-                    help="launch every step from Python with per-kernel events (launch-bound for "
-                         "small shards) instead of replaying a captured HIP graph")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--mode", choices=list(MODE_FLAGS), default="speculative",
+                    help="speculative: exact overflow skip with separate output state (the fused pass, "
+                         "then a restore kernel that acts only on overflow); exact: exact skip in place "
+                         "(one-pass kernel when the shard fits the co-resident grid, else two kernels); "
+                         "twophase: exact skip in place with two kernels; noskip: one pass, no gate")
+    ap.add_argument("--timing", choices=("auto", "graph", "eager"), default="auto",
+                    help="auto: eager launches with per-kernel events for steps of 0.2 ms and more, "
+                         "HIP graph replays for shorter (launch-bound) steps")
+    ap.add_argument("--eager", action="store_true", help="same as --timing eager")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the other modes, the pack and the copy reference")
+                    help="skip the other modes, the pack, layout and copy legs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (the `configs` entry of the default line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run fp_unshard (a plain copy of known size) for counter calibration")
     ap.add_argument("--dim0-only", action="store_true",
@@ -682,10 +828,14 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)
+    timing = "eager" if args.eager else args.timing
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the N_d ranks of the shard "
               f"step are buffers on that GPU; there is no multi-GPU path in this build.", file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
         return 2
 
     import torch
@@ -726,56 +876,58 @@ def main(argv=None) -> int:
     world, n = cfg.world, cfg.n_micro
     B = step_bytes_per_elem(world, n)
     ev = HipEvents()
-    path_names = {fp.FP_PATH_ONE_PASS: "one-pass", fp.FP_PATH_TWO_PHASE: "two-phase",
-                  fp.FP_PATH_NO_SKIP: "fused-no-skip", fp.FP_PATH_NO_SKIP_SPLIT: "fused-no-skip-split",
-                  fp.FP_PATH_SPECULATIVE: "speculative", fp.FP_PATH_SPECULATIVE_SPLIT: "speculative-split"}
+    K = args.steps
 
     w = make_workload(cfg, rank, dev, getattr(fp, MODE_FLAGS[args.mode]), args.mode in OUT_OF_PLACE_MODES)
     S = w.S
-    time_steps.spread = None
-    step_ms, ev_ms, K, timing = time_steps(w, args.steps, args.warmup, args.eager, ev)
-    spread = time_steps.spread
+    r = measure(w, K, args.warmup, timing, ev, B)
     bad = w.flagged()
     if bad:
         print(bad, file=sys.stderr)
         return 1
-    kernels = w.kernels(step_ms, ev_ms)
-    name, kernel_id, dur_ms, alg, _ = max(kernels, key=lambda x: x[2] * x[4])
+    step_ms, gbs = r["step_ms"], r["gbs"]
+    name, kernel_id, dur_ms, alg = r["dominant"]
     achieved = alg / (dur_ms * 1e-3) / 1e9
-    gbs = S * B / (step_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32/f64", "data": "synthetic",
         "config": {"workload": cfg.name, "N_d": world, "rank": rank, "shard_elems": S,
                    "units": len(cfg.units()), "n_micro": n, "mode": args.mode,
-                   "path": path_names[w.path], "alg_bytes_per_elem": B, "buffer_sets": w.n_sets},
+                   "path": PATH_NAMES[w.path], "alg_bytes_per_elem": B, "buffer_sets": w.n_sets},
         "params_per_s": round(S / (step_ms * 1e-3), 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "kernels": [{"name": nm, "avg_us": round(d * 1e3, 3), "launches_per_step": c, "alg_bytes": a,
-                     "alg_GBps": round(a / (d * 1e-3) / 1e9, 1)} for nm, _, d, a, c in kernels],
+        "kernels": kernel_lines(r["kernels"]),
         "roofline": {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(cfg.name, kernel_id)},
-        "timing": timing,
-        "spread": spread,
+        "timing": r["how"],
+        "spread": r["spread"],
         "source_hash": kernel_source_hash(),
     }
+    print(f"# main line done: {cfg.name} {args.mode} {step_ms:.4f} ms/step", file=sys.stderr, flush=True)
     if not args.no_extras:
-        modes = {}
+        modes, seen = {}, {w.path: args.mode}
         for mode in MODE_FLAGS:
             if mode == args.mode:
                 continue
-            if mode in OUT_OF_PLACE_MODES and not getattr(w, "supports_out_of_place", False):
-                continue
             w.set_flags(getattr(fp, MODE_FLAGS[mode]), mode in OUT_OF_PLACE_MODES)
-            ms = time_steps(w, min(args.steps, 400), min(args.warmup, 20), args.eager, ev)[0]
-            modes[mode] = {"path": path_names[w.path], "ms_per_step": round(ms, 5),
-                           "GBps": round(S * B / (ms * 1e-3) / 1e9, 2),
-                           "frac_of_hbm_peak": round(S * B / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if w.path in seen:
+                modes[mode] = {"path": PATH_NAMES[w.path], "same_path_as": seen[w.path]}
+                continue
+            seen[w.path] = mode
+            rm = measure(w, K, min(args.warmup, 20), timing, ev, B)
+            modes[mode] = summary(cfg, w, mode, rm, B)
         result["modes"] = modes
-        del w
-        torch.cuda.empty_cache()
+    del w
+    torch.cuda.empty_cache()
+    if args.workload == DEFAULT_WORKLOAD and not args.no_configs:
+        configs = {}
+        for name2 in SIDE_WORKLOADS:
+            configs[name2] = side_config(name2, K, args.warmup, timing, ev, dev)
+            print(f"# config done: {name2}", file=sys.stderr, flush=True)
+        result["configs"] = configs
+    if not args.no_extras:
         copy_gbs = copy_reference(fp, dev)
         result["copy_reference"] = {"GBps": copy_gbs, "what": "fp_unshard of 16 x 8M bf16 shards "
                                     "(256 MiB read + 256 MiB written): the plain-copy rate on this GPU",
@@ -791,6 +943,7 @@ def main(argv=None) -> int:
         if cfg.n_micro > 1:
             torch.cuda.empty_cache()
             result["no_sync"] = nosync_bench(cfg, dev, 10)
+        print("# extras done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, rank, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -164,11 +164,24 @@ fp_status fp_unpack_views(const fp_plan* plan, int32_t rank, fp_view* out, int32
 int64_t fp_workspace_bytes(int64_t shard);
 
 /* Byte offset, in the workspace, of a uint32 that counts grid-barrier waits
- * of the one-pass step that gave up.  It stays 0 as long as the step's
- * workgroups are co-resident, which the library sizes the grid for; a
- * caller that runs other kernels concurrently on the GPU can check it, or
- * pass FP_STEP_NO_COOP. */
+ * of the one-pass step that gave up (sticky: the library never clears it).
+ * It stays 0 as long as the step's workgroups are co-resident, which the
+ * library sizes the grid for; a caller that runs other kernels concurrently
+ * on the GPU can check it, or pass FP_STEP_NO_COOP. */
 #define FP_WORKSPACE_TIMEOUTS_OFFSET 8320
+
+/* Bits of the device int32 overflow flag (found_inf).  Kernels only ever OR
+ * bits into it; the caller zeroes it at the start of a step.  Any nonzero
+ * value makes AdamW skip and counts as an overflow for fp_scaler_update.
+ *   FP_FLAG_OVERFLOW -- a reduced gradient element was +-inf or NaN.
+ *   FP_FLAG_GAVE_UP  -- the one-pass step's grid barrier gave up waiting
+ *     (its workgroups were not resident together, e.g. because other
+ *     kernels shared the GPU): that call stored no state, no own-shard
+ *     element and no acc element that was an input, so the step was not
+ *     taken.  The caller may clear this bit and run the call again with
+ *     FP_STEP_NO_COOP. */
+#define FP_FLAG_OVERFLOW 1
+#define FP_FLAG_GAVE_UP 2
 
 /* One micro-batch of the reduce-scatter arithmetic for this rank's shard.
  * [GUIDE] section 2 (equation for the averaged gradient): the synchronised
@@ -181,9 +194,9 @@ int64_t fp_workspace_bytes(int64_t shard);
  *   s = bf16(grads[0][i]); s = s + bf16(grads[q][i]) for q = 1..N-1 in
  *   ascending order (fp32, round-to-nearest-even, no fused multiply-add);
  *   y = s * scale (fp32);  acc[i] = accumulate ? acc[i] + y : y.
- * Then *found_inf is set to 1 if any new acc[i] is +-inf or NaN (it is
- * never cleared: the caller zeroes it at the start of a step, so the flag
- * ORs over micro-batches), and, if sq_norm != NULL, *sq_norm = sum of
+ * Then FP_FLAG_OVERFLOW is OR-ed into *found_inf if any new acc[i] is
+ * +-inf or NaN (it is never cleared: the caller zeroes it at the start of a
+ * step, so the flag ORs over micro-batches), and, if sq_norm != NULL, *sq_norm = sum of
  * acc[i]^2 over the shard in fp64 (a fixed-order tree over a fixed grid:
  * bitwise reproducible run to run).
  * S >= 0; world in [1, FP_MAX_WORLD]; grads: host array of world device
@@ -300,7 +313,14 @@ fp_status fp_unshard(int64_t shard, int32_t world, const uint16_t* const* shards
  *   FP_STEP_NO_COOP (may be or-ed in) -- use the two-kernel form even when
  *     the one-pass cooperative kernel would fit (for callers that share the
  *     GPU with concurrent kernels).
- * On return *found_inf is the OR of its input and this call's check. */
+ * On return *found_inf is the OR of its input, this call's check
+ * (FP_FLAG_OVERFLOW) and, from the one-pass kernel only, FP_FLAG_GAVE_UP
+ * when its barrier gave up: then master / exp_avg / exp_avg_sq, full's own
+ * slice and acc are as they were (the one-pass kernel is not chosen when
+ * FP_STEP_KEEP_GRAD is combined with accumulate), the other shards may have
+ * been copied, and the step can be run again with FP_STEP_NO_COOP after
+ * clearing that bit.  The barrier decides for all workgroups alike, so no
+ * call ever leaves a partly updated shard. */
 typedef struct fp_step_args {
     int64_t shard;                 /* S */
     int32_t world;                 /* N_d, in [1, FP_MAX_WORLD] */
@@ -378,6 +398,15 @@ fp_status fp_shard_step(const fp_step_args* args, void* stream);
 #define FP_PATH_SPECULATIVE_SPLIT 5
 fp_status fp_step_path(const fp_step_args* args, int32_t* path);
 
+/* For tests of the one-pass kernel's give-up path.  Runs fp_shard_step's
+ * one-pass kernel (FP_ERR_INVALID unless fp_step_path would return
+ * FP_PATH_ONE_PASS for these arguments) with a grid barrier that waits for
+ * one workgroup more than the launch holds and gives up after 64 polls, so
+ * every wait gives up and the kernel ends normally: the result is the
+ * FP_FLAG_GAVE_UP outcome described above.  The barrier's counters are left
+ * mid-generation: zero-fill the workspace before passing it to another call. */
+fp_status fp_step_test_give_up(const fp_step_args* args, void* stream);
+
 /* ------------------------------------------------------------------ units */
 
 /* Many units (for example the ~25 MB DDP buckets of a model, or a model's
@@ -430,7 +459,16 @@ fp_status fp_units_reduce(const fp_units* units, float scale, int32_t accumulate
  * the casts into each unit's full + rank * S_u); FP_STEP_NO_SKIP one fused
  * launch; FP_STEP_KEEP_GRAD may be or-ed in.  acc, master, exp_avg,
  * exp_avg_sq: device fp32[partition], 16-byte aligned.  profile_events as
- * in fp_step_args.  Requires a plan made with shards and full. */
+ * in fp_step_args.  Requires a plan made with shards and full.
+ * master_out / exp_avg_out / exp_avg_sq_out: all NULL (in place) or all
+ * three device fp32[partition], 16-byte aligned, distinct from every other
+ * buffer: the speculative form, as in fp_step_args -- the fused launch
+ * writes the update of every unit to these partitions without waiting for
+ * the overflow check and, with FP_STEP_EXACT_SKIP, a last kernel copies the
+ * input state to them (and recasts every own slice) when the flag is set,
+ * so the result is the exact-skip step's; the caller swaps input and output
+ * partitions after each step.  The step then moves no reduced gradient
+ * through acc (with FP_STEP_KEEP_GRAD it is still written there). */
 typedef struct fp_units_step_args {
     float scale;
     int32_t accumulate;
@@ -445,6 +483,9 @@ typedef struct fp_units_step_args {
     int32_t flags;
     void* const* profile_events;
     const double* grad_coef;       /* as in fp_step_args, may be NULL */
+    float* master_out;             /* NULL, or with the next two the output partitions */
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
 } fp_units_step_args;
 fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream);
 

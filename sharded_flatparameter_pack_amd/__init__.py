@@ -23,13 +23,13 @@ from . import _lib
 from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_NO_SKIP_SPLIT, FP_PATH_ONE_PASS,  # noqa: F401
                    FP_PATH_SPECULATIVE, FP_PATH_SPECULATIVE_SPLIT,
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
-                   FP_STEP_NO_SKIP, FlatParamError, check, lib)
+                   FP_STEP_NO_SKIP, FP_FLAG_OVERFLOW, FP_FLAG_GAVE_UP, FlatParamError, check, lib)
 
 __all__ = ["Plan", "Units", "Shard0Plan", "ReshardPlan", "reduce_shard_hybrid", "local_accumulate", "local_finish", "grad_coef", "scaler_update", "reduce_shard", "adamw_shard", "unshard", "shard_step", "ShardStep", "state_bytes",
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
            "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "FP_PATH_NO_SKIP_SPLIT", "FP_PATH_SPECULATIVE",
-           "FP_PATH_SPECULATIVE_SPLIT", "library_path"]
+           "FP_PATH_SPECULATIVE_SPLIT", "FP_FLAG_OVERFLOW", "FP_FLAG_GAVE_UP", "library_path"]
 
 
 def library_path() -> str:
@@ -571,6 +571,15 @@ class ShardStep:
             a.profile_events = C.cast(self._events, C.c_void_p)
         check(self._fn(C.byref(a), _stream(self._device)))
 
+    def test_give_up(self, step: int):
+        """fp_step_test_give_up with these arguments: the one-pass kernel with a
+        barrier that always gives up (for tests of that path; the workspace must
+        be zero-filled again afterwards)."""
+        a = self._args
+        a.hp.step = int(step)
+        a.profile_events = None
+        check(lib().fp_step_test_give_up(C.byref(a), _stream(self._device)))
+
     def path(self) -> int:
         """One of the FP_PATH_* values: the kernels a call launches on this device."""
         torch = _torch()
@@ -670,8 +679,15 @@ class Units:
 
     def step(self, acc, master, exp_avg, exp_avg_sq, *, scale: float, lr, beta1, beta2, eps,
              weight_decay, step: int, found_inf, accumulate: bool = False, sq_norm=None,
-             workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None, grad_coef=None):
-        _one_device(acc, master, exp_avg, exp_avg_sq, found_inf, sq_norm, workspace, grad_coef)
+             workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None, grad_coef=None,
+             out=None):
+        """The last micro-batch's step over all units.  out: None (in place) or
+        (master_out, exp_avg_out, exp_avg_sq_out) partitions that receive the new
+        state while master / exp_avg / exp_avg_sq are only read (the speculative
+        step; the caller swaps the partitions after each step)."""
+        _one_device(acc, master, exp_avg, exp_avg_sq, found_inf, sq_norm, workspace, grad_coef, out)
+        if out is not None and len(out) != 3:
+            raise ValueError("out is (master_out, exp_avg_out, exp_avg_sq_out)")
         torch = _torch()
         P = self.partition
         a = _lib.fp_units_step_args()
@@ -684,6 +700,10 @@ class Units:
         a.workspace = self._opt(workspace, torch.uint8, self.workspace_bytes, "workspace")
         a.flags = int(flags)
         a.grad_coef = _coef_ptr(grad_coef)
+        if out is not None:
+            a.master_out = _f32(out[0], P, "master_out")
+            a.exp_avg_out = _f32(out[1], P, "exp_avg_out")
+            a.exp_avg_sq_out = _f32(out[2], P, "exp_avg_sq_out")
         ev = None
         if profile_events is not None:
             if len(profile_events) != _lib.FP_STEP_EVENTS:

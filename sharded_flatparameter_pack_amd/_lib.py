@@ -31,6 +31,8 @@ FP_PATH_NO_SKIP_SPLIT = 3
 FP_PATH_SPECULATIVE = 4
 FP_PATH_SPECULATIVE_SPLIT = 5
 FP_WORKSPACE_TIMEOUTS_OFFSET = 8320
+FP_FLAG_OVERFLOW = 1
+FP_FLAG_GAVE_UP = 2
 
 _i32, _i64, _f32, _f64, _vp = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p
 
@@ -58,7 +60,8 @@ class fp_units_step_args(C.Structure):
     _fields_ = [("scale", _f32), ("accumulate", _i32), ("acc", _vp), ("master", _vp),
                 ("exp_avg", _vp), ("exp_avg_sq", _vp), ("hp", fp_adamw_hparams),
                 ("found_inf", _vp), ("sq_norm", _vp), ("workspace", _vp), ("flags", _i32),
-                ("profile_events", _vp), ("grad_coef", _vp)]
+                ("profile_events", _vp), ("grad_coef", _vp), ("master_out", _vp), ("exp_avg_out", _vp),
+                ("exp_avg_sq_out", _vp)]
 
 
 # name -> (restype, argtypes); the export test compares this table with the header
@@ -75,6 +78,7 @@ SIGNATURES = {
     "fp_unshard": (_i32, [_i64, _i32, _vp, _vp, _vp]),
     "fp_shard_step": (_i32, [C.POINTER(fp_step_args), _vp]),
     "fp_step_path": (_i32, [C.POINTER(fp_step_args), C.POINTER(C.c_int32)]),
+    "fp_step_test_give_up": (_i32, [C.POINTER(fp_step_args), _vp]),
     "fp_units_create": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, C.POINTER(_vp)]),
     "fp_units_destroy": (None, [_vp]),
     "fp_units_info": (_i32, [_vp, _vp, _vp]),

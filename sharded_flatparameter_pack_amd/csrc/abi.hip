@@ -709,7 +709,11 @@ fp_status step_path(const fp_step_args& x, int32_t* path, int* variant, int* gri
         *path = x.shard >= kSplitElems ? FP_PATH_SPECULATIVE_SPLIT : FP_PATH_SPECULATIVE;
         return FP_OK;
     }
-    if (x.workspace != nullptr && !(x.flags & FP_STEP_NO_COOP)) {
+    // The one-pass kernel writes a kept gradient before its barrier, so it is
+    // not used when acc is also an input (a cancelled barrier must leave acc
+    // as it was).
+    const bool acc_in_and_out = (x.flags & FP_STEP_KEEP_GRAD) && x.accumulate;
+    if (x.workspace != nullptr && !(x.flags & FP_STEP_NO_COOP) && !acc_in_and_out) {
         const hipError_t e = plan_step_coop(x.shard, variant, grid);
         if (e != hipSuccess) return device_fail(e, "occupancy query");
     }
@@ -728,7 +732,8 @@ extern "C" fp_status fp_step_path(const fp_step_args* args, int32_t* path) {
     return step_path(*args, path, &variant, &grid);
 }
 
-extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
+namespace {
+fp_status shard_step_impl(const fp_step_args* args, void* stream, bool give_up_test) {
     if (args == nullptr) return fail(FP_ERR_INVALID, "args is NULL");
     const fp_step_args& x = *args;
     const int64_t S = x.shard;
@@ -739,6 +744,8 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     int32_t path = 0;
     int variant = -1, grid = 0;
     if ((st = step_path(x, &path, &variant, &grid)) != FP_OK) return st;
+    if (give_up_test && path != FP_PATH_ONE_PASS)
+        return fail(FP_ERR_INVALID, "these arguments do not take the one-pass path");
 
     const bool speculative = path == FP_PATH_SPECULATIVE || path == FP_PATH_SPECULATIVE_SPLIT;
     // the fused launch(es) without a gate: no-skip, and speculative (gate after)
@@ -784,7 +791,7 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
 
     if (path == FP_PATH_ONE_PASS) {
         if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-        if ((e = launch_step_coop(a, variant, grid, aligned, copy_aligned, s)) != hipSuccess)
+        if ((e = launch_step_coop(a, variant, grid, aligned, copy_aligned, s, give_up_test)) != hipSuccess)
             return device_fail(e, "one-pass step launch");
         if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
         if (x.sq_norm != nullptr && (e = launch_norm_finalize(a.partials, grid, x.sq_norm, s)) != hipSuccess)
@@ -853,6 +860,15 @@ extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
     }
     if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     return FP_OK;
+}
+}  // namespace
+
+extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
+    return shard_step_impl(args, stream, false);
+}
+
+extern "C" fp_status fp_step_test_give_up(const fp_step_args* args, void* stream) {
+    return shard_step_impl(args, stream, true);
 }
 
 // ---------------------------------------------------------------------- units
@@ -1121,9 +1137,12 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
     fill_units_args(units, &a);
     fp_status st;
     if ((st = check_hparams(&x.hp, &a.c)) != FP_OK) return st;
-    const float* f32[4] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq};
-    const char* names[4] = {"acc", "master", "exp_avg", "exp_avg_sq"};
-    if ((st = check_units_state(units, f32, names, 4)) != FP_OK) return st;
+    const int n_out = (x.master_out != nullptr) + (x.exp_avg_out != nullptr) + (x.exp_avg_sq_out != nullptr);
+    if (n_out != 0 && n_out != 3)
+        return fail(FP_ERR_INVALID, "master_out / exp_avg_out / exp_avg_sq_out: give all three or none");
+    const float* f32[7] = {x.acc, x.master, x.exp_avg, x.exp_avg_sq, x.master_out, x.exp_avg_out, x.exp_avg_sq_out};
+    const char* names[7] = {"acc", "master", "exp_avg", "exp_avg_sq", "master_out", "exp_avg_out", "exp_avg_sq_out"};
+    if ((st = check_units_state(units, f32, names, 4 + n_out)) != FP_OK) return st;
     if (x.found_inf == nullptr) return fail(FP_ERR_INVALID, "found_inf is NULL");
     if (!aligned(x.found_inf, 4)) return fail(FP_ERR_ALIGN, "found_inf misaligned");
     if (x.sq_norm != nullptr) {
@@ -1133,8 +1152,13 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
     }
     if (x.grad_coef != nullptr && !aligned(x.grad_coef, 8)) return fail(FP_ERR_ALIGN, "grad_coef misaligned");
     if ((st = check_units_device(units)) != FP_OK) return st;
-    const bool no_skip = (x.flags & FP_STEP_NO_SKIP) != 0;
+    const bool speculative = n_out == 3 && !(x.flags & FP_STEP_NO_SKIP);
+    // the fused launch without a gate: no-skip, and speculative (gate after)
+    const bool no_skip = (x.flags & FP_STEP_NO_SKIP) != 0 || speculative;
     a.g_coef = x.grad_coef;
+    a.master_out = x.master_out;
+    a.exp_avg_out = x.exp_avg_out;
+    a.exp_avg_sq_out = x.exp_avg_sq_out;
     a.acc = x.acc;
     a.master = x.master;
     a.exp_avg = x.exp_avg;
@@ -1158,6 +1182,9 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
         if (x.sq_norm != nullptr &&
             (e = launch_norm_finalize(a.partials, (int)units->reduce_groups, x.sq_norm, s)) != hipSuccess)
             return device_fail(e, "norm launch");
+        // the skip rule, applied after the update: restore on overflow
+        if (speculative && (e = launch_units_resolve(a, s)) != hipSuccess)
+            return device_fail(e, "units resolve launch");
     } else {
         a.sq_norm = x.sq_norm;
         if ((e = launch_units_adamw(a, units->aligned, s)) != hipSuccess) return device_fail(e, "units adamw launch");

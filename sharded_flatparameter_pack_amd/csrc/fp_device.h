@@ -181,10 +181,16 @@ __device__ __forceinline__ double group_sum(double x) {
     return r;
 }
 
-// Raise the overflow flag if any lane of the wave saw a non-finite value.
-// The flag is only ever set to 1, so concurrent stores of 1 are benign.
+// OR bits into the overflow flag (a vector atomic): the flag is never
+// cleared by a kernel, so bits set by earlier calls survive.
+__device__ __forceinline__ void flag_or(int32_t* flag, int32_t bits) {
+    __hip_atomic_fetch_or(flag, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Raise the overflow flag (bit 0) if any lane of the wave saw a non-finite
+// value: one atomic OR per wave, only on overflow.
 __device__ __forceinline__ void flag_if_any(bool bad, int32_t* flag) {
-    if (flag != nullptr && __ballot(bad) != 0ull && (threadIdx.x & 63) == 0) *flag = 1;
+    if (flag != nullptr && __ballot(bad) != 0ull && (threadIdx.x & 63) == 0) flag_or(flag, 1);
 }
 
 }  // namespace fpk

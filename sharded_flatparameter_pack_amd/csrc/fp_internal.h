@@ -181,6 +181,8 @@ struct StepArgs {
     int32_t reduce_groups;   // workgroups of the reduce role (barrier members in one pass)
     int32_t copy_tiles;      // copy tiles per shard
     GridSync* sync;          // one-pass: barrier state in the workspace
+    int32_t barrier_n;       // one-pass: members the barrier waits for
+    uint32_t spin_limit;     // one-pass: polls before a wait gives up
     // Where the fused update stores the state: separate buffers for the
     // speculative step, else master / exp_avg / exp_avg_sq themselves.
     float* master_out;
@@ -248,6 +250,11 @@ struct UnitsArgs {
     int32_t rank;
     int32_t accumulate;
     int32_t keep_grad;
+    // Where the fused update stores the state: separate partitions for the
+    // speculative step, else master / exp_avg / exp_avg_sq themselves.
+    float* master_out;
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
 };
 
 // Ranks reduced per group of loads in flight: 16 when more than 8 ranks
@@ -278,8 +285,10 @@ hipError_t launch_step_phase1(const StepArgs& a, int64_t grid, bool fused_update
 // 2 or 4 quads in registers) and a grid that fits the device's co-resident
 // capacity, or sets *variant = -1 when the shard is too large.
 hipError_t plan_step_coop(int64_t shard, int* variant, int* grid);
+// give_up_test: every barrier wait gives up (the cancelled decision), for
+// testing that path from the host.
 hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, bool copy_aligned,
-                            hipStream_t s);
+                            hipStream_t s, bool give_up_test = false);
 hipError_t launch_step_resolve(const ResolveArgs& r, hipStream_t s);
 // Multi-unit launches: one micro-batch's reduce over all units; the last
 // micro-batch's reduce (+ AdamW when fused) with the copies of all units'
@@ -289,5 +298,8 @@ hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s);
 hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update,
                                bool aligned, bool copy_aligned, hipStream_t s);
 hipError_t launch_units_adamw(const UnitsArgs& a, bool aligned, hipStream_t s);
+// The speculative multi-unit step's last kernel: on overflow, every unit's
+// output state takes its input state and its own slice the bf16 cast.
+hipError_t launch_units_resolve(const UnitsArgs& a, hipStream_t s);
 
 }  // namespace fpk

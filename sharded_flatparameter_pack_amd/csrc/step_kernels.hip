@@ -79,12 +79,16 @@ __global__ __launch_bounds__(kThreads) void step_resolve_kernel(const ResolveArg
 // the ranks' gradient quads (none of which depends on the overflow flag),
 // reduces, and computes the AdamW update into registers.  The workgroup ORs
 // its overflow bit (and the flag left by earlier micro-batches) into the
-// barrier and waits; the barrier returns the grid's flag, after which the
-// lanes only store: the new state and its bf16 cast, or on overflow just the
-// cast of the old master.  Workgroups past reduce_groups copy the other
-// ranks' shards meanwhile and take no part in the barrier.  The reduced
-// gradient never leaves the registers, so the step moves exactly the
-// algorithmic bytes.
+// barrier and waits; the barrier returns the grid's decision, after which
+// the lanes only store: the new state and its bf16 cast, or on overflow just
+// the cast of the old master.  Should a wait give up (the members were not
+// resident together), the barrier is cancelled for every member alike and
+// nothing is stored: the state, acc (unless the reduced gradient is kept
+// for a call without accumulation) and the own slice keep their contents,
+// and bit 1 is OR-ed into the flag.  The flag is only ever OR-ed into.
+// Workgroups past reduce_groups copy the other ranks' shards meanwhile and
+// take no part in the barrier.  The reduced gradient never leaves the
+// registers, so the step moves exactly the algorithmic bytes.
 template <bool kAligned, bool kCopyAligned, int kQ>
 __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     FP_PHASE_MARK(0);
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
         FP_PHASE_MARK(5);
         return;
     }
-    __shared__ unsigned s_skip;
+    __shared__ unsigned s_decision;
     const int64_t nq = a.shard >> 2;
     const bool want_sq = a.partials != nullptr;
     const bool acc_in = a.accumulate != 0;
@@ -123,6 +127,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
             old_bf16[u] = f32x4_to_bf16(st.th[u]);
             if (!Q.ok[u]) continue;
             check_quad(y[u], bad, sq, want_sq);
+            // (the path is chosen so that acc is not an input here)
             if (a.keep_grad) st_f32q(a.acc, Q, u, y[u]);
         }
         adamw_quads<kQ>(c, y, st);
@@ -149,14 +154,21 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     }
     FP_PHASE_MARK(2);
     if (threadIdx.x == 0) {
-        grid_arrive(a.sync, ticket, (group_bad || prior != 0) ? 1u : 0u, (unsigned)a.reduce_groups);
+        const unsigned n = (unsigned)a.barrier_n;
+        grid_arrive(a.sync, ticket, (group_bad || prior != 0) ? 1u : 0u, n);
         FP_PHASE_MARK(3);
-        s_skip = grid_wait(a.sync, ticket);
+        s_decision = grid_wait(a.sync, ticket, n, a.spin_limit);
     }
     FP_PHASE_MARK(4);
     __syncthreads();
-    const bool skip = s_skip != 0u;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.found_inf = skip ? 1 : 0;
+    const unsigned decision = s_decision;
+    if (decision == kBarrierCancelled) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) flag_or(a.found_inf, 2);
+        FP_PHASE_MARK(5);
+        return;
+    }
+    const bool skip = decision == kBarrierOverflow;
+    if (skip && blockIdx.x == 0 && threadIdx.x == 0) flag_or(a.found_inf, 1);
 
     // commit: stores only
     if (nq > 0) {
@@ -344,14 +356,20 @@ hipError_t plan_step_coop(int64_t shard, int* variant, int* grid) {
 }
 
 hipError_t launch_step_coop(const StepArgs& a, int variant, int grid, bool aligned, bool copy_aligned,
-                            hipStream_t s) {
+                            hipStream_t s, bool give_up_test) {
     // A plain launch (a cooperative launch costs ~17 us more per launch on
     // MI355X).  The barrier workgroups [0, reduce_groups) fit the device's
     // resident capacity and are dispatched before the copy workgroups, which
     // never wait; so on a GPU not running other work they are resident
     // together, and otherwise they become so as the copy workgroups finish.
+    // give_up_test: the barrier waits for one member more than the grid holds
+    // and gives up after a few polls, so every wait ends in the cancelled
+    // decision (the barrier never completes, and its counters are left
+    // mid-generation: the caller zero-fills the workspace again).
     StepArgs b = a;
     b.reduce_groups = grid;
+    b.barrier_n = give_up_test ? grid + 1 : grid;
+    b.spin_limit = give_up_test ? 64u : kSpinLimit;
     b.copy_tiles = (int32_t)copy_tiles_per_shard(a.shard, kCopyWordsCoop);
     const dim3 g((unsigned)((int64_t)grid + (int64_t)(a.world - 1) * b.copy_tiles));
 #define FP_COOP(AL, CA)                                                          \

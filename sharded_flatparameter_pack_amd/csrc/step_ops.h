@@ -404,16 +404,36 @@ __device__ __forceinline__ void unshard_edges(const uint16_t* src, uint16_t* ful
 // also ORs one bit (the overflow flag) over them.  Only thread 0 of a
 // workgroup takes part.  Arrival adds 1 (plus the bit at position 16) to
 // its group's counter; the group's last arrival resets that counter and
-// adds its group's result to the top counter; the last group resets the top
-// and writes the next generation, with the grid's bit in bit 31, into every
-// group's copy of the generation word, which the group's members poll.  The
-// bit travels only through read-modify-write results on the counters, so
-// relaxed agent-scope atomics suffice: no fences, no cache write-back.
-// Spreading the counters and the polled words over 32 cache lines keeps
-// arrival and polling off a single address.  The wait is bounded: should it
-// ever give up (possible only if the members were not resident together) it
-// counts a timeout in the workspace instead of hanging.
+// adds its group's result to the top counter; the last group decides,
+// resets the top counter and writes the next generation, with the decision
+// in bits 30-31, into every group's copy of the generation word, which the
+// group's members poll.  The bit travels only through read-modify-write
+// results on the counters, so relaxed agent-scope atomics suffice: no
+// fences, no cache write-back.  Spreading the counters and the polled words
+// over 32 cache lines keeps arrival and polling off a single address.
+//
+// The wait is bounded.  A member that gives up (possible only if the
+// members were not resident together) counts a timeout in the workspace and
+// cancels the barrier: a compare-and-swap sets the cancel bit in the top
+// counter while groups are still missing.  The last group's add returns
+// that bit, so it publishes "cancelled"; if instead every group had already
+// arrived, the member adopts the last group's decision.  Either way every
+// member leaves with the same one of three decisions, and a cancelled
+// barrier still completes (every member arrives before it waits), which
+// leaves the counters reusable.
+//
+// Top counter: bits 0-15 groups arrived, 16-21 groups that saw the bit,
+// 22 cancel requested, 23 / 24 overflow / cancelled decided by the
+// generation that completed last, 28-29 the generation in progress (low two
+// bits).  Generation word: bits 0-29 generation, 30 cancelled, 31 overflow.
 constexpr unsigned kSpinLimit = 1u << 22;
+constexpr unsigned kBarrierClean = 0u, kBarrierOverflow = 1u, kBarrierCancelled = 2u;
+constexpr unsigned kGenMask = 0x3FFFFFFFu;
+constexpr unsigned kTopCount = 0xFFFFu;
+constexpr unsigned kTopCancel = 1u << 22;
+constexpr unsigned kTopPrevOverflow = 1u << 23;
+constexpr unsigned kTopPrevCancel = 1u << 24;
+constexpr unsigned kTopTagShift = 28;
 
 __device__ __forceinline__ unsigned sync_load(const unsigned* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -424,21 +444,28 @@ __device__ __forceinline__ void sync_store(unsigned* p, unsigned v) {
 __device__ __forceinline__ unsigned sync_add(unsigned* p, unsigned v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Compare-and-swap; on failure `expect` receives the current value.
+__device__ __forceinline__ bool sync_cas(unsigned* p, unsigned& expect, unsigned v) {
+    return __hip_atomic_compare_exchange_strong(p, &expect, v, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct BarrierTicket {
     unsigned group;
-    unsigned gen0;
+    unsigned gen0;  // the generation in progress (bits 0-29)
 };
 
 __device__ __forceinline__ BarrierTicket grid_ticket(GridSync* s) {
     BarrierTicket t;
     t.group = blockIdx.x % kSyncGroups;
-    t.gen0 = sync_load(&s->gen[t.group * kLineWords]);
+    t.gen0 = sync_load(&s->gen[t.group * kLineWords]) & kGenMask;
     return t;
 }
 
+__device__ __forceinline__ unsigned sync_groups(unsigned n) { return n < (unsigned)kSyncGroups ? n : (unsigned)kSyncGroups; }
+
 __device__ __forceinline__ void grid_arrive(GridSync* s, const BarrierTicket& t, unsigned bit, unsigned n) {
-    const unsigned n_groups = n < (unsigned)kSyncGroups ? n : (unsigned)kSyncGroups;
+    const unsigned n_groups = sync_groups(n);
     const unsigned members = n / kSyncGroups + (t.group < n % kSyncGroups ? 1u : 0u);
     const unsigned inc = 1u + (bit << 16);
     const unsigned old = sync_add(&s->group[t.group * kLineWords], inc);
@@ -447,23 +474,48 @@ __device__ __forceinline__ void grid_arrive(GridSync* s, const BarrierTicket& t,
     const unsigned group_bit = ((old + inc) >> 16) != 0 ? 1u : 0u;
     const unsigned tinc = 1u + (group_bit << 16);
     const unsigned told = sync_add(&s->top[0], tinc);
-    if ((told & 0xFFFFu) != n_groups - 1) return;
-    sync_store(&s->top[0], 0u);
-    const unsigned grid_bit = ((told + tinc) >> 16) != 0 ? 1u : 0u;
-    const unsigned next = ((t.gen0 + 1u) & 0x7FFFFFFFu) | (grid_bit << 31);
-    for (unsigned k = 0; k < n_groups; ++k) sync_store(&s->gen[k * kLineWords], next);
+    if ((told & kTopCount) != n_groups - 1) return;
+    const unsigned v = told + tinc;
+    const unsigned overflow = ((v >> 16) & 0x3Fu) != 0 ? 1u : 0u;
+    const unsigned cancelled = (v & kTopCancel) != 0 ? 1u : 0u;
+    const unsigned next = (t.gen0 + 1u) & kGenMask;
+    sync_store(&s->top[0], ((next & 3u) << kTopTagShift) | (overflow ? kTopPrevOverflow : 0u) |
+                               (cancelled ? kTopPrevCancel : 0u));
+    const unsigned word = next | (cancelled << 30) | (overflow << 31);
+    for (unsigned k = 0; k < n_groups; ++k) sync_store(&s->gen[k * kLineWords], word);
 }
 
-// Returns the members' OR of the arrival bits.
-__device__ __forceinline__ unsigned grid_wait(GridSync* s, const BarrierTicket& t) {
+// A member that gave up waiting: cancel the barrier unless every group has
+// arrived, and return the decision all members share.  The top counter takes
+// at most n_groups + 2 distinct values per generation, and every failed
+// compare-and-swap returns a newer one, so the loop ends within its bound.
+__device__ __forceinline__ unsigned grid_cancel(GridSync* s, const BarrierTicket& t, unsigned n) {
+    const unsigned n_groups = sync_groups(n);
+    unsigned v = sync_load(&s->top[0]);
+    for (int k = 0; k < 4 * kSyncGroups; ++k) {
+        if (((v >> kTopTagShift) & 3u) != (t.gen0 & 3u))  // completed and reset: the decision is kept
+            return (v & kTopPrevCancel) ? kBarrierCancelled
+                                        : ((v & kTopPrevOverflow) ? kBarrierOverflow : kBarrierClean);
+        if (v & kTopCancel) return kBarrierCancelled;
+        if ((v & kTopCount) >= n_groups)                   // decided by the last group, not yet reset
+            return ((v >> 16) & 0x3Fu) != 0 ? kBarrierOverflow : kBarrierClean;
+        if (sync_cas(&s->top[0], v, v | kTopCancel)) return kBarrierCancelled;
+    }
+    return kBarrierCancelled;
+}
+
+// The barrier's decision: kBarrierClean, kBarrierOverflow (some member
+// arrived with the bit) or kBarrierCancelled (some member gave up).
+__device__ __forceinline__ unsigned grid_wait(GridSync* s, const BarrierTicket& t, unsigned n,
+                                              unsigned spin_limit) {
     const unsigned* word = &s->gen[t.group * kLineWords];
-    for (unsigned i = 0; i < kSpinLimit; ++i) {
+    for (unsigned i = 0; i < spin_limit; ++i) {
         const unsigned v = sync_load(word);
-        if ((v & 0x7FFFFFFFu) != (t.gen0 & 0x7FFFFFFFu)) return v >> 31;
+        if ((v & kGenMask) != t.gen0) return (v >> 30) & 1u ? kBarrierCancelled : (v >> 31);
         __builtin_amdgcn_s_sleep(2);
     }
     sync_add(&s->timeouts, 1u);
-    return 0u;
+    return grid_cancel(s, t, n);
 }
 
 // ---------------------------------------------------------------- norm

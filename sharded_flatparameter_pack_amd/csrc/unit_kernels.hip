@@ -22,6 +22,9 @@ struct UnitView {
     float* master;
     float* exp_avg;
     float* exp_avg_sq;
+    float* master_out;
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
     int64_t shard;
     int64_t tile0;
     int64_t copy0;
@@ -46,8 +49,7 @@ __device__ __forceinline__ int unit_of_group(const UnitsArgs& a, int64_t group) 
     return a.unit_of[group];
 }
 
-__device__ __forceinline__ UnitView unit_view(const UnitsArgs& a, int64_t group) {
-    const int u = unit_of_group(a, group);
+__device__ __forceinline__ UnitView unit_view_of(const UnitsArgs& a, int u) {
     const char* rec = a.records + (int64_t)u * a.record_bytes;
     const UnitDesc& d = *reinterpret_cast<const UnitDesc*>(rec);
     UnitView v;
@@ -58,6 +60,10 @@ __device__ __forceinline__ UnitView unit_view(const UnitsArgs& a, int64_t group)
     v.master = a.master + d.offset;
     v.exp_avg = a.exp_avg + d.offset;
     v.exp_avg_sq = a.exp_avg_sq + d.offset;
+    const bool out = a.master_out != nullptr;
+    v.master_out = (out ? a.master_out : a.master) + d.offset;
+    v.exp_avg_out = (out ? a.exp_avg_out : a.exp_avg) + d.offset;
+    v.exp_avg_sq_out = (out ? a.exp_avg_sq_out : a.exp_avg_sq) + d.offset;
     v.shard = d.shard;
     v.tile0 = d.tile0;
     v.copy0 = d.copy0;
@@ -70,8 +76,18 @@ __device__ __forceinline__ UnitView unit_view(const UnitsArgs& a, int64_t group)
     return v;
 }
 
+__device__ __forceinline__ UnitView unit_view(const UnitsArgs& a, int64_t group) {
+    return unit_view_of(a, unit_of_group(a, group));
+}
+
 __device__ __forceinline__ uint16_t* own_slice(const UnitView& v) {
     return v.full != nullptr ? v.full + (int64_t)v.rank * v.shard : nullptr;
+}
+
+// The fused update of a unit stores its state to the step's output
+// partitions (found by argument-dependent lookup from the tile bodies).
+__device__ __forceinline__ StateOut state_out(const UnitView& v) {
+    return {v.master_out, v.exp_avg_out, v.exp_avg_sq_out};
 }
 
 }  // namespace
@@ -101,6 +117,28 @@ __global__ __launch_bounds__(kThreads) void units_adamw_kernel(const UnitsArgs a
         finalize_norm(a.partials, (int)a.reduce_groups, a.sq_norm);
     const UnitView v = unit_view(a, blockIdx.x);
     adamw_tile<kAligned>(v, v.acc, (int64_t)blockIdx.x - v.tile0, a.found_inf, own_slice(v));
+}
+
+// Last kernel of the speculative multi-unit step: if the flag (the OR over
+// the step's micro-batches and all units) is set, every unit's output state
+// takes its unchanged input state and its own slice of full the bf16 cast
+// of the unchanged master, as a skipped step leaves them; otherwise every
+// workgroup returns at once.  A grid-stride loop over each unit in turn: it
+// only runs on a skipped step.
+__global__ __launch_bounds__(kThreads) void units_resolve_kernel(const UnitsArgs a) {
+    if (*a.found_inf == 0) return;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int u = 0; u < a.n_units; ++u) {
+        const UnitView v = unit_view_of(a, u);
+        uint16_t* own = own_slice(v);
+        for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < v.shard; j += stride) {
+            const float th = v.master[j];
+            v.master_out[j] = th;
+            v.exp_avg_out[j] = v.exp_avg[j];
+            v.exp_avg_sq_out[j] = v.exp_avg_sq[j];
+            if (own != nullptr) own[j] = (uint16_t)bf16x2(th, 0.0f);
+        }
+    }
 }
 
 namespace {
@@ -155,6 +193,14 @@ hipError_t launch_units_adamw(const UnitsArgs& a, bool aligned, hipStream_t s) {
     const dim3 g((unsigned)a.reduce_groups);
     if (aligned) units_adamw_kernel<true><<<g, kThreads, 0, s>>>(a);
     else units_adamw_kernel<false><<<g, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_units_resolve(const UnitsArgs& a, hipStream_t s) {
+    constexpr int64_t kMaxResolveGroups = 2048;
+    int64_t grid = a.reduce_groups < kMaxResolveGroups ? a.reduce_groups : kMaxResolveGroups;
+    if (grid < 1) grid = 1;
+    units_resolve_kernel<<<(unsigned)grid, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -56,6 +56,38 @@ def test_struct_layouts_match_the_header(fp):
     assert _lib.fp_step_args.master_out.offset == 64 + 48 + 5 * 8 + 8 + 8 + 8
     assert _lib.fp_step_args.exp_avg_sq_out.offset == 64 + 48 + 5 * 8 + 8 + 8 + 8 + 16
     assert C.sizeof(_lib.fp_step_args) == 64 + 48 + 5 * 8 + 8 + 8 + 8 + 24
+    assert _lib.fp_units_step_args.hp.offset == 40
+    assert _lib.fp_units_step_args.grad_coef.offset == 128
+    assert _lib.fp_units_step_args.exp_avg_sq_out.offset == 152
+    assert C.sizeof(_lib.fp_units_step_args) == 160
+
+
+def test_struct_layouts_match_a_c_compiler(fp, tmp_path):
+    """Every field offset and struct size of the ctypes declarations equals what
+    a C compiler makes of include/flatparam.h."""
+    import shutil
+    import subprocess
+    from sharded_flatparameter_pack_amd import _lib
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = [_lib.fp_view, _lib.fp_adamw_hparams, _lib.fp_step_args, _lib.fp_units_step_args]
+    lines = ['#include <stddef.h>', '#include <stdio.h>', f'#include "{HEADER}"', "int main(void) {"]
+    want = []
+    for st in structs:
+        name = st.__name__
+        lines.append(f'  printf("%zu\\n", sizeof({name}));')
+        want.append(C.sizeof(st))
+        for field, *_ in st._fields_:
+            lines.append(f'  printf("%zu\\n", offsetof({name}, {field}));')
+            want.append(getattr(st, field).offset)
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got == want
 
 
 def _random_shapes(r):
@@ -268,6 +300,14 @@ def test_step_path_without_a_device(fp):
     a.workspace, a.flags = 0xA000000, _lib.FP_STEP_NO_COOP
     assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
     assert path.value == _lib.FP_PATH_TWO_PHASE
+    # the test entry of the one-pass give-up refuses arguments of another path
+    assert _status(L.fp_step_test_give_up, C.byref(a), None) == -1
+    assert b"one-pass" in L.fp_last_error()
+    # a kept gradient into an accumulator that is also an input: never one pass
+    a.flags, a.accumulate = _lib.FP_STEP_KEEP_GRAD, 1
+    assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
+    assert path.value == _lib.FP_PATH_TWO_PHASE
+    a.accumulate = 0
     a.master = 0x4000010                       # overlaps acc
     assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -1
     assert _status(L.fp_step_path, C.byref(a), None) == -1

@@ -34,7 +34,7 @@ def _rows(host_rows, offset):
 
 
 def _units_case(fp, sizes, world, rank, n_micro, step, seed, flags, inf_unit=None, offset=0,
-                with_norm=True):
+                with_norm=True, out_of_place=False):
     U = len(sizes)
     scale = np.float32(1.0 / (world * n_micro))
     micro = [[[gen.bf16_normal(S, 1e-3, seed, gen.STREAM_GRAD, u, m, q) for q in range(world)]
@@ -84,13 +84,21 @@ def _units_case(fp, sizes, world, rank, n_micro, step, seed, flags, inf_unit=Non
     flag = torch.zeros(1, dtype=torch.int32, device=dev())
     sq = torch.zeros(1, dtype=torch.float64, device=dev()) if with_norm else None
     ws = plans[0].new_workspace() if with_norm else None
+    out = None
+    if out_of_place:
+        state0 = [t.clone() for t in state]
+        out = [torch.full((P,), 7.0, dtype=torch.float32, device=dev()) for _ in range(3)]
     for m in range(n_micro - 1):
         plans[m].reduce(acc, scale=float(scale), accumulate=m > 0, found_inf=flag)
     plans[-1].step(acc, *state, scale=float(scale), accumulate=n_micro > 1, step=step, found_inf=flag,
-                   sq_norm=sq, workspace=ws, flags=flags, **hp_kwargs(HP))
+                   sq_norm=sq, workspace=ws, flags=flags, out=out, **hp_kwargs(HP))
     torch.cuda.synchronize()
 
     assert int(flag.item()) == flag_o
+    if out_of_place:
+        for t, t0 in zip(state, state0):
+            assert torch.equal(t.view(torch.int32), t0.view(torch.int32)), "input state written"
+        state = out
     for u in range(U):
         got = [to_host(plans[0].unit_slice(t, u)) for t in state]
         if skip:
@@ -106,7 +114,7 @@ def _units_case(fp, sizes, world, rank, n_micro, step, seed, flags, inf_unit=Non
         mask = np.ones(world * S, bool)
         mask[own] = False
         assert_bf16_equal(fh[mask], full_o[u][mask], f"unit {u} other shards")
-        if flags & fp.FP_STEP_KEEP_GRAD or not flags & fp.FP_STEP_NO_SKIP:
+        if flags & fp.FP_STEP_KEEP_GRAD or not (flags & fp.FP_STEP_NO_SKIP or out_of_place):
             assert_f32_bitexact(to_host(plans[0].unit_slice(acc, u)), acc_o[u], f"unit {u} reduced gradient")
     if with_norm and np.isfinite(norm_o):
         assert float(sq.item()) == pytest.approx(norm_o, rel=1e-12)
@@ -182,3 +190,20 @@ def test_units_equal_buckets_with_a_tail(fp, tail):
     workgroup-to-unit mapping by division), at 16 ranks and 4 micro-batches."""
     say(f"units equal buckets tail={tail}")
     _units_case(fp, [20_480] * 5 + [tail], world=16, rank=0, n_micro=4, step=2, seed=21, flags=0)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2])
+@pytest.mark.parametrize("inf_unit", [None, 4])
+def test_units_speculative(fp, flags, inf_unit):
+    """Separate output partitions: the fused launch writes every unit's update
+    there, and with exact skip a last kernel restores the input state (and
+    recasts every own slice) on overflow; the input partitions are only read."""
+    say(f"units speculative flags={flags} inf_unit={inf_unit}")
+    _units_case(fp, [12, 0, 3, 2049, 20_480, 777], world=8, rank=5, n_micro=2, step=3, seed=31, flags=flags,
+                inf_unit=inf_unit, offset=1, out_of_place=True)
+
+
+def test_units_speculative_equal_buckets_16_ranks(fp):
+    say("units speculative: equal buckets, 16 ranks, 4 micro-batches")
+    _units_case(fp, [20_480] * 5 + [45_001], world=16, rank=0, n_micro=4, step=2, seed=22, flags=0,
+                out_of_place=True)
