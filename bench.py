@@ -374,7 +374,7 @@ def time_steps(w, K, W, timing, ev):
         timing = "eager" if a.elapsed_time(b) / 2 >= EAGER_MIN_MS else "graph"
         W += 2
 
-    def eager_pass(first, count, span=False):
+    def eager_pass(first, count):
         evs = [[ev.create() for _ in range(w.n_events())] for _ in range(count)]
         marks = [ev.create(), ev.create()]
         torch.cuda.synchronize()

@@ -294,6 +294,9 @@ def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_o
         assert path == fp.FP_PATH_NO_SKIP
     elif not workspace or flags & fp.FP_STEP_NO_COOP:
         assert path == fp.FP_PATH_TWO_PHASE
+    elif flags & fp.FP_STEP_KEEP_GRAD and n_micro > 1:
+        # the kept gradient would overwrite an input accumulator before the barrier
+        assert path == fp.FP_PATH_TWO_PHASE
     elif S <= 2_000_000:                  # far inside MI355X's co-resident capacity
         assert path == fp.FP_PATH_ONE_PASS
     call(step)
