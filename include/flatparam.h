@@ -407,6 +407,22 @@ fp_status fp_step_path(const fp_step_args* args, int32_t* path);
  * mid-generation: zero-fill the workspace before passing it to another call. */
 fp_status fp_step_test_give_up(const fp_step_args* args, void* stream);
 
+/* fp_shard_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same kernels and results as fp_shard_step with a workspace, but the
+ * step's scratch (the one-pass grid barrier's state and the norm partials)
+ * is a 2 MiB array inside the library, one per GPU, held until the process
+ * ends; the call allocates nothing.  args->workspace must be NULL
+ * (FP_ERR_INVALID otherwise).  With sq_norm, shards of more than
+ * 266,337,283 elements need more partials than the array holds:
+ * FP_ERR_RANGE before anything is enqueued.  The first call on a device
+ * takes the array's device address and enqueues a small kernel that clears
+ * the barrier state (again on later calls while that one was captured into
+ * a graph).  Every call on a GPU shares that GPU's array: calls that may
+ * overlap on one GPU (concurrent streams, graphs replayed concurrently)
+ * race and must not be issued. */
+fp_status fp_shard_step_noalloc(const fp_step_args* args, void* stream);
+
 /* ------------------------------------------------------------------ units */
 
 /* Many units (for example the ~25 MB DDP buckets of a model, or a model's

@@ -517,14 +517,20 @@ class ShardStep:
     the new state while master / exp_avg / exp_avg_sq are only read (the
     speculative step; the caller alternates two ShardStep objects whose
     input and output buffers are swapped).
+
+    library_scratch: call fp_shard_step_noalloc, whose scratch is an array
+    inside the library (workspace must then be None); for callers that
+    cannot allocate device memory.
     """
 
     def __init__(self, grads, acc, master, exp_avg, exp_avg_sq, shards, full, rank: int, *,
                  scale: float, lr, beta1, beta2, eps, weight_decay, found_inf,
                  accumulate: bool = False, sq_norm=None, workspace=None,
-                 flags: int = FP_STEP_EXACT_SKIP, grad_coef=None, out=None):
+                 flags: int = FP_STEP_EXACT_SKIP, grad_coef=None, out=None, library_scratch: bool = False):
         _one_device(grads, acc, master, exp_avg, exp_avg_sq, shards, full, found_inf, sq_norm, workspace,
                     grad_coef, out)
+        if library_scratch and workspace is not None:
+            raise ValueError("library_scratch uses the library's own scratch: pass no workspace")
         if out is not None and len(out) != 3:
             raise ValueError("out is (master_out, exp_avg_out, exp_avg_sq_out)")
         torch = _torch()
@@ -556,7 +562,7 @@ class ShardStep:
             a.exp_avg_sq_out = _f32(out[2], S, "exp_avg_sq_out")
         self._args = a
         self._device = master.device
-        self._fn = lib().fp_shard_step
+        self._fn = lib().fp_shard_step_noalloc if library_scratch else lib().fp_shard_step
 
     def __call__(self, step: int, profile_events=None):
         a = self._args

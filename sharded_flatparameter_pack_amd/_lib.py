@@ -79,6 +79,7 @@ SIGNATURES = {
     "fp_shard_step": (_i32, [C.POINTER(fp_step_args), _vp]),
     "fp_step_path": (_i32, [C.POINTER(fp_step_args), C.POINTER(C.c_int32)]),
     "fp_step_test_give_up": (_i32, [C.POINTER(fp_step_args), _vp]),
+    "fp_shard_step_noalloc": (_i32, [C.POINTER(fp_step_args), _vp]),
     "fp_units_create": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, C.POINTER(_vp)]),
     "fp_units_destroy": (None, [_vp]),
     "fp_units_info": (_i32, [_vp, _vp, _vp]),

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libflatparam.so")
 SOURCES = ["abi.hip", "step_kernels.hip", "unit_kernels.hip", "segment_kernels.hip",
-           "local_kernels.hip", "hybrid_kernels.hip"]
+           "local_kernels.hip", "hybrid_kernels.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",

@@ -732,8 +732,10 @@ extern "C" fp_status fp_step_path(const fp_step_args* args, int32_t* path) {
     return step_path(*args, path, &variant, &grid);
 }
 
-namespace {
-fp_status shard_step_impl(const fp_step_args* args, void* stream, bool give_up_test) {
+namespace fpk {
+fp_status report_error(fp_status status, const char* message) { return fail(status, "%s", message); }
+
+fp_status shard_step_run(const fp_step_args* args, void* stream, bool give_up_test) {
     if (args == nullptr) return fail(FP_ERR_INVALID, "args is NULL");
     const fp_step_args& x = *args;
     const int64_t S = x.shard;
@@ -861,14 +863,14 @@ fp_status shard_step_impl(const fp_step_args* args, void* stream, bool give_up_t
     if (ev[2] && (e = hipEventRecord(ev[2], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
     return FP_OK;
 }
-}  // namespace
+}  // namespace fpk
 
 extern "C" fp_status fp_shard_step(const fp_step_args* args, void* stream) {
-    return shard_step_impl(args, stream, false);
+    return shard_step_run(args, stream, false);
 }
 
 extern "C" fp_status fp_step_test_give_up(const fp_step_args* args, void* stream) {
-    return shard_step_impl(args, stream, true);
+    return shard_step_run(args, stream, true);
 }
 
 // ---------------------------------------------------------------------- units

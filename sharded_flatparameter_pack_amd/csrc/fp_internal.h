@@ -268,6 +268,12 @@ inline int64_t unit_tiles(int64_t S) {
     return t > 0 ? t : 1;
 }
 
+// Host helpers of the entry points (abi.hip): set the calling thread's
+// error message and return `status`; run fp_shard_step (give_up_test: the
+// one-pass kernel with a barrier that always gives up).
+fp_status report_error(fp_status status, const char* message);
+fp_status shard_step_run(const fp_step_args* args, void* stream, bool give_up_test);
+
 // Launchers (return the HIP error of the launch).
 // `aligned`: every bf16 quad stream of the launch (gradients, own shard) is
 // 8-byte aligned; `copy_aligned` (and `aligned` for fp_unshard's kernel):

@@ -308,6 +308,16 @@ def test_step_path_without_a_device(fp):
     assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == 0
     assert path.value == _lib.FP_PATH_TWO_PHASE
     a.accumulate = 0
+    # the entry point without allocation takes no workspace, and refuses a norm
+    # over more partials than its array holds, both before touching a device
+    assert _status(L.fp_shard_step_noalloc, C.byref(a), None) == -1
+    assert b"workspace must be NULL" in L.fp_last_error()
+    a.workspace, a.sq_norm, a.shard = None, 0xB000000, 266_337_284
+    assert L.fp_workspace_bytes(266_337_283) == 2 << 20 < L.fp_workspace_bytes(266_337_284)
+    assert _status(L.fp_shard_step_noalloc, C.byref(a), None) == -2
+    assert b"266337283" in L.fp_last_error()
+    assert _status(L.fp_shard_step_noalloc, None, None) == -1
+    a.sq_norm, a.shard = None, 16
     a.master = 0x4000010                       # overlaps acc
     assert _status(L.fp_step_path, C.byref(a), C.byref(path)) == -1
     assert _status(L.fp_step_path, C.byref(a), None) == -1
