@@ -79,9 +79,15 @@ def kernel_source_hash() -> str:
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch already loaded."""
 
+    # Timing-only events: no system-scope fence (cache write-back and
+    # invalidate) when an event is recorded, which would otherwise land inside
+    # the kernel spans that the events bracket.
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def __init__(self):
         self.L = C.CDLL("libamdhip64.so.7")
         self.L.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.L.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
         self.L.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.L.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.L.hipEventSynchronize.argtypes = [C.c_void_p]
@@ -89,8 +95,8 @@ class HipEvents:
 
     def create(self):
         e = C.c_void_p()
-        if self.L.hipEventCreate(C.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.L.hipEventCreateWithFlags(C.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         return e.value
 
     def record(self, e, stream):

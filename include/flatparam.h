@@ -572,9 +572,9 @@ fp_status fp_shard0_unpack(fp_shard0_plan* plan, int32_t elem_size, const void* 
 
 /* ------------------------------------------------------------------ reshard */
 
-/* Resharding a flat buffer from N to N' ranks: [DP] FSDP2 checkpoint
- * paragraphs (a sharded checkpoint may be loaded into a different number of
- * ranks).  The flat buffer of T elements is cut into N shards of
+/* Resharding a flat buffer from N to N' ranks: [DP] section
+ * "Checkpoint：让各张卡保存自己的分片" (a sharded checkpoint may be loaded
+ * into a different number of ranks).  The flat buffer of T elements is cut into N shards of
  * S = ceil(T / N) (old rank q holds flat[qS, (q+1)S), zeros past T) and is to
  * be cut into N' shards of S' = ceil(T / N').  New rank q' receives
  * flat[q'S' + k] for k < S', read from the old shards, and zeros past T

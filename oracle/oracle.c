@@ -234,9 +234,9 @@ void or_shard0_unpack(int32_t n, const int32_t* ndims, const int64_t* shapes,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Resharding a flat buffer from N to N' ranks.  [DP] FSDP2 checkpoint      */
-/* paragraphs: a sharded checkpoint may be loaded into a different number   */
-/* of ranks.  The flat buffer (T elements, then zero padding) is the same;  */
+/* Resharding a flat buffer from N to N' ranks.  [DP] section             */
+/* "Checkpoint：让各张卡保存自己的分片": a sharded checkpoint may be loaded  */
+/* into a different number of ranks.  The flat buffer (T elements, then zero padding) is the same;  */
 /* only the cut changes: new rank q' holds flat[q'S', (q'+1)S'), read from  */
 /* the old shards (old rank q holds flat[qS, (q+1)S)), zeros past T.        */
 /* new_rank = -1 writes every new rank's shard, one after the other.        */

@@ -254,17 +254,18 @@ def test_pack_worked_example_and_views(fp):
 
 
 # ------------------------------------------------------------------ whole step
-def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_off=0, workspace=True):
+def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_off=0, workspace=True,
+               grad_sigma=1e-3, master_sigma=0.02):
     hp = HP
     scale = np.float32(1.0 / (world * n_micro))
-    micro = [[gen.bf16_normal(S, 1e-3, seed, gen.STREAM_GRAD, 0, m, q) for q in range(world)]
+    micro = [[gen.bf16_normal(S, grad_sigma, seed, gen.STREAM_GRAD, 0, m, q) for q in range(world)]
              for m in range(n_micro)]
     if inf and S:
         micro[-1][world // 2][S // 2] = 0x7F80
-    th = gen.normal_f32(S, 0.02, seed, gen.STREAM_MASTER)
+    th = gen.normal_f32(S, master_sigma, seed, gen.STREAM_MASTER)
     m0 = gen.normal_f32(S, 1e-4, seed, gen.STREAM_EXP_AVG) if step > 1 else np.zeros(S, np.float32)
     v0 = (gen.normal_f32(S, 1e-3, seed, gen.STREAM_EXP_AVG_SQ) ** 2 if step > 1 else np.zeros(S, np.float32))
-    others = [gen.bf16_normal(S, 0.02, seed, gen.STREAM_SHARD, q) for q in range(world)]
+    others = [gen.bf16_normal(S, master_sigma, seed, gen.STREAM_SHARD, q) for q in range(world)]
 
     acc_o, th_o, m_o, v_o = np.zeros(S, np.float32), th.copy(), m0.copy(), v0.copy()
     full_o, flag_o, norm_o = oracle.shard_step(micro, acc_o, th_o, m_o, v_o, others, rank, hp=hp, step=step)
@@ -327,8 +328,12 @@ def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_o
 @pytest.mark.parametrize("rank", [0, 1])
 @pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 6])
 def test_step_worked_example(fp, rank, flags):
+    """The three (4, 2) weights over two ranks with the workload's own draws:
+    gradients and masters N(0, 1), one AdamW step."""
+    cfg = CONFIGS["c1_three_4x2_nd2"]
     say(f"step C1 rank={rank} flags={flags}")
-    _step_case(fp, world=2, S=12, rank=rank, n_micro=1, step=1, seed=0, flags=flags)
+    _step_case(fp, world=cfg.world, S=12, rank=rank, n_micro=cfg.n_micro, step=1, seed=cfg.seed, flags=flags,
+               grad_sigma=cfg.grad_sigma, master_sigma=cfg.master_sigma)
 
 
 @pytest.mark.parametrize("flags", [0, 4])

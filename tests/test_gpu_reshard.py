@@ -1,5 +1,5 @@
 """GPU parity of fp_reshard (a flat buffer cut into N shards recut into N'
-shards, "Infra: Data Parallel", FSDP2 checkpoint paragraphs) against the
+shards, "Infra: Data Parallel", section "Checkpoint：让各张卡保存自己的分片") against the
 oracle: byte equality, for bf16 and fp32 elements, every new rank at once
 and one rank at a time, odd element offsets, destinations pre-filled with
 garbage (the zeros past T must be written), old ranks that hold only

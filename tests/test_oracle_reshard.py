@@ -1,6 +1,6 @@
 """Pins of the oracle's N -> N' reshard of a flat buffer ("Infra: Data
-Parallel", FSDP2 checkpoint paragraphs: a sharded checkpoint can be loaded
-into a different number of ranks).
+Parallel", section "Checkpoint：让各张卡保存自己的分片": a sharded checkpoint
+can be loaded into a different number of ranks).
 
 * A hand-worked case (10 elements, 4 -> 3 ranks).
 * Resharding the shards of the pack oracle's FlatParameter for N ranks gives
