@@ -209,7 +209,7 @@ class SingleUnit:
             # (the speculative step's restore kernel runs between the second and third
             # event and returns at once without overflow)
             return [("step_phase1_kernel<true>", "step_phase1_fused", k1, S * B, 1)]
-        if self.path == fp.FP_PATH_ONE_PASS:
+        if self.path in (fp.FP_PATH_ONE_PASS, fp.FP_PATH_SPECULATIVE_ONE_PASS):
             return [("step_coop_kernel", "step_coop", k1, S * B, 1)]
         if self.path in (fp.FP_PATH_NO_SKIP_SPLIT, fp.FP_PATH_SPECULATIVE_SPLIT):
             # fused reduce + AdamW + cast, then the copies (and the restore kernel)
@@ -287,10 +287,10 @@ class Bucketed:
             elif "out" not in s:
                 P = s["plans"][0].partition
                 s["out"] = [torch.zeros(P, dtype=torch.float32, device=self.dev) for _ in range(3)]
-        if self.flags:
-            self.path = fp.FP_PATH_NO_SKIP
-        else:
-            self.path = fp.FP_PATH_SPECULATIVE if out_of_place else fp.FP_PATH_TWO_PHASE
+        s0 = self.sets[0]
+        self.path = s0["plans"][-1].step_path(s0["acc"], s0["master"], s0["exp_avg"], s0["exp_avg_sq"],
+                                              found_inf=s0["found_inf"], flags=self.flags,
+                                              out=s0.get("out"))
 
     def n_events(self):
         return self.n_micro + 2
@@ -321,6 +321,7 @@ class Bucketed:
                                profile_events=None if events is None else events[n - 1:n + 2])
 
     def kernels(self, ev_ms):
+        import sharded_flatparameter_pack_amd as fp
         S, N, n = self.S, self.world, self.n_micro
         d = [ev_ms[i + 1] - ev_ms[i] for i in range(n + 1)]
         out = []
@@ -329,7 +330,13 @@ class Bucketed:
             t_red = sum(d[:n - 1])
             alg_red = S * (2 * N * (n - 1) + 4 + 8 * (n - 2))   # the first writes acc, later ones read + write
             out.append(("units_reduce_kernel", "units_reduce", t_red / (n - 1), alg_red / (n - 1), n - 1))
-        if self.flags or self.out_of_place:
+        if self.path in (fp.FP_PATH_NO_SKIP_SPLIT, fp.FP_PATH_SPECULATIVE_SPLIT):
+            # fused reduce + AdamW + casts, then the copies (and the restore kernel,
+            # which returns at once without overflow)
+            out.append(("units_phase1_kernel<true>", "units_phase1_fused", d[n - 1],
+                        S * (2 * N + acc_in + 26), 1))
+            out.append(("units_copy_kernel", "units_copy", d[n], S * 4 * (N - 1), 1))
+        elif self.path != fp.FP_PATH_TWO_PHASE:
             # fused reduce + AdamW + casts + copies; the restore kernel (speculative)
             # follows between the last two events and returns at once without overflow
             out.append(("units_phase1_kernel<true>", "units_phase1_fused", d[n - 1],
@@ -754,7 +761,7 @@ def load_traffic(workload: str, kernel: str):
 
 # ------------------------------------------------------------------ main
 PATH_NAMES = {0: "one-pass", 1: "two-phase", 2: "fused-no-skip", 3: "fused-no-skip-split", 4: "speculative",
-              5: "speculative-split"}
+              5: "speculative-split", 6: "speculative-one-pass"}
 
 
 def kernel_lines(kernels):

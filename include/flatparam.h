@@ -357,7 +357,9 @@ typedef struct fp_step_args {
      * on overflow the outputs receive the unchanged input state (and full
      * the bf16 of the unchanged master), which is the skipped step's result;
      * the caller swaps input and output buffers after each step either way.
-     * With FP_STEP_NO_SKIP the outputs receive the update regardless. */
+     * With FP_STEP_NO_SKIP the outputs receive the update regardless.  A
+     * shard that fits the one-pass kernel (workspace given) takes it with
+     * the outputs as store targets (FP_PATH_SPECULATIVE_ONE_PASS). */
     float* master_out;
     float* exp_avg_out;
     float* exp_avg_sq_out;
@@ -388,6 +390,11 @@ fp_status fp_shard_step(const fp_step_args* args, void* stream);
  *                        step plus one small launch.
  *   FP_PATH_SPECULATIVE_SPLIT -- the same from 2^24 elements on, with the
  *                        kernels of FP_PATH_NO_SKIP_SPLIT.
+ *   FP_PATH_SPECULATIVE_ONE_PASS -- exact skip with separate output state
+ *                        on the one-pass kernel (when it fits, as for
+ *                        FP_PATH_ONE_PASS): after the barrier the kernel
+ *                        stores the new state to the outputs, or on overflow
+ *                        copies the input state to them; no restore launch.
  * The one-pass choice depends on the device's co-resident capacity, hence
  * on the device current at the call. */
 #define FP_PATH_ONE_PASS 0
@@ -396,15 +403,18 @@ fp_status fp_shard_step(const fp_step_args* args, void* stream);
 #define FP_PATH_NO_SKIP_SPLIT 3
 #define FP_PATH_SPECULATIVE 4
 #define FP_PATH_SPECULATIVE_SPLIT 5
+#define FP_PATH_SPECULATIVE_ONE_PASS 6
 fp_status fp_step_path(const fp_step_args* args, int32_t* path);
 
 /* For tests of the one-pass kernel's give-up path.  Runs fp_shard_step's
  * one-pass kernel (FP_ERR_INVALID unless fp_step_path would return
- * FP_PATH_ONE_PASS for these arguments) with a grid barrier that waits for
- * one workgroup more than the launch holds and gives up after 64 polls, so
- * every wait gives up and the kernel ends normally: the result is the
- * FP_FLAG_GAVE_UP outcome described above.  The barrier's counters are left
- * mid-generation: zero-fill the workspace before passing it to another call. */
+ * FP_PATH_ONE_PASS or FP_PATH_SPECULATIVE_ONE_PASS for these arguments)
+ * with a grid barrier that waits for one workgroup more than the launch
+ * holds and gives up after 64 polls, so every wait gives up and the kernel
+ * ends normally: the result is the FP_FLAG_GAVE_UP outcome described above
+ * (with output state buffers, the outputs are not written either).  The
+ * barrier's counters are left mid-generation: zero-fill the workspace
+ * before passing it to another call. */
 fp_status fp_step_test_give_up(const fp_step_args* args, void* stream);
 
 /* fp_shard_step for callers that cannot allocate device memory: code under
@@ -504,6 +514,15 @@ typedef struct fp_units_step_args {
     float* exp_avg_sq_out;
 } fp_units_step_args;
 fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream);
+
+/* The launches fp_units_step makes for these arguments, after the same
+ * argument checks (host only, nothing launched): FP_PATH_TWO_PHASE (exact
+ * skip in place), FP_PATH_NO_SKIP / FP_PATH_SPECULATIVE (one fused launch
+ * with the copies of the other shards, then for the speculative form the
+ * restore kernel), or FP_PATH_NO_SKIP_SPLIT / FP_PATH_SPECULATIVE_SPLIT for
+ * partitions of 2^24 elements and more: the fused reduce + AdamW + cast
+ * launch, then the copies in a launch of their own. */
+fp_status fp_units_step_path(const fp_units* units, const fp_units_step_args* args, int32_t* path);
 
 /* ------------------------------------------------------------------ dim-0 */
 

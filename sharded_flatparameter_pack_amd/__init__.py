@@ -21,7 +21,7 @@ from typing import Optional, Sequence
 
 from . import _lib
 from ._lib import (FP_MAX_WORLD, FP_PATH_NO_SKIP, FP_PATH_NO_SKIP_SPLIT, FP_PATH_ONE_PASS,  # noqa: F401
-                   FP_PATH_SPECULATIVE, FP_PATH_SPECULATIVE_SPLIT,
+                   FP_PATH_SPECULATIVE, FP_PATH_SPECULATIVE_ONE_PASS, FP_PATH_SPECULATIVE_SPLIT,
                    FP_PATH_TWO_PHASE, FP_STEP_EXACT_SKIP, FP_STEP_KEEP_GRAD, FP_STEP_NO_COOP,
                    FP_STEP_NO_SKIP, FP_FLAG_OVERFLOW, FP_FLAG_GAVE_UP, FlatParamError, check, lib)
 
@@ -29,7 +29,7 @@ __all__ = ["Plan", "Units", "Shard0Plan", "ReshardPlan", "reduce_shard_hybrid", 
            "workspace_bytes", "new_workspace", "workspace_timeouts", "FlatParamError", "FP_STEP_EXACT_SKIP",
            "FP_STEP_NO_SKIP", "FP_STEP_KEEP_GRAD", "FP_STEP_NO_COOP", "FP_PATH_ONE_PASS",
            "FP_PATH_TWO_PHASE", "FP_PATH_NO_SKIP", "FP_PATH_NO_SKIP_SPLIT", "FP_PATH_SPECULATIVE",
-           "FP_PATH_SPECULATIVE_SPLIT", "FP_FLAG_OVERFLOW", "FP_FLAG_GAVE_UP", "library_path"]
+           "FP_PATH_SPECULATIVE_SPLIT", "FP_PATH_SPECULATIVE_ONE_PASS", "FP_FLAG_OVERFLOW", "FP_FLAG_GAVE_UP", "library_path"]
 
 
 def library_path() -> str:
@@ -683,14 +683,8 @@ class Units:
             self._opt(workspace, torch.uint8, self.workspace_bytes, "workspace"), _stream(acc)))
         return acc
 
-    def step(self, acc, master, exp_avg, exp_avg_sq, *, scale: float, lr, beta1, beta2, eps,
-             weight_decay, step: int, found_inf, accumulate: bool = False, sq_norm=None,
-             workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None, grad_coef=None,
-             out=None):
-        """The last micro-batch's step over all units.  out: None (in place) or
-        (master_out, exp_avg_out, exp_avg_sq_out) partitions that receive the new
-        state while master / exp_avg / exp_avg_sq are only read (the speculative
-        step; the caller swaps the partitions after each step)."""
+    def _step_args(self, acc, master, exp_avg, exp_avg_sq, *, scale, lr, beta1, beta2, eps, weight_decay,
+                   step, found_inf, accumulate, sq_norm, workspace, flags, profile_events, grad_coef, out):
         _one_device(acc, master, exp_avg, exp_avg_sq, found_inf, sq_norm, workspace, grad_coef, out)
         if out is not None and len(out) != 3:
             raise ValueError("out is (master_out, exp_avg_out, exp_avg_sq_out)")
@@ -716,7 +710,32 @@ class Units:
                 raise ValueError(f"profile_events needs {_lib.FP_STEP_EVENTS} hipEvent_t handles")
             ev = (C.c_void_p * _lib.FP_STEP_EVENTS)(*profile_events)
             a.profile_events = C.cast(ev, C.c_void_p)
+        return a, ev
+
+    def step(self, acc, master, exp_avg, exp_avg_sq, *, scale: float, lr, beta1, beta2, eps,
+             weight_decay, step: int, found_inf, accumulate: bool = False, sq_norm=None,
+             workspace=None, flags: int = FP_STEP_EXACT_SKIP, profile_events=None, grad_coef=None,
+             out=None):
+        """The last micro-batch's step over all units.  out: None (in place) or
+        (master_out, exp_avg_out, exp_avg_sq_out) partitions that receive the new
+        state while master / exp_avg / exp_avg_sq are only read (the speculative
+        step; the caller swaps the partitions after each step)."""
+        a, _ev = self._step_args(acc, master, exp_avg, exp_avg_sq, scale=scale, lr=lr, beta1=beta1, beta2=beta2,
+                                 eps=eps, weight_decay=weight_decay, step=step, found_inf=found_inf,
+                                 accumulate=accumulate, sq_norm=sq_norm, workspace=workspace, flags=flags,
+                                 profile_events=profile_events, grad_coef=grad_coef, out=out)
         check(lib().fp_units_step(self._h, C.byref(a), _stream(master)))
+
+    def step_path(self, acc, master, exp_avg, exp_avg_sq, *, found_inf, flags: int = FP_STEP_EXACT_SKIP,
+                  out=None, sq_norm=None, workspace=None):
+        """One of the FP_PATH_* values: the launches step() makes with these buffers."""
+        a, _ev = self._step_args(acc, master, exp_avg, exp_avg_sq, scale=1.0, lr=1e-3, beta1=0.9, beta2=0.999,
+                                 eps=1e-8, weight_decay=0.0, step=1, found_inf=found_inf, accumulate=False,
+                                 sq_norm=sq_norm, workspace=workspace, flags=flags, profile_events=None,
+                                 grad_coef=None, out=out)
+        path = C.c_int32(-1)
+        check(lib().fp_units_step_path(self._h, C.byref(a), C.byref(path)))
+        return path.value
 
 
 # ------------------------------------------------------------------ helpers

@@ -30,6 +30,7 @@ FP_PATH_NO_SKIP = 2
 FP_PATH_NO_SKIP_SPLIT = 3
 FP_PATH_SPECULATIVE = 4
 FP_PATH_SPECULATIVE_SPLIT = 5
+FP_PATH_SPECULATIVE_ONE_PASS = 6
 FP_WORKSPACE_TIMEOUTS_OFFSET = 8320
 FP_FLAG_OVERFLOW = 1
 FP_FLAG_GAVE_UP = 2
@@ -86,6 +87,7 @@ SIGNATURES = {
     "fp_units_offsets": (_i32, [_vp, _vp]),
     "fp_units_reduce": (_i32, [_vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "fp_units_step": (_i32, [_vp, C.POINTER(fp_units_step_args), _vp]),
+    "fp_units_step_path": (_i32, [_vp, C.POINTER(fp_units_step_args), C.POINTER(C.c_int32)]),
     "fp_shard0_plan_create": (_i32, [_i32, _vp, _vp, _i32, C.POINTER(_vp)]),
     "fp_shard0_plan_destroy": (None, [_vp]),
     "fp_shard0_plan_info": (_i32, [_vp, _vp, _vp]),

@@ -705,10 +705,7 @@ fp_status step_path(const fp_step_args& x, int32_t* path, int* variant, int* gri
         *path = x.shard >= kSplitElems ? FP_PATH_NO_SKIP_SPLIT : FP_PATH_NO_SKIP;
         return FP_OK;
     }
-    if (x.master_out != nullptr) {
-        *path = x.shard >= kSplitElems ? FP_PATH_SPECULATIVE_SPLIT : FP_PATH_SPECULATIVE;
-        return FP_OK;
-    }
+    const bool out_of_place = x.master_out != nullptr;
     // The one-pass kernel writes a kept gradient before its barrier, so it is
     // not used when acc is also an input (a cancelled barrier must leave acc
     // as it was).
@@ -717,7 +714,13 @@ fp_status step_path(const fp_step_args& x, int32_t* path, int* variant, int* gri
         const hipError_t e = plan_step_coop(x.shard, variant, grid);
         if (e != hipSuccess) return device_fail(e, "occupancy query");
     }
-    *path = *variant >= 0 ? FP_PATH_ONE_PASS : FP_PATH_TWO_PHASE;
+    if (*variant >= 0) {
+        *path = out_of_place ? FP_PATH_SPECULATIVE_ONE_PASS : FP_PATH_ONE_PASS;
+    } else if (out_of_place) {
+        *path = x.shard >= kSplitElems ? FP_PATH_SPECULATIVE_SPLIT : FP_PATH_SPECULATIVE;
+    } else {
+        *path = FP_PATH_TWO_PHASE;
+    }
     return FP_OK;
 }
 
@@ -746,8 +749,8 @@ fp_status shard_step_run(const fp_step_args* args, void* stream, bool give_up_te
     int32_t path = 0;
     int variant = -1, grid = 0;
     if ((st = step_path(x, &path, &variant, &grid)) != FP_OK) return st;
-    if (give_up_test && path != FP_PATH_ONE_PASS)
-        return fail(FP_ERR_INVALID, "these arguments do not take the one-pass path");
+    const bool one_pass = path == FP_PATH_ONE_PASS || path == FP_PATH_SPECULATIVE_ONE_PASS;
+    if (give_up_test && !one_pass) return fail(FP_ERR_INVALID, "these arguments do not take the one-pass path");
 
     const bool speculative = path == FP_PATH_SPECULATIVE || path == FP_PATH_SPECULATIVE_SPLIT;
     // the fused launch(es) without a gate: no-skip, and speculative (gate after)
@@ -791,7 +794,7 @@ fp_status shard_step_run(const fp_step_args* args, void* stream, bool give_up_te
         for (int i = 0; i < FP_STEP_EVENTS; ++i) ev[i] = static_cast<hipEvent_t>(x.profile_events[i]);
     hipError_t e;
 
-    if (path == FP_PATH_ONE_PASS) {
+    if (one_pass) {
         if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
         if ((e = launch_step_coop(a, variant, grid, aligned, copy_aligned, s, give_up_test)) != hipSuccess)
             return device_fail(e, "one-pass step launch");
@@ -1130,15 +1133,14 @@ extern "C" fp_status fp_units_reduce(const fp_units* units, float scale, int32_t
     return FP_OK;
 }
 
-extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream) {
-    if (units == nullptr || args == nullptr) return fail(FP_ERR_INVALID, "units or args is NULL");
-    const fp_units_step_args& x = *args;
+namespace {
+// Every check of fp_units_step's arguments; fills the launch arguments.
+fp_status check_units_step(const fp_units* units, const fp_units_step_args& x, UnitsArgs* a) {
     if (!units->has_unshard) return fail(FP_ERR_INVALID, "units plan has no shards / full buffers");
     if (x.flags & ~(FP_STEP_NO_SKIP | FP_STEP_KEEP_GRAD)) return fail(FP_ERR_INVALID, "unknown flags");
-    UnitsArgs a;
-    fill_units_args(units, &a);
+    fill_units_args(units, a);
     fp_status st;
-    if ((st = check_hparams(&x.hp, &a.c)) != FP_OK) return st;
+    if ((st = check_hparams(&x.hp, &a->c)) != FP_OK) return st;
     const int n_out = (x.master_out != nullptr) + (x.exp_avg_out != nullptr) + (x.exp_avg_sq_out != nullptr);
     if (n_out != 0 && n_out != 3)
         return fail(FP_ERR_INVALID, "master_out / exp_avg_out / exp_avg_sq_out: give all three or none");
@@ -1153,23 +1155,57 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
         if (!aligned(x.workspace, 16)) return fail(FP_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
     if (x.grad_coef != nullptr && !aligned(x.grad_coef, 8)) return fail(FP_ERR_ALIGN, "grad_coef misaligned");
+    a->g_coef = x.grad_coef;
+    a->master_out = x.master_out;
+    a->exp_avg_out = x.exp_avg_out;
+    a->exp_avg_sq_out = x.exp_avg_sq_out;
+    a->acc = x.acc;
+    a->master = x.master;
+    a->exp_avg = x.exp_avg;
+    a->exp_avg_sq = x.exp_avg_sq;
+    a->found_inf = x.found_inf;
+    a->partials = x.sq_norm != nullptr ? partials_of(x.workspace) : nullptr;
+    a->scale = x.scale;
+    a->accumulate = x.accumulate ? 1 : 0;
+    a->keep_grad = (x.flags & FP_STEP_KEEP_GRAD) ? 1 : 0;
+    return FP_OK;
+}
+
+// The launches of a validated multi-unit step: FP_PATH_TWO_PHASE, or the
+// fused launch without a gate -- no-skip, or speculative (gate after) --
+// whose copies go to a launch of their own for partitions of kSplitElems
+// elements and more (measured at the bucketed 611M model: 1.58 ms per step
+// with the copies in the fused launch, 1.55 ms split).
+int32_t units_path(const fp_units* u, const fp_units_step_args& x) {
+    const bool speculative = x.master_out != nullptr && !(x.flags & FP_STEP_NO_SKIP);
+    if (!speculative && !(x.flags & FP_STEP_NO_SKIP)) return FP_PATH_TWO_PHASE;
+    const bool split = u->partition >= kSplitElems && u->copy_groups > 0;
+    if (speculative) return split ? FP_PATH_SPECULATIVE_SPLIT : FP_PATH_SPECULATIVE;
+    return split ? FP_PATH_NO_SKIP_SPLIT : FP_PATH_NO_SKIP;
+}
+}  // namespace
+
+extern "C" fp_status fp_units_step_path(const fp_units* units, const fp_units_step_args* args, int32_t* path) {
+    if (units == nullptr || args == nullptr || path == nullptr)
+        return fail(FP_ERR_INVALID, "units, args or path is NULL");
+    UnitsArgs a;
+    fp_status st = check_units_step(units, *args, &a);
+    if (st != FP_OK) return st;
+    *path = units_path(units, *args);
+    return FP_OK;
+}
+
+extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_args* args, void* stream) {
+    if (units == nullptr || args == nullptr) return fail(FP_ERR_INVALID, "units or args is NULL");
+    const fp_units_step_args& x = *args;
+    UnitsArgs a;
+    fp_status st = check_units_step(units, x, &a);
+    if (st != FP_OK) return st;
     if ((st = check_units_device(units)) != FP_OK) return st;
-    const bool speculative = n_out == 3 && !(x.flags & FP_STEP_NO_SKIP);
-    // the fused launch without a gate: no-skip, and speculative (gate after)
-    const bool no_skip = (x.flags & FP_STEP_NO_SKIP) != 0 || speculative;
-    a.g_coef = x.grad_coef;
-    a.master_out = x.master_out;
-    a.exp_avg_out = x.exp_avg_out;
-    a.exp_avg_sq_out = x.exp_avg_sq_out;
-    a.acc = x.acc;
-    a.master = x.master;
-    a.exp_avg = x.exp_avg;
-    a.exp_avg_sq = x.exp_avg_sq;
-    a.found_inf = x.found_inf;
-    a.partials = x.sq_norm != nullptr ? partials_of(x.workspace) : nullptr;
-    a.scale = x.scale;
-    a.accumulate = x.accumulate ? 1 : 0;
-    a.keep_grad = (x.flags & FP_STEP_KEEP_GRAD) ? 1 : 0;
+    const int32_t path = units_path(units, x);
+    const bool speculative = path == FP_PATH_SPECULATIVE || path == FP_PATH_SPECULATIVE_SPLIT;
+    const bool split = path == FP_PATH_SPECULATIVE_SPLIT || path == FP_PATH_NO_SKIP_SPLIT;
+    const bool no_skip = path != FP_PATH_TWO_PHASE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t ev[FP_STEP_EVENTS] = {nullptr, nullptr, nullptr};
@@ -1177,9 +1213,16 @@ extern "C" fp_status fp_units_step(const fp_units* units, const fp_units_step_ar
         for (int i = 0; i < FP_STEP_EVENTS; ++i) ev[i] = static_cast<hipEvent_t>(x.profile_events[i]);
     hipError_t e;
     if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
-    if ((e = launch_units_phase1(a, units->copy_groups, no_skip, units->aligned, units->copy_aligned, s)) != hipSuccess)
+    // The split launch's reduce + AdamW workgroups keep full occupancy: at the
+    // bucketed 611M model's 16 ranks (38.2M-element partition) the occupancy
+    // cap that serves the single-unit step made them slower (MI355X: 612 us
+    // capped at four workgroups per CU, 517 us at five, 445 us uncapped).
+    if ((e = launch_units_phase1(a, split ? 0 : units->copy_groups, no_skip, false, units->aligned,
+                                 units->copy_aligned, s)) != hipSuccess)
         return device_fail(e, "units step launch");
     if (ev[1] && (e = hipEventRecord(ev[1], s)) != hipSuccess) return device_fail(e, "hipEventRecord");
+    if (split && (e = launch_units_copy(a, units->copy_groups, units->copy_aligned, s)) != hipSuccess)
+        return device_fail(e, "units copy launch");
     if (no_skip) {
         if (x.sq_norm != nullptr &&
             (e = launch_norm_finalize(a.partials, (int)units->reduce_groups, x.sq_norm, s)) != hipSuccess)

@@ -301,8 +301,11 @@ hipError_t launch_step_resolve(const ResolveArgs& r, hipStream_t s);
 // other shards (copy_groups workgroups after the reduce tiles); AdamW over
 // all units.
 hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s);
-hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update,
+// `capped`: only the reduce tiles (copy_groups = 0), at the occupancy cap.
+hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update, bool capped,
                                bool aligned, bool copy_aligned, hipStream_t s);
+// The copy workgroups of a units launch in a launch of their own.
+hipError_t launch_units_copy(const UnitsArgs& a, int64_t copy_groups, bool copy_aligned, hipStream_t s);
 hipError_t launch_units_adamw(const UnitsArgs& a, bool aligned, hipStream_t s);
 // The speculative multi-unit step's last kernel: on overflow, every unit's
 // output state takes its input state and its own slice the bf16 cast.

@@ -88,7 +88,11 @@ __global__ __launch_bounds__(kThreads) void step_resolve_kernel(const ResolveArg
 // and bit 1 is OR-ed into the flag.  The flag is only ever OR-ed into.
 // Workgroups past reduce_groups copy the other ranks' shards meanwhile and
 // take no part in the barrier.  The reduced gradient never leaves the
-// registers, so the step moves exactly the algorithmic bytes.
+// registers, so the step moves exactly the algorithmic bytes.  With separate
+// output state (state_out differs from the input), the new state goes to
+// the outputs, and on overflow the outputs receive the input state, read
+// again after the barrier (the skipped step's result, with no restore
+// launch).
 template <bool kAligned, bool kCopyAligned, int kQ>
 __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     FP_PHASE_MARK(0);
@@ -169,18 +173,30 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
     }
     const bool skip = decision == kBarrierOverflow;
     if (skip && blockIdx.x == 0 && threadIdx.x == 0) flag_or(a.found_inf, 1);
+    const StateOut o = state_out(a);
+    const bool out_of_place = o.master != a.master;
 
-    // commit: stores only
+    // commit: stores only (and on an overflowed out-of-place step, the copy
+    // of the input state)
     if (nq > 0) {
 #pragma unroll
         for (int u = 0; u < kQ; ++u) {
             if (!Q.ok[u]) continue;
             if (skip) {
                 st_bf16q<kAligned>(own, Q, u, old_bf16[u]);
+                if (out_of_place) {
+                    float f[4];
+                    ld_f32q(a.master, Q, u, f);
+                    st_f32q(o.master, Q, u, f);
+                    ld_f32q(a.exp_avg, Q, u, f);
+                    st_f32q(o.exp_avg, Q, u, f);
+                    ld_f32q(a.exp_avg_sq, Q, u, f);
+                    st_f32q(o.exp_avg_sq, Q, u, f);
+                }
             } else {
-                st_f32q(a.master, Q, u, st.th[u]);
-                st_f32q(a.exp_avg, Q, u, st.m[u]);
-                st_f32q(a.exp_avg_sq, Q, u, st.v[u]);
+                st_f32q(o.master, Q, u, st.th[u]);
+                st_f32q(o.exp_avg, Q, u, st.m[u]);
+                st_f32q(o.exp_avg_sq, Q, u, st.v[u]);
                 st_bf16q<kAligned>(own, Q, u, f32x4_to_bf16(st.th[u]));
             }
         }
@@ -189,10 +205,15 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
         const int64_t j = tail0 + threadIdx.x;
         if (skip) {
             own[j] = (uint16_t)bf16x2(told, 0.0f);
+            if (out_of_place) {
+                o.master[j] = told;
+                o.exp_avg[j] = a.exp_avg[j];
+                o.exp_avg_sq[j] = a.exp_avg_sq[j];
+            }
         } else {
-            a.master[j] = tt;
-            a.exp_avg[j] = tm;
-            a.exp_avg_sq[j] = tv;
+            o.master[j] = tt;
+            o.exp_avg[j] = tm;
+            o.exp_avg_sq[j] = tv;
             own[j] = (uint16_t)bf16x2(tt, 0.0f);
         }
     }

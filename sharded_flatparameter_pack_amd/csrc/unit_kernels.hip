@@ -111,6 +111,16 @@ __global__ __launch_bounds__(kThreads) void units_phase1_kernel(const UnitsArgs 
                                            a.partials != nullptr ? a.partials + blockIdx.x : nullptr);
 }
 
+// The copies of every unit's other shards in a launch of their own (the
+// split form of the fused step): copy workgroup g is workgroup
+// reduce_groups + g of the combined launch's numbering.
+template <bool kCopyAligned>
+__global__ __launch_bounds__(kThreads) void units_copy_kernel(const UnitsArgs a) {
+    const int64_t group = a.reduce_groups + (int64_t)blockIdx.x;
+    const UnitView v = unit_view(a, group);
+    copy_role<kCopyAligned, kCopyWordsStream>(v, (unsigned)((int64_t)blockIdx.x - v.copy0));
+}
+
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void units_adamw_kernel(const UnitsArgs a) {
     if (a.sq_norm != nullptr && blockIdx.x == 0)
@@ -149,15 +159,15 @@ void units_reduce_launch(const UnitsArgs& a, dim3 g, hipStream_t s) {
 }
 
 template <bool kAligned, bool kCopyAligned, bool kFused>
-void units_phase1_launch(const UnitsArgs& a, dim3 g, hipStream_t s) {
-    if (wide_group(a.world)) units_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, 0, s>>>(a);
-    else units_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, 0, s>>>(a);
+void units_phase1_launch(const UnitsArgs& a, dim3 g, unsigned lds, hipStream_t s) {
+    if (wide_group(a.world)) units_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, lds, s>>>(a);
+    else units_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, lds, s>>>(a);
 }
 
 template <bool kAligned, bool kCopyAligned>
-void units_phase1_launch(const UnitsArgs& a, dim3 g, bool fused, hipStream_t s) {
-    if (fused) units_phase1_launch<kAligned, kCopyAligned, true>(a, g, s);
-    else units_phase1_launch<kAligned, kCopyAligned, false>(a, g, s);
+void units_phase1_launch(const UnitsArgs& a, dim3 g, bool fused, unsigned lds, hipStream_t s) {
+    if (fused) units_phase1_launch<kAligned, kCopyAligned, true>(a, g, lds, s);
+    else units_phase1_launch<kAligned, kCopyAligned, false>(a, g, lds, s);
 }
 }  // namespace
 
@@ -176,16 +186,24 @@ hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s) 
     return hipGetLastError();
 }
 
-hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update,
+hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update, bool capped,
                                bool aligned, bool copy_aligned, hipStream_t s) {
     const dim3 g((unsigned)(a.reduce_groups + copy_groups));
+    const unsigned lds = capped ? kCapLds : 0u;
     if (aligned) {
-        if (copy_aligned) units_phase1_launch<true, true>(a, g, fused_update, s);
-        else units_phase1_launch<true, false>(a, g, fused_update, s);
+        if (copy_aligned) units_phase1_launch<true, true>(a, g, fused_update, lds, s);
+        else units_phase1_launch<true, false>(a, g, fused_update, lds, s);
     } else {
-        if (copy_aligned) units_phase1_launch<false, true>(a, g, fused_update, s);
-        else units_phase1_launch<false, false>(a, g, fused_update, s);
+        if (copy_aligned) units_phase1_launch<false, true>(a, g, fused_update, lds, s);
+        else units_phase1_launch<false, false>(a, g, fused_update, lds, s);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_units_copy(const UnitsArgs& a, int64_t copy_groups, bool copy_aligned, hipStream_t s) {
+    const dim3 g((unsigned)copy_groups);
+    if (copy_aligned) units_copy_kernel<true><<<g, kThreads, 0, s>>>(a);
+    else units_copy_kernel<false><<<g, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -114,5 +114,13 @@ def assert_bf16_equal(got: np.ndarray, want: np.ndarray, what: str = ""):
                              f"first at {i}: got {got[i]:#06x} want {want[i]:#06x}")
 
 
+def norm_rel_tol(n: int) -> float:
+    """Relative tolerance of a GPU sum of n squares against the oracle's serial
+    fp64 sum: each order's rounding error is below n * 2^-53 of the sum of
+    non-negative terms (recursive summation bound), so the two differ by at
+    most twice that (floored at 1e-12)."""
+    return max(1e-12, 2.0 * n * 2.0 ** -53)
+
+
 def hp_kwargs(hp):
     return dict(lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps, weight_decay=hp.weight_decay)

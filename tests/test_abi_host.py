@@ -338,10 +338,11 @@ def test_step_path_without_a_device(fp):
 
 
 def test_speculative_step_path_and_checks(fp):
-    """With output state buffers, the exact-skip step takes the speculative
-    paths (split from 2^24 elements on) and the no-skip step writes the
-    outputs; the output buffers come as all three or none, and may overlap
-    no other buffer of the call."""
+    """With output state buffers and no workspace (so no one-pass kernel, whose
+    choice needs the device's occupancy), the exact-skip step takes the
+    speculative paths (split from 2^24 elements on) and the no-skip step
+    writes the outputs; the output buffers come as all three or none, and
+    may overlap no other buffer of the call."""
     from sharded_flatparameter_pack_amd import _lib
     L = fp.lib()
     step = 1 << 40
@@ -352,7 +353,7 @@ def test_speculative_step_path_and_checks(fp):
     a.grads, a.shards = C.cast(grads, C.c_void_p), C.cast(shards, C.c_void_p)
     a.acc, a.master, a.exp_avg, a.exp_avg_sq = 4 * step, 5 * step, 6 * step, 7 * step
     a.hp = _lib.fp_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
-    a.full, a.found_inf, a.workspace = 8 * step, 9 * step, 10 * step
+    a.full, a.found_inf, a.workspace = 8 * step, 9 * step, None
     a.master_out, a.exp_avg_out, a.exp_avg_sq_out = 11 * step, 12 * step, 13 * step
     path = C.c_int32(-1)
     for S, spec, nsk in ((1 << 24, _lib.FP_PATH_SPECULATIVE_SPLIT, _lib.FP_PATH_NO_SKIP_SPLIT),

@@ -51,9 +51,14 @@ def _bucketed(n_sets=2):
     w = bench.Bucketed.__new__(bench.Bucketed)
     w.cfg, w.rank, w.world, w.n_micro, w.dev = cfg, 0, cfg.world, cfg.n_micro, "cpu"
     w.S, w.n_sets = 64, n_sets
-    plan = types.SimpleNamespace(partition=64)
+    def step_path(*args, flags=0, out=None, **kw):
+        if flags & fp.FP_STEP_NO_SKIP:
+            return fp.FP_PATH_NO_SKIP_SPLIT
+        return fp.FP_PATH_SPECULATIVE_SPLIT if out is not None else fp.FP_PATH_TWO_PHASE
+
+    plan = types.SimpleNamespace(partition=64, step_path=step_path)
     w.sets = [dict(plans=[plan] * cfg.n_micro, master=torch.zeros(64), exp_avg=torch.zeros(64),
-                   exp_avg_sq=torch.zeros(64)) for _ in range(n_sets)]
+                   exp_avg_sq=torch.zeros(64), acc=None, found_inf=None) for _ in range(n_sets)]
     return w
 
 
@@ -105,10 +110,12 @@ def test_single_unit_kernel_bytes_add_up(monkeypatch, path):
     assert ks[0][2] == 1.0
 
 
-@pytest.mark.parametrize("flags,oop", [(0, False), (fp.FP_STEP_NO_SKIP, False), (0, True)])
-def test_bucketed_kernel_bytes_add_up(flags, oop):
+@pytest.mark.parametrize("path", [fp.FP_PATH_TWO_PHASE, fp.FP_PATH_NO_SKIP, fp.FP_PATH_NO_SKIP_SPLIT,
+                                  fp.FP_PATH_SPECULATIVE, fp.FP_PATH_SPECULATIVE_SPLIT])
+def test_bucketed_kernel_bytes_add_up(path):
     w = _bucketed()
-    w.set_flags(flags, oop)
+    w.set_flags(0, path in (fp.FP_PATH_SPECULATIVE, fp.FP_PATH_SPECULATIVE_SPLIT))
+    w.path = path
     n = w.n_micro
     ks = w.kernels(_ev([0.25] * (n - 1) + [0.6, 0.2]))
     B = bench.step_bytes_per_elem(w.world, n)

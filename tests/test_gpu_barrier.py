@@ -58,10 +58,10 @@ class OnePass:
         self.flag = torch.zeros(1, dtype=torch.int32, device=dev())
         self.ws = fp.new_workspace(dev(), S)
 
-    def call(self, flags=0):
+    def call(self, flags=0, out=None):
         return self.fp.ShardStep(self.grads, self.acc, *self.state, self.shards, self.full, self.rank,
                                  scale=1.0 / self.world, found_inf=self.flag, workspace=self.ws, flags=flags,
-                                 **hp_kwargs(HP))
+                                 out=out, **hp_kwargs(HP))
 
     def oracle_step(self, step):
         h = self.host
@@ -117,6 +117,39 @@ def test_give_up_stores_nothing_and_keeps_the_flag(fp, prior, keep_grad):
         for t, w, name in zip(c.state, state_o, ("master", "exp_avg", "exp_avg_sq")):
             assert_f32_close(to_host(t), w, name)
         assert_bf16_within_1ulp(to_host(c.own()), full_o[own], "own shard")
+
+
+@pytest.mark.parametrize("inject", [False, True])
+def test_speculative_one_pass_give_up_and_decisions(fp, inject):
+    """The one-pass kernel with separate output state: a give-up writes neither
+    the inputs nor the outputs; run normally, the outputs get the update, or
+    on overflow the input state, and the inputs stay untouched."""
+    say(f"speculative one-pass: give-up, then a normal call (overflow {inject})")
+    c = OnePass(fp, S=90_001, seed=44, inf_at=777 if inject else None)
+    out = [torch.full((c.S,), CANARY_F32, dtype=torch.float32, device=dev()) for _ in range(3)]
+    step = c.call(out=out)
+    assert step.path() == fp.FP_PATH_SPECULATIVE_ONE_PASS
+    step.test_give_up(3)
+    torch.cuda.synchronize()
+    assert int(c.flag.item()) == fp.FP_FLAG_GAVE_UP
+    assert all(bool((t == CANARY_F32).all()) for t in out), "outputs written by a cancelled step"
+    assert bool((c.own() == CANARY_BF16).all())
+    c.flag.zero_()
+    c.ws.zero_()
+    step(3)
+    torch.cuda.synchronize()
+    assert int(c.flag.item()) == int(inject)
+    for t, t0 in zip(c.state, c.state0):
+        assert torch.equal(_bits(t), _bits(t0)), "input state written"
+    acc_o, state_o, full_o, flag_o = c.oracle_step(3)
+    assert flag_o == int(inject)
+    for t, w, name in zip(out, state_o, ("master", "exp_avg", "exp_avg_sq")):
+        if inject:
+            assert_f32_bitexact(to_host(t), w, f"{name} of a skipped step")
+        else:
+            assert_f32_close(to_host(t), w, name)
+    own = slice(c.rank * c.S, (c.rank + 1) * c.S)
+    assert_bf16_within_1ulp(to_host(c.own()), full_o[own], "own shard")
 
 
 @pytest.mark.parametrize("prior", [2, 3])

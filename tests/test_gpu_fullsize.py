@@ -51,6 +51,7 @@ def test_611m_buckets_as_benchmarked(fp, mode, inject):
     rank, N, n = cfg.ranks[0], cfg.world, cfg.n_micro
     say(f"611M buckets as benchmarked: mode={mode} inject={inject}")
     w = bench.Bucketed(cfg, rank, dev(), flags, oop, n_sets=1)
+    assert w.path == (fp.FP_PATH_SPECULATIVE_SPLIT if oop else fp.FP_PATH_TWO_PHASE)
     s = w.sets[0]
     sizes, offs = w.sizes, w.offsets
     assert len(sizes) == 47 and sizes[:46] == [819_200] * 46 and sizes[46] == 504_300

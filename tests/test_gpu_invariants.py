@@ -295,9 +295,10 @@ def test_split_no_skip_step_at_large_shards(fp, world, rank, full_off):
 @pytest.mark.parametrize("world,S,rank,full_off,overflow", [(3, 300_001, 1, 1, False), (8, 4_099, 7, 0, True),
                                                             (1, 7, 0, 3, True), (8, (1 << 24) + 1, 2, 1, True)])
 def test_speculative_step_writes_only_its_outputs(fp, world, S, rank, full_off, overflow):
-    """The speculative step (separate output state) writes only the output
-    state, full and the flag / norm, leaves its input state unchanged, and
-    ends bitwise where the in-place two-phase step does, overflowed or not."""
+    """The speculative step (separate output state), on the one-pass kernel and
+    as the fused pass plus restore kernel, writes only the output state, full
+    and the flag / norm, leaves its input state unchanged, and ends bitwise
+    where the in-place two-phase step does, overflowed or not."""
     say(f"speculative guard bands: world={world} S={S} rank={rank} full offset={full_off} overflow={overflow}")
     grads = [gen.torch_bf16_normal(S, 1e-3, 75, (gen.STREAM_GRAD, q), dev()) for q in range(world)]
     if overflow:
@@ -308,7 +309,12 @@ def test_speculative_step_writes_only_its_outputs(fp, world, S, rank, full_off, 
             gen.torch_normal_f32(S, 1e-4, 75, (gen.STREAM_EXP_AVG,), dev()),
             gen.torch_normal_f32(S, 1e-3, 75, (gen.STREAM_EXP_AVG_SQ,), dev()).square()]
     results = {}
-    for name in ("speculative", "two-phase"):
+    fused = fp.FP_PATH_SPECULATIVE_SPLIT if S >= 1 << 24 else fp.FP_PATH_SPECULATIVE
+    modes = {"speculative-one-pass": (fp.FP_STEP_EXACT_SKIP, fp.FP_PATH_SPECULATIVE_ONE_PASS if S <= 2_000_000
+                                      else fused),
+             "speculative": (fp.FP_STEP_EXACT_SKIP | fp.FP_STEP_NO_COOP, fused),
+             "two-phase": (fp.FP_STEP_NO_COOP, fp.FP_PATH_TWO_PHASE)}
+    for name, (flags, want_path) in modes.items():
         st = [Guarded(S, torch.float32, init=t) for t in init]
         out = [Guarded(S, torch.float32, init=torch.full((S,), 5.0, device=dev())) for _ in range(3)]
         b = dict(acc=Guarded(S, torch.float32), full=Guarded(world * S, torch.int16, off=full_off),
@@ -316,13 +322,11 @@ def test_speculative_step_writes_only_its_outputs(fp, world, S, rank, full_off, 
                  flag=Guarded(1, torch.int32, init=torch.zeros(1, dtype=torch.int32, device=dev())))
         ws = Guarded(fp.workspace_bytes(S), torch.uint8,
                      init=torch.zeros(fp.workspace_bytes(S), dtype=torch.uint8, device=dev()))
-        spec = name == "speculative"
+        spec = name != "two-phase"
         call = fp.ShardStep(grads, b["acc"].view, *[g.view for g in st], shards, b["full"].view, rank,
                             scale=1.0 / world, found_inf=b["flag"].view, sq_norm=b["sq"].view, workspace=ws.view,
-                            flags=fp.FP_STEP_EXACT_SKIP if spec else fp.FP_STEP_NO_COOP,
-                            out=[g.view for g in out] if spec else None, **hp_kwargs(HP))
-        assert call.path() == ((fp.FP_PATH_SPECULATIVE_SPLIT if S >= 1 << 24 else fp.FP_PATH_SPECULATIVE)
-                               if spec else fp.FP_PATH_TWO_PHASE)
+                            flags=flags, out=[g.view for g in out] if spec else None, **hp_kwargs(HP))
+        assert call.path() == want_path
         call(3)
         _check(*st, *out, *b.values(), ws)
         assert int(b["flag"].view.item()) == (1 if overflow else 0)
@@ -332,5 +336,6 @@ def test_speculative_step_writes_only_its_outputs(fp, world, S, rank, full_off, 
         results[name] = [g.view.clone() for g in (out if spec else st)] + [b["full"].view.clone()]
         del st, out, b, ws, call
         torch.cuda.empty_cache()
-    for i, (x, y) in enumerate(zip(results["speculative"], results["two-phase"])):
-        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"buffer {i} differs"
+    for name in ("speculative-one-pass", "speculative"):
+        for i, (x, y) in enumerate(zip(results[name], results["two-phase"])):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"{name}: buffer {i} differs"

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from gpu_common import (assert_bf16_equal, assert_bf16_within_1ulp, assert_f32_bitexact,
-                        assert_f32_close, dev, hp_kwargs, say, to_dev, to_host)
+                        assert_f32_close, dev, hp_kwargs, say, to_dev, to_host, norm_rel_tol)
 from workloads import CONFIGS, gen
 from workloads.configs import AdamW
 
@@ -319,7 +319,7 @@ def _step_case(fp, world, S, rank, n_micro, step, seed, flags, inf=False, grad_o
     if flags & fp.FP_STEP_KEEP_GRAD:
         assert_f32_bitexact(to_host(acc), acc_o, "kept gradient")
     if workspace and math.isfinite(norm_o):
-        assert float(sq.item()) == pytest.approx(norm_o, rel=1e-12)
+        assert float(sq.item()) == pytest.approx(norm_o, rel=norm_rel_tol(S))
     if workspace:
         assert fp.workspace_timeouts(ws) == 0, "grid barrier wait gave up"
     return full_h

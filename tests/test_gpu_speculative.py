@@ -2,7 +2,8 @@
 
 The fused pass stores the update to the output buffers without waiting for
 the overflow check, and a last kernel restores the input state into them on
-overflow.  Its results must equal, bit for bit, those of the in-place
+overflow; a shard that fits the one-pass kernel takes it instead, with the
+outputs as store targets and the input state copied to them on overflow.  Its results must equal, bit for bit, those of the in-place
 two-phase exact-skip step on the same inputs (the same per-element
 arithmetic), with the input buffers left untouched:
 * finite gradients, shards from 1 element to a few tiles with a ragged tail,
@@ -94,9 +95,13 @@ def _keep_fp(fp):
 
 
 def _run_pair(fp, case, step, inject=None, preset_flag=False):
-    """The speculative and the in-place two-phase step on the same inputs."""
+    """The speculative step in its two forms -- on the one-pass kernel (when the
+    shard fits it) and as the fused pass plus the restore kernel -- and the
+    in-place two-phase step, on the same inputs."""
     res = {}
-    for name, spec in (("spec", True), ("two", False)):
+    for name, spec, flags in (("spec1", True, fp.FP_STEP_EXACT_SKIP),
+                              ("spec", True, fp.FP_STEP_EXACT_SKIP | fp.FP_STEP_NO_COOP),
+                              ("two", False, fp.FP_STEP_NO_COOP)):
         b = case.buffers()
         accumulate = False
         if preset_flag:
@@ -108,38 +113,47 @@ def _run_pair(fp, case, step, inject=None, preset_flag=False):
             q, j = inject
             keep = case.grads[q][j].clone()
             case.grads[q][j] = 0x7F80
-        call = case.call(b, fp.FP_STEP_EXACT_SKIP if spec else fp.FP_STEP_NO_COOP, spec, step,
-                         accumulate=accumulate)
-        want_path = ((fp.FP_PATH_SPECULATIVE_SPLIT if case.S >= 1 << 24 else fp.FP_PATH_SPECULATIVE) if spec
-                     else fp.FP_PATH_TWO_PHASE)
-        assert call.path() == want_path
+        call = case.call(b, flags, spec, step, accumulate=accumulate)
+        fused = fp.FP_PATH_SPECULATIVE_SPLIT if case.S >= 1 << 24 else fp.FP_PATH_SPECULATIVE
+        path = call.path()
+        if name == "spec1":
+            if case.S <= 2_000_000:               # far inside MI355X's co-resident capacity
+                assert path == fp.FP_PATH_SPECULATIVE_ONE_PASS
+            else:
+                assert path in (fp.FP_PATH_SPECULATIVE_ONE_PASS, fused)
+        else:
+            assert path == (fused if spec else fp.FP_PATH_TWO_PHASE)
         call(step)
         torch.cuda.synchronize()
         if inject is not None:
             case.grads[q][j] = keep
         res[name] = b
         assert fp.workspace_timeouts(b["ws"]) == 0
-    return res["spec"], res["two"]
+    return res
 
 
-def _check_pair(case, spec, two, overflow):
+def _check_pair(case, res, overflow):
     S = case.S
-    for i, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
-        _same(spec["state"][i][:S], case.state0[i][:S], f"input {name} untouched")
-        _same(spec["out"][i][:S], two["state"][i][:S], f"out {name} = two-phase {name}")
-        if overflow:
-            _same(spec["out"][i][:S], case.state0[i][:S], f"out {name} = input on overflow")
-    _same(spec["full"], two["full"], "full")
-    assert int(spec["flag"].item()) == int(two["flag"].item()) == (1 if overflow else 0)
-    assert float(spec["sq"].item()) == pytest.approx(float(two["sq"].item()), rel=1e-12, nan_ok=True)
+    two = res["two"]
+    for key in ("spec1", "spec"):
+        spec = res[key]
+        for i, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
+            _same(spec["state"][i][:S], case.state0[i][:S], f"{key}: input {name} untouched")
+            _same(spec["out"][i][:S], two["state"][i][:S], f"{key}: out {name} = two-phase {name}")
+            if overflow:
+                _same(spec["out"][i][:S], case.state0[i][:S], f"{key}: out {name} = input on overflow")
+        _same(spec["full"], two["full"], f"{key}: full")
+        assert int(spec["flag"].item()) == int(two["flag"].item()) == (1 if overflow else 0)
+        assert float(spec["sq"].item()) == pytest.approx(float(two["sq"].item()), rel=1e-12, nan_ok=True)
 
 
 @pytest.mark.parametrize("world,S,rank", [(1, 1, 0), (3, 5, 2), (8, 4099, 1), (8, 1_574_531, 6), (3, 300_001, 0)])
 def test_speculative_matches_two_phase_and_oracle(fp, world, S, rank):
     say(f"speculative step: world={world} S={S} rank={rank}")
     case = Case(world, S, rank, seed=80 + S % 97)
-    spec, two = _run_pair(fp, case, step=3)
-    _check_pair(case, spec, two, overflow=False)
+    res = _run_pair(fp, case, step=3)
+    _check_pair(case, res, overflow=False)
+    spec = res["spec1"]
     if S <= 300_001:
         h = case.host
         acc_o = np.zeros(S, np.float32)
@@ -161,12 +175,12 @@ def test_speculative_overflow_restores_state(fp, world, S, rank, where):
     say(f"speculative step overflow ({where} micro-batch): world={world} S={S} rank={rank}")
     case = Case(world, S, rank, seed=90 + S % 89)
     if where == "this":
-        spec, two = _run_pair(fp, case, step=2, inject=(world - 1, S - 1))
+        res = _run_pair(fp, case, step=2, inject=(world - 1, S - 1))
     else:
-        spec, two = _run_pair(fp, case, step=2, preset_flag=True)
-    _check_pair(case, spec, two, overflow=True)
+        res = _run_pair(fp, case, step=2, preset_flag=True)
+    _check_pair(case, res, overflow=True)
     # the own shard holds bf16 of the unchanged master
-    own = to_host(spec["full"][rank * S:(rank + 1) * S])
+    own = to_host(res["spec1"]["full"][rank * S:(rank + 1) * S])
     assert_bf16_equal(own, oracle.f32_to_bf16(to_host(case.state0[0][:S])), "own shard")
 
 
@@ -175,9 +189,9 @@ def test_speculative_split_at_large_shards(fp, inject):
     world, S, rank = 8, (1 << 24) + 3, 4
     say(f"speculative split step: world={world} S={S} inject={inject}")
     case = Case(world, S, rank, seed=71, on_device=True)
-    spec, two = _run_pair(fp, case, step=4, inject=inject)
-    _check_pair(case, spec, two, overflow=inject is not None)
-    del spec, two
+    res = _run_pair(fp, case, step=4, inject=inject)
+    _check_pair(case, res, overflow=inject is not None)
+    del res
     torch.cuda.empty_cache()
 
 

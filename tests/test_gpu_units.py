@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from gpu_common import (assert_bf16_equal, assert_bf16_within_1ulp, assert_f32_bitexact,
-                        assert_f32_close, dev, hp_kwargs, say, to_dev, to_host)
+                        assert_f32_close, dev, hp_kwargs, say, to_dev, to_host, norm_rel_tol)
 from workloads import gen
 from workloads.configs import AdamW
 
@@ -34,7 +34,7 @@ def _rows(host_rows, offset):
 
 
 def _units_case(fp, sizes, world, rank, n_micro, step, seed, flags, inf_unit=None, offset=0,
-                with_norm=True, out_of_place=False):
+                with_norm=True, out_of_place=False, want_path=None):
     U = len(sizes)
     scale = np.float32(1.0 / (world * n_micro))
     micro = [[[gen.bf16_normal(S, 1e-3, seed, gen.STREAM_GRAD, u, m, q) for q in range(world)]
@@ -88,6 +88,9 @@ def _units_case(fp, sizes, world, rank, n_micro, step, seed, flags, inf_unit=Non
     if out_of_place:
         state0 = [t.clone() for t in state]
         out = [torch.full((P,), 7.0, dtype=torch.float32, device=dev()) for _ in range(3)]
+    if want_path is not None:
+        assert plans[-1].step_path(acc, *state, found_inf=flag, flags=flags, out=out, sq_norm=sq,
+                                   workspace=ws) == want_path
     for m in range(n_micro - 1):
         plans[m].reduce(acc, scale=float(scale), accumulate=m > 0, found_inf=flag)
     plans[-1].step(acc, *state, scale=float(scale), accumulate=n_micro > 1, step=step, found_inf=flag,
@@ -117,7 +120,7 @@ def _units_case(fp, sizes, world, rank, n_micro, step, seed, flags, inf_unit=Non
         if flags & fp.FP_STEP_KEEP_GRAD or not (flags & fp.FP_STEP_NO_SKIP or out_of_place):
             assert_f32_bitexact(to_host(plans[0].unit_slice(acc, u)), acc_o[u], f"unit {u} reduced gradient")
     if with_norm and np.isfinite(norm_o):
-        assert float(sq.item()) == pytest.approx(norm_o, rel=1e-12)
+        assert float(sq.item()) == pytest.approx(norm_o, rel=norm_rel_tol(sum(sizes)))
     for p in plans:
         p.close()
 
@@ -207,3 +210,18 @@ def test_units_speculative_equal_buckets_16_ranks(fp):
     say("units speculative: equal buckets, 16 ranks, 4 micro-batches")
     _units_case(fp, [20_480] * 5 + [45_001], world=16, rank=0, n_micro=4, step=2, seed=22, flags=0,
                 out_of_place=True)
+
+
+@pytest.mark.parametrize("mode", ["noskip", "speculative", "speculative_overflow"])
+def test_units_split_launch(fp, mode):
+    """Partitions of 2^24 elements and more: the fused reduce + AdamW launch and
+    the copies of every unit's other shards in a launch of their own (odd unit
+    sizes, so copy sources and units start off the 16-byte grid)."""
+    say(f"units split launch: {mode}")
+    sizes = [8_388_613, 8_388_611, 1001]
+    if mode == "noskip":
+        _units_case(fp, sizes, world=3, rank=1, n_micro=1, step=2, seed=41, flags=fp.FP_STEP_NO_SKIP,
+                    want_path=fp.FP_PATH_NO_SKIP_SPLIT)
+    else:
+        _units_case(fp, sizes, world=3, rank=1, n_micro=2, step=2, seed=42, flags=0, out_of_place=True,
+                    inf_unit=1 if mode == "speculative_overflow" else None, want_path=fp.FP_PATH_SPECULATIVE_SPLIT)

@@ -25,7 +25,7 @@ import torch
 
 import oracle
 from gpu_common import (assert_bf16_equal, assert_bf16_within_1ulp, assert_f32_bitexact,
-                        assert_f32_close, dev, hp_kwargs, say, to_dev, to_host)
+                        assert_f32_close, dev, hp_kwargs, say, to_dev, to_host, norm_rel_tol)
 from workloads import CONFIGS, gen
 
 pytestmark = pytest.mark.gpu
@@ -94,7 +94,7 @@ def test_layer_d1024_full_shard_three_steps(fp, rank, flags):
         mask = np.ones(world * S, bool)
         mask[own] = False
         assert_bf16_equal(fh[mask], full_o[mask], "other shards")
-        assert float(sq.item()) == pytest.approx(norm_o, rel=1e-12)
+        assert float(sq.item()) == pytest.approx(norm_o, rel=norm_rel_tol(S))
     assert fp.workspace_timeouts(ws) == 0
 
 
@@ -207,7 +207,7 @@ def test_layer_d12288_shard(fp):
     assert torch.equal(own, _torch_cast(th))
     assert torch.equal(full[S:], others[S:])                      # rank 0: every other shard
     norm = float(acc.double().square().sum().item())
-    assert float(sq.item()) == pytest.approx(norm, rel=1e-12)
+    assert float(sq.item()) == pytest.approx(norm, rel=norm_rel_tol(S))
 
 
 def test_layer_d12288_pack(fp):
