@@ -455,10 +455,16 @@ def time_steps(w, K, W, timing, ev):
                              "steps_per_replay": n, "tail_steps": rem}
     del graphs, main, tail
     _, ev_ms = eager_pass(W + K, min(K, 200))
+    # An eager step of a short shard is host-bound: the GPU waits between the
+    # library's events, so the eager per-kernel split is scaled to the graph's
+    # step time (for a one-kernel step, its kernel time is the step time).
+    span = ev_ms[-1]
+    if span > 0:
+        ev_ms = [x * step_ms / span for x in ev_ms]
     return step_ms, ev_ms, ("HIP graphs of one step per buffer set (and of the K mod sets remaining steps), "
                             "replayed for exactly K steps; span timed by hipEvents on the replay stream; "
-                            "per-kernel times from the library's hipEvents in an eager pass of min(K, 200) "
-                            "steps")
+                            "per-kernel split from the library's hipEvents in an eager pass of min(K, 200) "
+                            "steps, scaled to the graph's step time")
 
 
 def measure(w, K, W, timing, ev, B):
@@ -771,13 +777,14 @@ def kernel_lines(kernels):
 
 def summary(cfg, w, mode, r, B):
     """The figures of one timed run, for the `configs` and `modes` entries."""
-    name, _, dur_ms, alg = r["dominant"]
+    name, kernel_id, dur_ms, alg = r["dominant"]
     kgbs = alg / (dur_ms * 1e-3) / 1e9
     return {"mode": mode, "path": PATH_NAMES[w.path], "ms_per_step": round(r["step_ms"], 5),
             "GBps": round(r["gbs"], 2), "frac_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4),
             "params_per_s": round(w.S / (r["step_ms"] * 1e-3), 1),
             "dominant_kernel": {"name": name, "avg_us": round(dur_ms * 1e3, 3), "alg_bytes": alg,
-                                "alg_GBps": round(kgbs, 1), "frac": round(kgbs / HBM_PEAK_GBS, 4)}}
+                                "alg_GBps": round(kgbs, 1), "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                                "traffic": load_traffic(cfg.name, kernel_id)}}
 
 
 def side_config(name, K, W, timing, ev, dev):
