@@ -258,7 +258,8 @@ struct UnitsArgs {
 };
 
 // Ranks reduced per group of loads in flight: 16 when more than 8 ranks
-// contribute (one round trip for up to 16 ranks), else 8.
+// contribute (one round trip for up to 16 ranks), else 8.  The fused
+// reduce + AdamW launches always take 8.
 inline bool wide_group(int world) { return world > 8; }
 
 // Reduce / AdamW workgroups of one unit: at least one, so that its tail

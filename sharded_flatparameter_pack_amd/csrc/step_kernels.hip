@@ -273,9 +273,12 @@ hipError_t launch_unshard(const UnshardArgs& a, int64_t grid_x, bool aligned, hi
 }
 
 namespace {
+// The fused reduce + AdamW keeps 8 ranks' loads in flight per round trip
+// whatever the group size: with 16 it ran slower at 64 ranks (the 10k-tensor
+// group's fused launch 1175 -> 1141 us with 8) and no faster at 16.
 template <bool kAligned, bool kCopyAligned, bool kFused>
 void phase1_launch(const StepArgs& a, dim3 g, unsigned lds, hipStream_t s) {
-    if (wide_group(a.world)) step_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, lds, s>>>(a);
+    if (wide_group(a.world) && !kFused) step_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, lds, s>>>(a);
     else step_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, lds, s>>>(a);
 }
 
