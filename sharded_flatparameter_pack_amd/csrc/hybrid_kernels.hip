@@ -34,13 +34,7 @@ __device__ __forceinline__ void sum_ranks(const HybridArgs& a, const Quads<kU>& 
     int j0 = 0;                      // position in its group of rank q0
     for (int q0 = 0; q0 < world; q0 += kG) {
         uint2 w[kG][kU];
-#pragma unroll
-        for (int k = 0; k < kG; ++k) {
-            if (q0 + k < world) {
-#pragma unroll
-                for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(a.grads[q0 + k], Q, u);
-            }
-        }
+        load_group<kAligned, kG, kU, false>(a.grads, q0, world, Q, w);
         int j = j0;
 #pragma unroll
         for (int k = 0; k < kG; ++k) {

@@ -28,6 +28,9 @@
 // IEEE round-to-nearest-even operation, in the order written.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "fp_device.h"
 
 namespace fpk {
@@ -129,18 +132,52 @@ __device__ __forceinline__ uint4 ld_bf16_word(const uint16_t* base, int64_t word
 // groups of ranks, at the price of the registers that hold them).  "Infra:
 // Data Parallel", ZeRO-1/ZeRO-2 paragraphs (reduce-scatter with averaging);
 // "4.1 数据并行详解" section 2 (average of the local gradients).
+//
+// The gradient quads of ranks [q0, q0 + kG) below world.  From a table in
+// device memory (a multi-unit plan's unit record, kTable), a whole group
+// reads all its row pointers before its first gradient load, so that the
+// group's loads leave back to back; read inside the per-rank condition,
+// each pointer's scalar load was waited for before its rank's load was
+// issued (measured on MI355X: the bucketed 611M model's fused multi-unit
+// launch 436 -> 391 us).  From kernel arguments the per-rank form stays:
+// there the hoisted form raised the one-pass kernel's registers (86 -> 108
+// VGPRs, a smaller co-resident grid) and slowed the 64-rank fused launch.
+template <bool kAligned, int kG, int kU, bool kTable, class P>
+__device__ __forceinline__ void load_group(const P& grads, int q0, int world, const Quads<kU>& Q,
+                                           uint2 w[kG][kU]) {
+    if (kTable && q0 + kG <= world) {
+        const uint16_t* p[kG];
+#pragma unroll
+        for (int k = 0; k < kG; ++k) p[k] = grads[q0 + k];
+#pragma unroll
+        for (int k = 0; k < kG; ++k) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(p[k], Q, u);
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < kG; ++k) {
+        if (q0 + k < world) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(grads[q0 + k], Q, u);
+        }
+    }
+}
+
+// Whether a stream view's gradient row pointers sit in device memory (a
+// pointer to a table) rather than in the kernel arguments (an array).
+template <class A>
+constexpr bool grads_in_table() {
+    return std::is_pointer<std::remove_reference_t<decltype(std::declval<A>().grads)>>::value;
+}
+
 template <bool kAligned, int kG, int kU, class A>
 __device__ __forceinline__ void sum_ranks(const A& a, const Quads<kU>& Q, float s[kU][4]) {
     const int world = a.world;
     for (int q0 = 0; q0 < world; q0 += kG) {
         uint2 w[kG][kU];
-#pragma unroll
-        for (int k = 0; k < kG; ++k) {
-            if (q0 + k < world) {
-#pragma unroll
-                for (int u = 0; u < kU; ++u) w[k][u] = ld_bf16q<kAligned>(a.grads[q0 + k], Q, u);
-            }
-        }
+        load_group<kAligned, kG, kU, grads_in_table<A>()>(a.grads, q0, world, Q, w);
 #pragma unroll
         for (int k = 0; k < kG; ++k) {
             if (q0 + k < world) {
