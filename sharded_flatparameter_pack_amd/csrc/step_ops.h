@@ -139,13 +139,16 @@ __device__ __forceinline__ uint4 ld_bf16_word(const uint16_t* base, int64_t word
 // group's loads leave back to back; read inside the per-rank condition,
 // each pointer's scalar load was waited for before its rank's load was
 // issued (measured on MI355X: the bucketed 611M model's fused multi-unit
-// launch 436 -> 391 us).  From kernel arguments the per-rank form stays:
+// launch 436 -> 391 us).  Groups of 16 keep the per-rank form: sixteen
+// held pointers raised their multi-unit kernels from 48 to 78 VGPRs (six
+// workgroups per SIMD instead of eight) and slowed the in-place multi-unit
+// reduce 658 -> 766 us.  From kernel arguments the per-rank form stays too:
 // there the hoisted form raised the one-pass kernel's registers (86 -> 108
 // VGPRs, a smaller co-resident grid) and slowed the 64-rank fused launch.
 template <bool kAligned, int kG, int kU, bool kTable, class P>
 __device__ __forceinline__ void load_group(const P& grads, int q0, int world, const Quads<kU>& Q,
                                            uint2 w[kG][kU]) {
-    if (kTable && q0 + kG <= world) {
+    if (kTable && kG <= 8 && q0 + kG <= world) {
         const uint16_t* p[kG];
 #pragma unroll
         for (int k = 0; k < kG; ++k) p[k] = grads[q0 + k];
