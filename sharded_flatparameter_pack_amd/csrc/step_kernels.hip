@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void unshard_kernel(const UnshardArgs a) 
     const uint16_t* src = a.shards[q];
     if (src == nullptr) return;
     const ShardSpan sp = shard_span(a.full, a.shard, q);
-    copy_tile<kAligned, kCopyWordsStream>(src, a.full, sp, blockIdx.x);
+    copy_tile<kAligned, kCopyWordsStream, false>(src, a.full, sp, blockIdx.x);
     if (blockIdx.x == 0) unshard_edges(src, a.full, a.shard, q, threadIdx.x, kThreads);
 }
 
