@@ -158,12 +158,16 @@ void units_reduce_launch(const UnitsArgs& a, dim3 g, hipStream_t s) {
     else units_reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, 0, s>>>(a);
 }
 
-// As in the single-unit step, the fused launch keeps 8 ranks' loads in
-// flight per round trip (the bucketed 611M model at 16 ranks: 453 -> 436 us).
+// The last micro-batch's launch keeps 8 ranks' loads in flight per round
+// trip whatever the group size, each group's row pointers read up front.
+// Measured on MI355X at the bucketed 611M model (16 ranks): the fused launch
+// 453 -> 436 us, the two-phase launch with its copies 641 -> 618 us (groups
+// of 16 read their pointers rank by rank: sixteen held pointers cost
+// occupancy).  The reduce-only launch keeps groups of 16 (245 us against
+// 248 with 8).
 template <bool kAligned, bool kCopyAligned, bool kFused>
 void units_phase1_launch(const UnitsArgs& a, dim3 g, unsigned lds, hipStream_t s) {
-    if (wide_group(a.world) && !kFused) units_phase1_kernel<kAligned, kCopyAligned, kFused, 16><<<g, kThreads, lds, s>>>(a);
-    else units_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, lds, s>>>(a);
+    units_phase1_kernel<kAligned, kCopyAligned, kFused, 8><<<g, kThreads, lds, s>>>(a);
 }
 
 template <bool kAligned, bool kCopyAligned>
