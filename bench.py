@@ -692,15 +692,34 @@ def copy_calibration(fp, dev, launches: int) -> int:
     return 0
 
 
+def cpu_model_from_lscpu(text: str) -> str:
+    """The model name in lscpu's output.  A name without a model number (a
+    virtual machine's "AMD EPYC") gets lscpu's family / model / stepping and the
+    hypervisor, which identify the part."""
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    name = fields.get("Model name", "")
+    if name and not any(c.isdigit() for c in name):
+        ids = [f"{k.lower()} {fields[k]}" for k in ("CPU family", "Model", "Stepping") if fields.get(k)]
+        if fields.get("Hypervisor vendor"):
+            ids.append(f"{fields['Hypervisor vendor']} guest")
+        if ids:
+            name = f"{name} ({', '.join(ids)})"
+    return name
+
+
 def cpu_model() -> str:
     """The host CPU's model name as lscpu reports it, else /proc/cpuinfo's, else
     the machine type."""
     import subprocess
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
-        for line in out.splitlines():
-            if line.strip().startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+        name = cpu_model_from_lscpu(out)
+        if name:
+            return name
     except (OSError, subprocess.SubprocessError):
         pass
     try:

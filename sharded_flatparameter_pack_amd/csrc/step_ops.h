@@ -141,8 +141,8 @@ __device__ __forceinline__ uint4 ld_bf16_word(const uint16_t* base, int64_t word
 // issued (measured on MI355X: the bucketed 611M model's fused multi-unit
 // launch 436 -> 391 us).  Groups of 16 keep the per-rank form: sixteen
 // held pointers raised their multi-unit kernels from 48 to 78 VGPRs (six
-// workgroups per SIMD instead of eight) and slowed the in-place multi-unit
-// reduce 658 -> 766 us.  From kernel arguments the per-rank form stays too:
+// workgroups per SIMD instead of eight) and slowed the two-phase
+// multi-unit launch at 16 ranks 658 -> 766 us.  From kernel arguments the per-rank form stays too:
 // there the hoisted form raised the one-pass kernel's registers (86 -> 108
 // VGPRs, a smaller co-resident grid) and slowed the 64-rank fused launch.
 template <bool kAligned, int kG, int kU, bool kTable, class P>

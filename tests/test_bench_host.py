@@ -8,7 +8,9 @@
   count the same bytes;
 * the speculative modes alternate input and output state from step to step
   on each buffer set;
-* --gpus above 1 is refused with a message.
+* --gpus above 1 is refused with a message;
+* the CPU baseline names the host CPU: lscpu's model name, with family /
+  model / stepping where the name carries no model number.
 """
 
 import types
@@ -125,3 +127,27 @@ def test_bucketed_kernel_bytes_add_up(path):
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU only" in capsys.readouterr().err
+
+
+_LSCPU_VM = """Architecture:                            x86_64
+Vendor ID:                               AuthenticAMD
+Model name:                              AMD EPYC
+CPU family:                              26
+Model:                                   2
+Thread(s) per core:                      1
+Stepping:                                1
+Hypervisor vendor:                       KVM
+"""
+
+_LSCPU_HOST = """Architecture:            x86_64
+Model name:              Intel(R) Xeon(R) Processor @ 2.70GHz
+CPU family:              6
+Model:                   143
+Stepping:                8
+"""
+
+
+def test_cpu_model_names_the_part():
+    assert bench.cpu_model_from_lscpu(_LSCPU_VM) == "AMD EPYC (cpu family 26, model 2, stepping 1, KVM guest)"
+    assert bench.cpu_model_from_lscpu(_LSCPU_HOST) == "Intel(R) Xeon(R) Processor @ 2.70GHz"
+    assert bench.cpu_model_from_lscpu("") == ""
