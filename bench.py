@@ -657,10 +657,14 @@ def reshard_bench(cfg, dev, reps: int):
     return res
 
 
+COPY_REFERENCE_SHARD = 64 * 1024 * 1024   # 16 shards: 2 GiB read and 2 GiB written per copy
+
+
 def copy_reference(fp, dev, reps: int = 20):
-    """Measured plain-copy bandwidth (fp_unshard of 16 x 8M bf16 shards, 256 MiB each way)."""
+    """Measured plain-copy bandwidth (fp_unshard of 16 x 64M bf16 shards, 2 GiB each
+    way: large enough that launch and drain cost under 1 % of a copy)."""
     import torch
-    world, S = 16, 8 * 1024 * 1024
+    world, S = 16, COPY_REFERENCE_SHARD
     src = torch.ones(world * S, dtype=torch.int16, device=dev)
     full = torch.zeros(world * S, dtype=torch.int16, device=dev)
     shards = [src[q * S:(q + 1) * S] for q in range(world)]
@@ -968,8 +972,9 @@ def main(argv=None) -> int:
         result["configs"] = configs
     if not args.no_extras:
         copy_gbs = copy_reference(fp, dev)
-        result["copy_reference"] = {"GBps": copy_gbs, "what": "fp_unshard of 16 x 8M bf16 shards "
-                                    "(256 MiB read + 256 MiB written): the plain-copy rate on this GPU",
+        torch.cuda.empty_cache()
+        result["copy_reference"] = {"GBps": copy_gbs, "what": "fp_unshard of 16 x 64M bf16 shards "
+                                    "(2 GiB read + 2 GiB written): the plain-copy rate on this GPU",
                                     "value_over_copy": round(gbs / copy_gbs, 4)}
         if cfg.shapes is not None:
             result["pack"] = pack_bench(cfg, dev, 20)
