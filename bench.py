@@ -875,7 +875,7 @@ def main(argv=None) -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the N_d ranks of the shard "
-              f"step are buffers on that GPU; there is no multi-GPU path in this build.", file=sys.stderr)
+              f"step are buffers on that GPU, and the library has no multi-GPU path.", file=sys.stderr)
         return 2
     if args.steps < 1:
         print("--steps must be at least 1", file=sys.stderr)
