@@ -1126,7 +1126,7 @@ extern "C" fp_status fp_units_reduce(const fp_units* units, float scale, int32_t
     a.scale = scale;
     a.accumulate = accumulate ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_units_reduce(a, units->aligned, s);
+    hipError_t e = launch_units_reduce(a, units->aligned, units->partition >= kSplitElems, s);
     if (e != hipSuccess) return device_fail(e, "units reduce launch");
     if (sq_norm != nullptr && (e = launch_norm_finalize(a.partials, (int)units->reduce_groups, sq_norm, s)) != hipSuccess)
         return device_fail(e, "norm launch");

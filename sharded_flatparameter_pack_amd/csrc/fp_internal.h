@@ -45,6 +45,13 @@ constexpr int kMaxCoopQuads = 4;       // quads a lane keeps in registers in the
 constexpr int64_t kCapElems = (int64_t)1 << 26;
 constexpr unsigned kCapLds = 40u << 10;
 inline unsigned capped_lds(int64_t shard) { return shard >= kCapElems ? kCapLds : 0u; }
+// The multi-unit reduce (16 ranks' loads per round trip, row pointers from
+// the unit records) of partitions from kSplitElems elements on runs with at
+// most three workgroups per CU.  Measured on MI355X at the bucketed 611M
+// model (16 ranks, 38.2M elements): 245 us at full occupancy, 241 at four
+// workgroups per CU, 233 at three, 241 at two.  The single-unit kernels
+// gained nothing from three over four.
+constexpr unsigned kUnitsReduceCapLds = 53504u;
 // The fused no-skip step of shards from kSplitElems elements on runs its
 // reduce + AdamW workgroups under the same cap and the copies of the other
 // shards in a launch of their own (measured: the d=12288 layer at 8 ranks
@@ -301,7 +308,7 @@ hipError_t launch_step_resolve(const ResolveArgs& r, hipStream_t s);
 // micro-batch's reduce (+ AdamW when fused) with the copies of all units'
 // other shards (copy_groups workgroups after the reduce tiles); AdamW over
 // all units.
-hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s);
+hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, bool capped, hipStream_t s);
 // `capped`: only the reduce tiles (copy_groups = 0), at the occupancy cap.
 hipError_t launch_units_phase1(const UnitsArgs& a, int64_t copy_groups, bool fused_update, bool capped,
                                bool aligned, bool copy_aligned, hipStream_t s);

@@ -153,9 +153,9 @@ __global__ __launch_bounds__(kThreads) void units_resolve_kernel(const UnitsArgs
 
 namespace {
 template <bool kAligned, bool kAcc, bool kNorm>
-void units_reduce_launch(const UnitsArgs& a, dim3 g, hipStream_t s) {
-    if (wide_group(a.world)) units_reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, 0, s>>>(a);
-    else units_reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, 0, s>>>(a);
+void units_reduce_launch(const UnitsArgs& a, dim3 g, unsigned lds, hipStream_t s) {
+    if (wide_group(a.world)) units_reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, lds, s>>>(a);
+    else units_reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, lds, s>>>(a);
 }
 
 // The last micro-batch's launch keeps 8 ranks' loads in flight per round
@@ -177,10 +177,11 @@ void units_phase1_launch(const UnitsArgs& a, dim3 g, bool fused, unsigned lds, h
 }
 }  // namespace
 
-hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, hipStream_t s) {
+hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, bool capped, hipStream_t s) {
     const bool norm = a.partials != nullptr, acc = a.accumulate != 0;
     const dim3 g((unsigned)a.reduce_groups);
-#define FP_UREDUCE(AL, AC, NO) units_reduce_launch<AL, AC, NO>(a, g, s)
+    const unsigned lds = capped ? kUnitsReduceCapLds : 0u;
+#define FP_UREDUCE(AL, AC, NO) units_reduce_launch<AL, AC, NO>(a, g, lds, s)
     if (aligned) {
         if (acc) { if (norm) FP_UREDUCE(true, true, true); else FP_UREDUCE(true, true, false); }
         else { if (norm) FP_UREDUCE(true, false, true); else FP_UREDUCE(true, false, false); }
