@@ -32,10 +32,11 @@ constexpr int kCopyWordsStream = 1;
 constexpr int kCopyWordsCoop = 4;
 constexpr int kMaxCoopQuads = 4;       // quads a lane keeps in registers in the one-pass step
 
-// Streaming kernels with many loads in flight per lane (the reduce, AdamW)
+// Streaming kernels with many loads in flight per lane (AdamW, the reduce)
 // run shards of kCapElems elements and more with at most four workgroups
-// resident per CU: the launch asks for kCapLds bytes of dynamic LDS, which
-// the kernels never touch, so that 160 KiB of LDS admits four.  Measured on
+// resident per CU (the reduce-only kernels at three, below): the launch asks
+// for kCapLds bytes of dynamic LDS, which the kernels never touch, so that
+// 160 KiB of LDS admits four.  Measured on
 // MI355X at full occupancy they lost bandwidth on the largest shards
 // (fp_adamw_shard at 226.5M elements: 1231 us uncapped, 1154 us capped;
 // fp_reduce_shard of 8 ranks: 906 vs 844 us; at 100M 508 vs 499 and 389
@@ -45,13 +46,15 @@ constexpr int kMaxCoopQuads = 4;       // quads a lane keeps in registers in the
 constexpr int64_t kCapElems = (int64_t)1 << 26;
 constexpr unsigned kCapLds = 40u << 10;
 inline unsigned capped_lds(int64_t shard) { return shard >= kCapElems ? kCapLds : 0u; }
-// The multi-unit reduce (16 ranks' loads per round trip, row pointers from
-// the unit records) of partitions from kSplitElems elements on runs with at
-// most three workgroups per CU.  Measured on MI355X at the bucketed 611M
-// model (16 ranks, 38.2M elements): 245 us at full occupancy, 241 at four
-// workgroups per CU, 233 at three, 241 at two.  The single-unit kernels
-// gained nothing from three over four.
-constexpr unsigned kUnitsReduceCapLds = 53504u;
+// The reduce-only kernels (single-unit and hybrid from kCapElems elements,
+// multi-unit from kSplitElems partition elements) run with at most three
+// workgroups per CU.  Measured on MI355X: the multi-unit reduce at the
+// bucketed 611M model (16 ranks, 38.2M elements) 245 us at full occupancy,
+// 241 at four workgroups per CU, 233 at three, 241 at two; fp_reduce_shard
+// of 16 ranks at 226.5M elements 1326-1348 us at four, 1306-1309 at three.
+// The fused step and AdamW kernels gained nothing from three over four.
+constexpr unsigned kReduceCapLds = 53504u;
+inline unsigned capped_reduce_lds(int64_t shard) { return shard >= kCapElems ? kReduceCapLds : 0u; }
 // The fused no-skip step of shards from kSplitElems elements on runs its
 // reduce + AdamW workgroups under the same cap and the copies of the other
 // shards in a launch of their own (measured: the d=12288 layer at 8 ranks

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void hybrid_reduce_kernel(const HybridArg
 
 template <bool kAligned, bool kAcc, bool kNorm>
 void hybrid_launch(const HybridArgs& a, dim3 g, bool wide, hipStream_t s) {
-    const unsigned lds = capped_lds(a.shard);
+    const unsigned lds = capped_reduce_lds(a.shard);
     if (wide) hybrid_reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, lds, s>>>(a);
     else hybrid_reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, lds, s>>>(a);
 }

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void step_coop_kernel(const StepArgs a) {
 
 template <bool kAligned, bool kAcc, bool kNorm>
 void reduce_launch(const ReduceArgs& a, dim3 g, bool wide, hipStream_t s) {
-    const unsigned lds = capped_lds(a.shard);
+    const unsigned lds = capped_reduce_lds(a.shard);
     if (wide) reduce_kernel<kAligned, kAcc, kNorm, 16><<<g, kThreads, lds, s>>>(a);
     else reduce_kernel<kAligned, kAcc, kNorm, 8><<<g, kThreads, lds, s>>>(a);
 }

@@ -180,7 +180,7 @@ void units_phase1_launch(const UnitsArgs& a, dim3 g, bool fused, unsigned lds, h
 hipError_t launch_units_reduce(const UnitsArgs& a, bool aligned, bool capped, hipStream_t s) {
     const bool norm = a.partials != nullptr, acc = a.accumulate != 0;
     const dim3 g((unsigned)a.reduce_groups);
-    const unsigned lds = capped ? kUnitsReduceCapLds : 0u;
+    const unsigned lds = capped ? kReduceCapLds : 0u;
 #define FP_UREDUCE(AL, AC, NO) units_reduce_launch<AL, AC, NO>(a, g, lds, s)
     if (aligned) {
         if (acc) { if (norm) FP_UREDUCE(true, true, true); else FP_UREDUCE(true, true, false); }
