@@ -398,6 +398,9 @@ def time_steps(w, K, W, timing, ev):
         torch.cuda.synchronize()
         total = ev.elapsed_ms(marks[0], marks[1])
         mean = [0.0] * w.n_events()
+        # each step from its first event to the next step's (the last one to the end mark)
+        per_step = [ev.elapsed_ms(evs[k][0], evs[k + 1][0] if k + 1 < count else marks[1])
+                    for k in range(count)]
         for e in evs:
             for j in range(1, len(e)):
                 mean[j] += ev.elapsed_ms(e[0], e[j]) / count
@@ -405,11 +408,15 @@ def time_steps(w, K, W, timing, ev):
                 ev.destroy(x)
         for x in marks:
             ev.destroy(x)
-        return total / count, mean
+        return total / count, mean, sorted(per_step)
 
     time_steps.spread = None
     if timing == "eager":
-        step_ms, ev_ms = eager_pass(W, K)
+        step_ms, ev_ms, per_step = eager_pass(W, K)
+        time_steps.spread = {"median_ms_per_step": round(per_step[len(per_step) // 2], 5),
+                             "min_ms_per_step": round(per_step[0], 5),
+                             "max_ms_per_step": round(per_step[-1], 5), "steps": K,
+                             "how": "each step from the library's first event of the step to the next step's"}
         return step_ms, ev_ms, ("eager launches from Python, exactly K steps; step time from hipEvents around "
                                 "the region, per-kernel times from the hipEvents the library records around "
                                 "its kernels on its stream inside the same region")
@@ -454,7 +461,7 @@ def time_steps(w, K, W, timing, ev):
                              "max_ms_per_step": round(per_replay[-1], 5), "replays": reps,
                              "steps_per_replay": n, "tail_steps": rem}
     del graphs, main, tail
-    _, ev_ms = eager_pass(W + K, min(K, 200))
+    _, ev_ms, _ = eager_pass(W + K, min(K, 200))
     # An eager step of a short shard is host-bound: the GPU waits between the
     # library's events, so the eager per-kernel split is scaled to the graph's
     # step time (for a one-kernel step, its kernel time is the step time).
@@ -829,6 +836,7 @@ def side_config(name, K, W, timing, ev, dev):
     out.update(summary(cfg, w, "speculative", r, B))
     out["kernels"] = kernel_lines(r["kernels"])
     out["timing"] = r["how"]
+    out["spread"] = r["spread"]
     w.set_flags(fp.FP_STEP_EXACT_SKIP, False)
     r = measure(w, K, W, timing, ev, B)
     out["in_place_exact"] = summary(cfg, w, "exact", r, B)
