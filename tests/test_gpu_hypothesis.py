@@ -9,7 +9,13 @@ GPU must match the oracle on each.
   subnormals, the largest finite values, +-inf, NaN) mixed with normals,
   one or two micro-batches: bitwise, non-finite values by class;
 * the shard step on the same kind of inputs (finite gradients whose sum may
-  still overflow fp32), every path, in place or with separate output state.
+  still overflow fp32), every path, in place or with separate output state;
+* the multi-unit step: one to eight units of random sizes (empty, shorter
+  than a quad, ragged, several workgroups), N_d up to 16, one to three
+  micro-batches, rows at odd element offsets, an overflow in a random unit
+  or none, in place or with separate output partitions, with or without the
+  norm: every unit against the oracle's unit-by-unit step with one overflow
+  decision for all.
 Examples are derandomised (a fixed sequence per test) so that a failure
 repeats; no example database is written.
 """
@@ -151,3 +157,18 @@ def test_step_matches_oracle(fp, world, S, rank_frac, flags, step, frac, out_of_
     mask[own] = False
     assert_bf16_equal(fh[mask], full_o[mask], "other shards")
     assert fp.workspace_timeouts(ws) == 0
+
+
+@settings(max_examples=40, deadline=None, database=None, derandomize=True,
+          suppress_health_check=list(HealthCheck))
+@given(world=st.sampled_from([1, 2, 3, 8, 16]), sizes=st.lists(st.integers(0, 6000), min_size=1, max_size=8),
+       rank_frac=st.floats(0, 0.999), n_micro=st.integers(1, 3), step=st.integers(1, 3),
+       flags=st.sampled_from([0, 1, 2]), inf=st.booleans(), offset=st.integers(0, 7),
+       out_of_place=st.booleans(), with_norm=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_units_match_oracle(fp, world, sizes, rank_frac, n_micro, step, flags, inf, offset, out_of_place,
+                            with_norm, seed):
+    from test_gpu_units import _units_case
+    rank = int(rank_frac * world)
+    inf_unit = seed % len(sizes) if inf else None
+    _units_case(fp, sizes, world, rank, n_micro, step, seed % 100_000, flags, inf_unit=inf_unit, offset=offset,
+                with_norm=with_norm, out_of_place=out_of_place)
