@@ -10,7 +10,9 @@
   on each buffer set;
 * --gpus above 1 is refused with a message;
 * the CPU baseline names the host CPU: lscpu's model name, with family /
-  model / stepping where the name carries no model number.
+  model / stepping where the name carries no model number;
+* the roofline's traffic comes only from a counter summary taken on the
+  current kernel sources, and every timed path's dominant kernel has one.
 """
 
 import types
@@ -151,3 +153,35 @@ def test_cpu_model_names_the_part():
     assert bench.cpu_model_from_lscpu(_LSCPU_VM) == "AMD EPYC (cpu family 26, model 2, stepping 1, KVM guest)"
     assert bench.cpu_model_from_lscpu(_LSCPU_HOST) == "Intel(R) Xeon(R) Processor @ 2.70GHz"
     assert bench.cpu_model_from_lscpu("") == ""
+
+
+def test_traffic_comes_only_from_counters_of_the_current_sources(tmp_path, monkeypatch):
+    import json
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "f" * 16)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    f = tmp_path / "profiles" / "counters_k_w.json"
+    assert bench.load_traffic("w", "k") is None                      # no summary
+    f.write_text(json.dumps({"source_hash": "0" * 16, "hbm_bytes_per_launch": 123}))
+    assert bench.load_traffic("w", "k") is None                      # taken on other sources
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.load_traffic("w", "k") == 123
+
+
+def test_every_timed_kernel_has_a_counter_summary():
+    """The default line's and the configs' dominant kernels each have a committed
+    counter summary (profiles/counters_<kernel>_<workload>.json) with the
+    calibrated HBM bytes and the commands that produced them."""
+    import json
+    import os
+    names = [("step_phase1_fused", "c4_layer_d12288_nd8"), ("unshard", "c4_layer_d12288_nd8"),
+             ("step_phase1_fused", "c5_ragged10k_nd64"), ("unshard", "c5_ragged10k_nd64"),
+             ("units_reduce", "c3_611m_buckets_nd16"), ("units_phase1_fused", "c3_611m_buckets_nd16"),
+             ("units_copy", "c3_611m_buckets_nd16"), ("step_coop", "c2_layer_d1024_nd8")]
+    for kernel, workload in names:
+        path = os.path.join(bench.ROOT, "profiles", f"counters_{kernel}_{workload}.json")
+        with open(path) as f:
+            d = json.load(f)
+        assert d["hbm_bytes_per_launch"] > 0 and d["algorithmic_bytes_per_launch"] > 0, path
+        assert set(d["commands"]) == {"FETCH_SIZE", "WRITE_SIZE", "calibration"}, path
+        assert 0.9 < d["traffic_over_algorithmic"] < 1.2, path
