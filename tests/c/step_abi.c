@@ -16,7 +16,8 @@
  * 1e-9 absolute, the own bf16 slice within 1 ulp, the other ranks' slices
  * and the flag exactly.  step_abi_run() returns the number of failed cases
  * (0 when every case holds; 100 without a GPU) and prints one line per case
- * on stdout. */
+ * on stdout; a failed call ends its case (its buffers are not freed) but
+ * never the process. */
 
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -39,24 +40,28 @@ static const int64_t S = 1000003; /* odd: rows off the 8-byte grid, a ragged las
 static const double LR = 1e-3, B1 = 0.9, B2 = 0.999, EPS = 1e-8, WD = 0.01;
 static const int64_t STEP = 3;
 
-#define HIP_OK(x)                                                                  \
-    do {                                                                           \
-        hipError_t e_ = (x);                                                       \
-        if (e_ != hipSuccess) {                                                    \
-            fprintf(stderr, "%s:%d: %s\n", __FILE__, __LINE__, hipGetErrorString(e_)); \
-            exit(3);                                                               \
-        }                                                                          \
+/* A failed HIP or library call ends the case with an error (returned to the
+ * caller, which is a test in its own process: nothing here exits). */
+#define HIP_OK(x)                                                                      \
+    do {                                                                               \
+        hipError_t e_ = (x);                                                           \
+        if (e_ != hipSuccess) {                                                        \
+            fprintf(stderr, "%s:%d: %s\n", __FILE__, __LINE__, hipGetErrorString(e_));  \
+            return CASE_ERROR;                                                         \
+        }                                                                              \
     } while (0)
 
-#define CHECK_FP(x)                                                                         \
-    do {                                                                                   \
-        fp_status s_ = (x);                                                                \
+#define CHECK_FP(x)                                                                      \
+    do {                                                                                 \
+        fp_status s_ = (x);                                                              \
         if (s_ != FP_OK) {                                                               \
-            fprintf(stderr, "%s:%d: %s: %s\n", __FILE__, __LINE__, fp_status_string(s_),   \
-                    fp_last_error());                                                      \
-            exit(2);                                                                       \
-        }                                                                                  \
+            fprintf(stderr, "%s:%d: %s: %s\n", __FILE__, __LINE__, fp_status_string(s_), \
+                    fp_last_error());                                                    \
+            return CASE_ERROR;                                                           \
+        }                                                                                \
     } while (0)
+
+enum { CASE_ERROR = 1000 };
 
 /* splitmix64: seeded inputs, the same bytes for the GPU and the oracle */
 static uint64_t mix(uint64_t* s) {
@@ -69,11 +74,10 @@ static float uniform(uint64_t* s, float lo, float hi) {
     return lo + (hi - lo) * (float)((mix(s) >> 40) * (1.0 / 16777216.0));
 }
 
-static void* dev_copy(const void* host, size_t bytes) {
-    void* p = NULL;
-    HIP_OK(hipMalloc(&p, bytes));
-    HIP_OK(hipMemcpy(p, host, bytes, hipMemcpyHostToDevice));
-    return p;
+static int dev_copy(void** p, const void* host, size_t bytes) {
+    HIP_OK(hipMalloc(p, bytes));
+    HIP_OK(hipMemcpy(*p, host, bytes, hipMemcpyHostToDevice));
+    return 0;
 }
 
 static int ulp_distance_over_one(uint16_t a, uint16_t b) {
@@ -111,11 +115,12 @@ static int run_case(int form, int inf, int32_t want_path) {
     }
 
     /* device side: one buffer of rows per micro-batch, as a bucket would hold them */
-    uint16_t* d_grads = dev_copy(grads, (size_t)MICRO * WORLD * nb);
-    uint16_t* d_others = dev_copy(others, (size_t)WORLD * nb);
-    float* d_master = dev_copy(master, nf);
-    float* d_m = dev_copy(exp_avg, nf);
-    float* d_v = dev_copy(exp_avg_sq, nf);
+    uint16_t *d_grads = NULL, *d_others = NULL;
+    float *d_master = NULL, *d_m = NULL, *d_v = NULL;
+    if (dev_copy((void**)&d_grads, grads, (size_t)MICRO * WORLD * nb) ||
+        dev_copy((void**)&d_others, others, (size_t)WORLD * nb) || dev_copy((void**)&d_master, master, nf) ||
+        dev_copy((void**)&d_m, exp_avg, nf) || dev_copy((void**)&d_v, exp_avg_sq, nf))
+        return CASE_ERROR;
     float *d_acc = NULL, *d_out[3] = {NULL, NULL, NULL};
     uint16_t* d_full = NULL;
     int32_t* d_flag = NULL;
@@ -256,9 +261,12 @@ int step_abi_run(void) {
     }
     int failures = 0;
     for (int inf = 0; inf < 2; ++inf) {
-        failures += run_case(0, inf, FP_PATH_ONE_PASS);
-        failures += run_case(1, inf, FP_PATH_TWO_PHASE);
-        failures += run_case(2, inf, FP_PATH_SPECULATIVE);
+        const int32_t want[3] = {FP_PATH_ONE_PASS, FP_PATH_TWO_PHASE, FP_PATH_SPECULATIVE};
+        for (int form = 0; form < 3; ++form) {
+            const int r = run_case(form, inf, want[form]);
+            if (r == CASE_ERROR) printf("FAIL form=%d overflow=%d: a call failed (above)\n", form, inf);
+            failures += r != 0;
+        }
     }
     printf("%s: %d case(s) failed\n", failures ? "FAIL" : "ok", failures);
     fflush(stdout);
